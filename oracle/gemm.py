@@ -1,0 +1,67 @@
+"""Plain GEMM with optional per-row A and per-column B scales (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Definition followed ("gemm_rowcolquant dispatcher bridge" PR, final
+description, scope section; and the stream-K GEMM bridge commit
+"feat(ck-tile): stream-K GEMM TE to dispatcher bridge", Validation):
+
+    R[m][n] = sA[m] * sB[n] * sum_{k < K} a(m, k) * b(k, n)
+
+in the "rcr" layout: A row-major (element (m, k) at ``A[m*lda + k]``), B
+column-major (element (k, n) at ``B[n*ldb + k]``), C row-major.  The scales
+are float32 vectors of length M and N; an absent scale is 1.  Everything is
+evaluated in float64 on the decoded input codes, so the result is the exact
+product sum up to float64 rounding.  The matrix product itself is numpy's
+float64 matmul (a library primitive); there is no blocking or reordering here.
+"""
+
+import numpy as np
+
+from .codecs import decode
+
+
+def operand_matrix(fmt, codes, rows, cols, ld):
+    """Decode a ``rows x cols`` block stored with leading dimension ``ld``."""
+    flat = np.asarray(codes).reshape(-1)
+    if ld < cols:
+        raise ValueError("leading dimension smaller than the row length")
+    need = (rows - 1) * ld + cols if rows > 0 else 0
+    if flat.size < need:
+        raise ValueError("operand buffer too small")
+    if rows == 0 or cols == 0:
+        return np.zeros((rows, cols))
+    padded = np.zeros(rows * ld, dtype=flat.dtype)
+    padded[:need] = flat[:need]
+    return decode(fmt, padded.reshape(rows, ld)[:, :cols])
+
+
+def gemm(fmt, a_codes, b_codes, M, N, K, lda=None, ldb=None,
+         scale_a=None, scale_b=None):
+    """float64 ``R`` (M x N) for rcr operands holding ``fmt`` codes."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    a = operand_matrix(fmt, a_codes, M, K, lda)          # a[m][k]
+    bt = operand_matrix(fmt, b_codes, N, K, ldb)         # bt[n][k] = b(k, n)
+    r = a @ bt.T
+    if scale_a is not None:
+        r = r * np.asarray(scale_a, dtype=np.float64).reshape(M, 1)
+    if scale_b is not None:
+        r = r * np.asarray(scale_b, dtype=np.float64).reshape(1, N)
+    return r
+
+
+def gemm_entry(fmt, a_codes, b_codes, m, n, K, lda=None, ldb=None,
+               scale_a=None, scale_b=None):
+    """One output element R[m][n], computed on its own (for sampled checks of
+    outputs too large to form whole)."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    a_row = decode(fmt, np.asarray(a_codes).reshape(-1)[m * lda: m * lda + K])
+    b_col = decode(fmt, np.asarray(b_codes).reshape(-1)[n * ldb: n * ldb + K])
+    v = float(np.dot(a_row, b_col))
+    if scale_a is not None:
+        v *= float(np.asarray(scale_a).reshape(-1)[m])
+    if scale_b is not None:
+        v *= float(np.asarray(scale_b).reshape(-1)[n])
+    return v

@@ -1,0 +1,74 @@
+"""Pins of the oracle GEMM (CPU only).
+
+The oracle computes R[m][n] = sA[m] sB[n] sum_k a(m,k) b(k,n) on rcr operands.
+It is pinned by closed forms (identity B, all-ones operands), by an
+independent pure-Python triple loop written from the rcr index definition on
+small shapes with padded leading dimensions, and by its per-element form.  A
+transposed operand, a wrong leading dimension, a dropped scale or a wrong sign
+fails at least one of these.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import codecs
+from oracle.gemm import gemm, gemm_entry
+
+
+def rand_codes(fmt, shape, rng, lo=-3, hi=3):
+    vals = rng.integers(lo, hi + 1, size=shape).astype(np.float64) / 2
+    return codecs.encode(fmt, vals)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3"])
+def test_identity_b_gives_scaled_a(fmt):
+    rng = np.random.default_rng(1)
+    M, K = 7, 12
+    a = rand_codes(fmt, (M, K), rng)
+    eye = codecs.encode(fmt, np.eye(K))          # column-major identity == identity
+    sa = 2.0 ** rng.integers(-2, 3, size=M)
+    sb = 2.0 ** rng.integers(-2, 3, size=K)
+    r = gemm(fmt, a, eye, M, K, K, scale_a=sa, scale_b=sb)
+    expect = codecs.decode(fmt, a) * sa[:, None] * sb[None, :]
+    assert np.array_equal(r, expect)
+
+
+def test_all_ones_gives_k():
+    M, N, K = 5, 9, 33
+    one = codecs.encode("f16", np.ones(M * K))
+    oneb = codecs.encode("f16", np.ones(N * K))
+    assert np.array_equal(gemm("f16", one, oneb, M, N, K), np.full((M, N), float(K)))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3"])
+def test_matches_triple_loop_with_leading_dimensions(fmt):
+    rng = np.random.default_rng(2)
+    M, N, K, lda, ldb = 5, 4, 6, 9, 8
+    a = rand_codes(fmt, (M * lda,), rng)
+    b = rand_codes(fmt, (N * ldb,), rng)
+    sa = rng.uniform(0.5, 2, M).astype(np.float32)
+    sb = rng.uniform(0.5, 2, N).astype(np.float32)
+    r = gemm(fmt, a, b, M, N, K, lda=lda, ldb=ldb, scale_a=sa, scale_b=sb)
+    av = [float(v) for v in codecs.decode(fmt, a)]
+    bv = [float(v) for v in codecs.decode(fmt, b)]
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += av[m * lda + k] * bv[n * ldb + k]   # A row-major, B column-major
+            expect = acc * float(sa[m]) * float(sb[n])
+            assert r[m, n] == pytest.approx(expect, rel=1e-14, abs=1e-14)
+            assert gemm_entry(fmt, a, b, m, n, K, lda, ldb, sa, sb) == pytest.approx(expect, rel=1e-14, abs=1e-14)
+
+
+def test_nonsymmetric_hand_example():
+    # A = [[1, 2], [3, 4]] (row-major), B = [[5, 6], [7, 8]] stored column-major
+    # as [5, 7, 6, 8]; A @ B = [[19, 22], [43, 50]].
+    a = codecs.encode("f16", [1, 2, 3, 4])
+    b = codecs.encode("f16", [5, 7, 6, 8])
+    assert gemm("f16", a, b, 2, 2, 2).tolist() == [[19.0, 22.0], [43.0, 50.0]]
+
+
+def test_rejects_short_buffers():
+    with pytest.raises(ValueError):
+        gemm("f16", np.zeros(5, np.uint16), np.zeros(6, np.uint16), 2, 2, 3)

@@ -1,0 +1,181 @@
+"""Pins of the oracle partitioner and dispatch simulator (CPU only).
+
+* Values the pages print (tests/golden/printed_values.json, each cited).
+* Brute force over every small problem: each MAC iteration covered exactly
+  once, contiguous and balanced stream-K ranges, at most one non-owner tile per
+  stream-K CTA, the contributor bound, a safe all-DP plan.
+* The invariant checker itself is shown to catch planted mistakes (a plan with
+  an off-by-one range, a wrong inverse map), so a passing sweep means
+  something.
+* The dispatch model: waits only target higher block ids, every plan completes
+  when the pool is resident.
+"""
+
+import json
+import os
+from dataclasses import replace
+
+import pytest
+
+from oracle import partition as P
+from oracle import simulate as S
+
+
+@pytest.fixture(scope="module")
+def printed(golden_dir):
+    with open(os.path.join(golden_dir, "printed_values.json")) as f:
+        return json.load(f)
+
+
+def test_default_pool_printed(printed):
+    d = printed["default_pool_workspace"]
+    assert P.default_pool("workspace", d["num_cus"], 8) == d["pool"]
+    assert P.default_pool("atomic", d["num_cus"], 8) == d["pool"]
+    assert P.default_pool("linear", 256, 8) == 256
+    assert P.default_pool("tree", 256, 1) == 256
+    # capped by what stays resident
+    assert P.default_pool("workspace", 256, 2) == 512
+
+
+def test_one_tile_short_reduction_is_all_dp(printed):
+    d = printed["one_tile_all_dp"]
+    for ipt in (d["iters_first"], d["iters_last"]):
+        p = P.plan(1, 1, ipt, 128, 128, 4, "dp_sk", "workspace", d["pool"])
+        assert p.sk_ctas == d["sk_ctas"] and p.dp_tiles == 1 and p.grid == 1
+        assert p.workspace_bytes == 0 and p.iters_per_sk_cta == 1
+    p = P.plan(1, 1, d["iters_last"] + 1, 128, 128, 4, "dp_sk", "workspace", d["pool"])
+    assert p.sk_ctas == d["pool"]
+
+
+def test_flag_table_printed(printed):
+    d = printed["flag_table_bytes"]
+    # A shape with a stream-K remainder under the 256-CTA pool.
+    p = P.plan(19, 16, 64, 256, 256, d["n_waves"], "dp_sk", "tree", d["pool"])
+    assert p.sk_ctas == d["pool"]
+    assert p.flags_bytes == d["bytes_per_wave_flags"]
+    assert P.ceil_div(4 * p.sk_ctas, 256) * 256 == d["bytes_per_cta_flags"]
+
+
+def test_four_contributors_two_rounds(printed):
+    d = printed["tree_rounds_four_ctas"]
+    # one tile of 8 iterations over 4 CTAs: every CTA takes 2 iterations
+    p = P.plan(1, 1, 8, 64, 64, 4, "dp_sk", "tree", 4)
+    assert p.max_contrib == d["contributors"] and p.tree_rounds == d["tree_rounds"]
+    assert p.linear_partners == 3
+
+
+def test_small_gemm_plan_ranges():
+    # 256x256x4096 GEMM, 128x128x32 tiles, 6-CTA pool, linear.
+    tm, tn, ipt = P.gemm_tiles(256, 256, 4096, 128, 128, 32)
+    p = P.plan(tm, tn, ipt, 128, 128, 4, "dp_sk", "linear", 6)
+    assert (p.tiles, p.iters_per_tile, p.dp_tiles, p.sk_tiles, p.sk_ctas) == (4, 128, 0, 4, 6)
+    assert (p.iters_per_sk_cta, p.extra_iters, p.grid) == (85, 2, 6)
+    assert [p.sk_range(b) for b in range(6)] == [
+        (0, 86), (86, 172), (172, 257), (257, 342), (342, 427), (427, 512)]
+    assert p.contributors(2) == [2, 3, 4]
+    assert p.segments(2) == [(1, 44, 128, False, True), (2, 0, 1, True, False)]
+    assert p.max_contrib == 3 and p.flags_bytes == 256
+    assert p.partials_bytes == 6 * 128 * 128 * 4
+
+
+def test_large_gemm_plan():
+    tm, tn, ipt = P.gemm_tiles(4864, 4096, 4096, 256, 256, 64)
+    p = P.plan(tm, tn, ipt, 256, 256, 4, "dp_sk", "tree", 256)
+    assert (p.tiles, p.dp_tiles, p.sk_tiles, p.sk_ctas, p.iters_per_sk_cta, p.extra_iters) == \
+        (304, 256, 48, 256, 12, 0)
+    assert p.grid == 512 and p.max_contrib == 6 and p.tree_rounds == 3
+    q = P.plan(tm, tn, ipt, 256, 256, 4, "persistent", "tree", 256)
+    assert q.grid == 256
+
+
+def test_wgrad_tiles_fold_groups():
+    # 32 groups of 16 output channels with a 32-row tile: one partial M tile
+    # per group; GEMM-N = 16*3*3 = 144 -> 3 tiles of 64; Ho = Wo = 14.
+    assert P.wgrad_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 32, 64, 64) == (32, 3, 196)
+    assert P.wgrad_tiles(32, 56, 56, 256, 256, 3, 3, 1, 1, 1, 1, 1, 128, 128, 32) == (2, 18, 3136)
+
+
+def test_all_dp_plan_has_safe_divisor():
+    p = P.plan(4, 4, 10, 64, 64, 4, "dp_sk", "linear", 16)
+    assert p.sk_ctas == 0 and p.iters_per_sk_cta == 1 and p.workspace_bytes == 0
+    assert p.cta_of(0) == 0                      # no division by zero
+    q = P.plan(2, 2, 3, 64, 64, 4, "persistent", "linear", 16)
+    assert q.grid == 4 and P.check_plan(q) == []
+
+
+def test_rejects_bad_pools():
+    for bad in (0, -2, -7):
+        with pytest.raises(ValueError):
+            P.plan(1, 1, 4, 64, 64, 4, "dp_sk", "linear", bad)
+    with pytest.raises(ValueError):
+        P.plan(1, 1, 4, 64, 64, 4, "split_k", "linear", 4)
+    with pytest.raises(ValueError):
+        P.plan(1, 1, 4, 64, 64, 4, "dp_sk", "fancy", 4)
+
+
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent", "dp"])
+def test_bruteforce_invariants(mode):
+    n = 0
+    for T in range(1, 25):
+        tiles_m = 1 if T % 2 else 2
+        tiles_n = T // tiles_m
+        for ipt in range(1, 21):
+            for pool in range(1, 41):
+                if mode != "dp_sk" and (pool % 3):
+                    continue
+                p = P.plan(tiles_m, tiles_n, ipt, 32, 32, 4, mode, "linear", pool)
+                assert P.check_plan(p) == [], (T, ipt, pool)
+                n += 1
+    assert n > 1000
+
+
+def test_checker_catches_planted_mistakes():
+    p = P.plan(1, 3, 10, 32, 32, 4, "dp_sk", "linear", 4)
+    assert P.check_plan(p) == []
+
+    class OffByOne(P.Plan):
+        def sk_range(self, b):
+            s, e = super().sk_range(b)
+            return s, e + (1 if b == 1 else 0)
+
+    bad = OffByOne(**p.__dict__)
+    assert "a MAC iteration is not covered exactly once" in P.check_plan(bad)
+
+    class WrongInverse(P.Plan):
+        def cta_of(self, it):
+            return it // (self.iters_per_sk_cta + 1)
+
+    assert "inverse map disagrees with the ranges" in P.check_plan(WrongInverse(**p.__dict__))
+    # an unclamped all-DP divisor is flagged
+    q = P.plan(2, 2, 5, 32, 32, 4, "dp_sk", "linear", 4)
+    assert q.sk_ctas == 0
+    assert P.check_plan(replace(q, iters_per_sk_cta=0)) != []
+
+
+@pytest.mark.parametrize("reduction", ["linear", "tree"])
+def test_waits_target_higher_ctas_and_resident_pool_completes(reduction):
+    for T in (1, 3, 5, 7, 12):
+        for ipt in (1, 3, 8, 13):
+            for pool in (2, 3, 5, 8, 11):
+                for mode in ("dp_sk", "persistent"):
+                    p = P.plan(1, T, ipt, 32, 32, 4, mode, reduction, pool)
+                    assert S.waits_target_higher(p)
+                    assert S.completes(p, max(p.sk_ctas, 1))
+                    cap = S.min_capacity(p)
+                    assert cap is not None and cap <= max(p.sk_ctas, 1)
+
+
+def test_simulator_reports_stall_below_capacity():
+    # One tile, four CTAs, linear: the owner (CTA 0) waits on CTAs 1..3 while
+    # holding its slot, so a single resident CTA cannot finish.
+    p = P.plan(1, 1, 8, 32, 32, 4, "dp_sk", "linear", 4)
+    assert not S.completes(p, 1)
+    assert S.completes(p, 2)
+    assert S.min_capacity(p) == 2
+    # Tree on the same plan: CTA 2 waits on 3 and publishes, CTA 0 waits on
+    # 1 then 2.
+    t = P.plan(1, 1, 8, 32, 32, 4, "dp_sk", "tree", 4)
+    assert S.events(t, 0) == [("wait", 1), ("wait", 2)]
+    assert S.events(t, 1) == [("pub", 1)]
+    assert S.events(t, 2) == [("wait", 3), ("pub", 2)]
+    assert S.events(t, 3) == [("pub", 3)]
