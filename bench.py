@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the stream-K engine on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input resident in HBM: a single skg_run_gemm / skg_run_wgrad call (argument
+checks, plan, resets, the stream-K kernel with its fix-up, and the second
+stage when the reduction has one).  Default workload: the bf16 GEMM
+4864 x 4096 x 4096 with 256x256x64 tiles (256 data-parallel tiles, 48 spread
+stream-K over a 256-CTA pool, tree fix-up).
+
+Prints one JSON line: TFLOP/s of the whole step, the roofline of the
+stream-K kernel (timed alone with HIP events on the stream it runs on), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Dense MFMA peaks of MI355X (TFLOP/s) and its HBM3E bandwidth (GB/s).
+MFMA_PEAK = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
+HBM_PEAK_GBS = 8000.0
+METRIC = "TFLOP/s and % of MFMA peak, stream-K GEMM and conv wgrad on 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--mode", default=None)
+    ap.add_argument("--reduction", default=None)
+    ap.add_argument("--ctas", type=int, default=None)
+    ap.add_argument("--tile", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle sample (0 disables it)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with the measured HBM bytes per launch of the kernel")
+    return ap.parse_args()
+
+
+def alg_bytes(wl):
+    """Each input read once plus the output written once."""
+    if wl.op == "gemm":
+        eab = 1 if wl.dtype_ab == "e4m3" else 2
+        ec = 4 if wl.dtype_c == "f32" else 2
+        extra = 4 * (wl.M + wl.N) if wl.scales else 0
+        return eab * (wl.M * wl.K + wl.N * wl.K) + ec * wl.M * wl.N + extra
+    ho, wo = wl.out_hw
+    return 2 * (wl.n * wl.h * wl.w * wl.c + wl.n * ho * wo * wl.k) + \
+        4 * wl.k * wl.r * wl.s * (wl.c // wl.groups)
+
+
+def cpu_baseline(wl, inp, target_s):
+    """The oracle as it stands, timed on a bounded sample of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle.gemm import gemm as oracle_gemm
+    from oracle.wgrad import wgrad as oracle_wgrad
+
+    def run(frac_units):
+        t0 = time.perf_counter()
+        if wl.op == "gemm":
+            rows = frac_units
+            oracle_gemm(wl.dtype_ab, inp["A"][:rows * wl.K], inp["B"], rows, wl.N, wl.K,
+                        scale_a=None if "scale_a" not in inp else inp["scale_a"][:rows],
+                        scale_b=inp.get("scale_b"))
+            flops = 2.0 * rows * wl.N * wl.K
+        else:
+            imgs = frac_units
+            ho, wo = wl.out_hw
+            oracle_wgrad(wl.dtype, inp["x"][:imgs * wl.h * wl.w * wl.c],
+                         inp["dy"][:imgs * ho * wo * wl.k], imgs, wl.h, wl.w, wl.c, wl.k, wl.r,
+                         wl.s, wl.stride[0], wl.stride[1], wl.pad[0], wl.pad[1], wl.groups)
+            flops = wl.flops() * imgs / wl.n
+        return time.perf_counter() - t0, flops
+
+    full = wl.M if wl.op == "gemm" else wl.n
+    unit = max(1, full // 64)
+    t, _ = run(unit)
+    units = int(min(full, max(unit, unit * target_s / max(t, 1e-3))))
+    t, flops = run(units)
+    threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    what = ("rows [0, %d) of the %d-row output" % (units, full)) if wl.op == "gemm" else \
+        ("images [0, %d) of %d" % (units, full))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%s, fp64 oracle (numpy float64 matmul), %.1f s" % (what, t),
+            "seconds": t}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import implicit_gemm_conv_dp_amd as skg
+    from implicit_gemm_conv_dp_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    mode = args.mode or wl.modes[0]
+    red = args.reduction or wl.reductions[0]
+    ctas = args.ctas if args.ctas is not None else wl.ctas
+    tile = args.tile or wl.tile
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.inputs()
+
+    def up(codes):
+        a = np.ascontiguousarray(codes)
+        a = a.view(np.uint8) if a.dtype.itemsize == 1 else a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    if wl.op == "gemm":
+        dA, dB = up(inp["A"]), up(inp["B"])
+        sa = torch.from_numpy(inp["scale_a"]).to(dev) if wl.scales else None
+        sb = torch.from_numpy(inp["scale_b"]).to(dev) if wl.scales else None
+        out = torch.empty(wl.M * wl.N, dtype=torch.float32 if wl.dtype_c == "f32" else torch.int16,
+                          device=dev)
+        kw = dict(M=wl.M, N=wl.N, K=wl.K, dtype_ab=wl.dtype_ab, dtype_c=wl.dtype_c, tile=tile,
+                  mode=mode, reduction=red, ctas=ctas)
+        plan = skg.plan_gemm(**kw)
+        ws = skg.workspace_for(plan, dev)
+
+        def step():
+            skg.gemm(dA, dB, out, sa, sb, workspace=ws, **kw)
+        dtype = wl.dtype_ab
+    else:
+        dx, ddy = up(inp["x"]), up(inp["dy"])
+        out = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device=dev)
+        kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
+                  pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile=tile, mode=mode,
+                  reduction=red, ctas=ctas)
+        plan = skg.plan_wgrad(**kw)
+        ws = skg.workspace_for(plan, dev)
+
+        def step():
+            skg.wgrad(dx, ddy, out, workspace=ws, **kw)
+        dtype = wl.dtype
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    # One event pair per timed step brackets the stream-K kernel alone.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in pairs:   # create the underlying HIP events
+        a.record(stream)
+        b.record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in pairs:
+        skg.skg_profile_events(a.cuda_event, b.cuda_event)
+        step()
+    skg.skg_profile_events(None, None)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = total_ms / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
+
+    flops = wl.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = MFMA_PEAK[dtype]
+    hbm_bound = args.workload == 4
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    if hbm_bound:
+        achieved = alg_bytes(wl) / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    else:
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic}
+    roof["kernel_ms"] = kernel_ms
+    roof["alg_flop"] = flops
+    roof["alg_bytes"] = alg_bytes(wl)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "pct_of_mfma_peak": 100.0 * value / peak,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tile": tile, "mode": mode, "reduction": red,
+                   "ctas": ctas, "plan": {k: plan[k] for k in (
+                       "tiles", "iters_per_tile", "dp_tiles", "sk_tiles", "sk_ctas",
+                       "iters_per_sk_cta", "extra_iters", "grid", "max_contrib", "tree_rounds")}},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

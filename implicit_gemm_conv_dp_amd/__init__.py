@@ -1,0 +1,111 @@
+"""Stream-K GEMM and conv-wgrad engine for MI355X (gfx950).
+
+The compute path is the HIP library ``libskgemm.so`` (C ABI in
+``include/skgemm.h``); this package only marshals torch device tensors and
+streams into its calls.  PyTorch provides device memory and streams.
+
+    import implicit_gemm_conv_dp_amd as skg
+    plan = skg.gemm(A, B, C, M=..., N=..., K=..., dtype_ab="bf16", dtype_c="bf16",
+                    tile="256x256x64", mode="dp_sk", reduction="tree", ctas=256)
+
+``A`` is M x K row-major, ``B`` is K x N column-major (N rows of K), ``C`` is
+M x N row-major; tensors are passed as raw storage (any torch dtype), their
+element type is ``dtype_ab`` / ``dtype_c``.  ``wgrad`` takes NHWC ``x`` and
+``dy`` and writes the fp32 KRSC filter gradient ``dw``.
+"""
+
+from . import _lib
+from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
+                   skg_plan_wgrad, skg_run_gemm, skg_run_wgrad, skg_tile_info, MODES,
+                   REDUCTIONS, DTYPES, TILES)
+
+__all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
+           "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES",
+           "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
+           "skg_run_gemm", "skg_run_wgrad", "skg_tile_info"]
+
+
+def _enum(table, v, what):
+    if isinstance(v, int):
+        return v
+    try:
+        return table[v]
+    except KeyError:
+        raise ValueError("unknown %s %r" % (what, v)) from None
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def gemm_args(A=None, B=None, C=None, *, M, N, K, dtype_ab, dtype_c, lda=None, ldb=None,
+              ldc=None, scale_a=None, scale_b=None, tile, mode, reduction, ctas):
+    a = _lib.skg_gemm_args_t()
+    a.M, a.N, a.K = M, N, K
+    a.dtype_ab = _enum(DTYPES, dtype_ab, "dtype")
+    a.dtype_c = _enum(DTYPES, dtype_c, "dtype")
+    a.A, a.B, a.C = _ptr(A), _ptr(B), _ptr(C)
+    a.lda = K if lda is None else lda
+    a.ldb = K if ldb is None else ldb
+    a.ldc = N if ldc is None else ldc
+    a.scale_a, a.scale_b = _ptr(scale_a), _ptr(scale_b)
+    a.tile_id = _enum(TILES, tile, "tile")
+    a.mode = _enum(MODES, mode, "mode")
+    a.reduction = _enum(REDUCTIONS, reduction, "reduction")
+    a.ctas = ctas
+    return a
+
+
+def wgrad_args(x=None, dy=None, dw=None, *, n, h, w, c, k, r, s, stride=(1, 1), pad=(0, 0),
+               groups=1, dtype, tile, mode, reduction, ctas):
+    a = _lib.skg_wgrad_args_t()
+    a.n, a.h, a.w, a.c, a.k, a.r, a.s = n, h, w, c, k, r, s
+    a.stride_h, a.stride_w = stride
+    a.pad_h, a.pad_w = pad
+    a.groups = groups
+    a.dtype = _enum(DTYPES, dtype, "dtype")
+    a.x, a.dy, a.dw = _ptr(x), _ptr(dy), _ptr(dw)
+    a.tile_id = _enum(TILES, tile, "tile")
+    a.mode = _enum(MODES, mode, "mode")
+    a.reduction = _enum(REDUCTIONS, reduction, "reduction")
+    a.ctas = ctas
+    return a
+
+
+def plan_gemm(**kw):
+    return skg_plan_gemm(gemm_args(**kw)).as_dict()
+
+
+def plan_wgrad(**kw):
+    return skg_plan_wgrad(wgrad_args(**kw)).as_dict()
+
+
+def workspace_for(plan, device):
+    """A device buffer large enough for ``plan`` (torch owns the memory)."""
+    import torch
+    return torch.empty(max(int(plan["workspace_bytes"]), 1), dtype=torch.uint8, device=device)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def gemm(A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, **kw):
+    """Enqueue C = epilogue(A @ B) on ``stream`` (default: torch's current
+    stream).  Returns the plan (a dict)."""
+    args = gemm_args(A, B, C, scale_a=scale_a, scale_b=scale_b, **kw)
+    plan = skg_plan_gemm(args).as_dict()
+    ws = workspace if workspace is not None else workspace_for(plan, C.device)
+    skg_run_gemm(args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    return plan
+
+
+def wgrad(x, dy, dw, workspace=None, stream=None, **kw):
+    """Enqueue dw = wgrad(x, dy) on ``stream``.  Returns the plan (a dict)."""
+    args = wgrad_args(x, dy, dw, **kw)
+    plan = skg_plan_wgrad(args).as_dict()
+    ws = workspace if workspace is not None else workspace_for(plan, dw.device)
+    skg_run_wgrad(args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    return plan

@@ -1,0 +1,327 @@
+// C ABI of the engine: device queries, plans and the run calls.
+//
+// Status convention of the stream-K GEMM bridge (composable_kernel commit
+// "feat(ck-tile): stream-K GEMM TE to dispatcher bridge", Changes): 0, -1 for
+// a HIP error or a C++ exception, -2 for arguments the engine does not
+// support, decided before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <exception>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "skg_internal.hpp"
+#include "skg_launch.hpp"
+
+namespace skg {
+namespace {
+
+struct DeviceRec {
+  bool valid = false;
+  bool gfx950 = false;
+  int cus = 0;
+  std::string arch;
+};
+
+std::mutex g_dev_mu;
+std::vector<DeviceRec> g_devs;
+
+// Optional timing hook (skg_profile_events), per host thread.
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+int current_device(DeviceRec* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failure(std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_devs.size() <= dev) g_devs.resize(dev + 1);
+  DeviceRec& r = g_devs[dev];
+  if (!r.valid) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_failure(std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    r.arch = prop.gcnArchName;
+    r.gfx950 = r.arch.compare(0, 6, "gfx950") == 0;
+    r.cus = prop.multiProcessorCount;
+    r.valid = true;
+  }
+  *out = r;
+  return SKG_OK;
+}
+
+// CU count and resident CTAs per CU of one instance on the current device.
+int device_capacity(int op, int tile_id, int dtype, int* cus, int* per_cu) {
+  DeviceRec d;
+  int rc = current_device(&d);
+  if (rc) return rc;
+  if (!d.gfx950) return unsupported("unsupported arch " + d.arch + " (the engine is built for gfx950)");
+  int occ = 0;
+  hipError_t e;
+  if (op == SKG_OP_GEMM) {
+    GemmInst in = gemm_instance(tile_id, dtype);
+    if (!in.occupancy) return unsupported("no GEMM instance for this tile and dtype");
+    e = in.occupancy(&occ);
+  } else if (op == SKG_OP_WGRAD) {
+    WgradInst in = wgrad_instance(tile_id, dtype);
+    if (!in.occupancy) return unsupported("no wgrad instance for this tile and dtype");
+    e = in.occupancy(&occ);
+  } else {
+    return unsupported("unknown op");
+  }
+  if (e != hipSuccess) return hip_failure(std::string("occupancy query: ") + hipGetErrorString(e));
+  if (occ <= 0) return unsupported("kernel instance cannot be resident on this device");
+  *cus = d.cus;
+  *per_cu = occ;
+  return SKG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+KPlan to_kplan(const skg_plan_t& pl) {
+  KPlan k;
+  k.tiles_m = (int)pl.tiles_m;
+  k.tiles_n = (int)pl.tiles_n;
+  k.ipt = (int)pl.iters_per_tile;
+  k.dp_tiles = (int)pl.dp_tiles;
+  k.sk_tiles = (int)pl.sk_tiles;
+  k.sk_ctas = (int)pl.sk_ctas;
+  k.ipc = (int)pl.iters_per_sk_cta;
+  k.extra = (int)pl.extra_iters;
+  k.grid = (int)pl.grid;
+  k.mode = pl.mode;
+  k.reduction = pl.reduction;
+  return k;
+}
+
+Scratch carve(const skg_plan_t& pl, void* ws) {
+  Scratch s{nullptr, nullptr, nullptr};
+  char* base = static_cast<char*>(ws);
+  if (pl.sk_ctas && (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE)) {
+    s.flags = reinterpret_cast<uint32_t*>(base);
+    s.partials = reinterpret_cast<float*>(base + pl.flags_bytes);  // partials after the flags
+  } else if (pl.sk_ctas && pl.reduction == SKG_RED_WORKSPACE) {
+    s.ws = reinterpret_cast<float*>(base);
+  }
+  return s;
+}
+
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  f.shift = s;
+  f.magic = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+  return f;
+}
+
+// Checks shared by both run calls once the plan is known: the workspace
+// covers the plan, and a linear/tree pool fits on the device at once (its
+// CTAs wait on each other, so all of them must be resident).
+int check_run(const skg_plan_t& pl, void* ws, size_t ws_bytes, int cus, int per_cu) {
+  if ((size_t)pl.workspace_bytes > ws_bytes) return unsupported("workspace too small for this plan");
+  if (pl.workspace_bytes && (!ws || !aligned(ws, 256))) return unsupported("workspace must be 256-byte aligned device memory");
+  if ((pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE) && pl.sk_ctas > (int64_t)cus * per_cu)
+    return unsupported("linear/tree stream-K pool exceeds the resident capacity of the device");
+  return SKG_OK;
+}
+
+int reset_scratch(const skg_plan_t& pl, void* ws, hipStream_t st) {
+  if (!pl.sk_ctas) return SKG_OK;
+  hipError_t e = hipSuccess;
+  if (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE)
+    e = hipMemsetAsync(ws, 0, (size_t)pl.flags_bytes, st);
+  else if (pl.reduction == SKG_RED_WORKSPACE)
+    e = hipMemsetAsync(ws, 0, (size_t)pl.workspace_bytes, st);
+  if (e != hipSuccess) return hip_failure(std::string("reset: ") + hipGetErrorString(e));
+  return SKG_OK;
+}
+
+}  // namespace
+}  // namespace skg
+
+using namespace skg;
+
+extern "C" {
+
+int skg_device_info(int32_t op, int32_t tile_id, int32_t dtype_ab, int32_t* num_cus,
+                    int32_t* resident_per_cu) {
+  try {
+    clear_error();
+    if (!num_cus || !resident_per_cu) return unsupported("null output");
+    int c = 0, r = 0;
+    int rc = device_capacity(op, tile_id, dtype_ab, &c, &r);
+    if (rc) return rc;
+    *num_cus = c;
+    *resident_per_cu = r;
+    return SKG_OK;
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+int skg_profile_events(void* start, void* stop) {
+  clear_error();
+  if ((start == nullptr) != (stop == nullptr)) return unsupported("set both events or neither");
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
+  return SKG_OK;
+}
+
+int skg_plan_gemm(const skg_gemm_args_t* a, skg_plan_t* out) {
+  try {
+    clear_error();
+    int rc = validate_gemm(a);
+    if (rc) return rc;
+    if (!out) return unsupported("null output");
+    const TileDesc* t = tile_desc(a->tile_id);
+    int cus = 0, per_cu = 0;
+    if (a->ctas == -1) {
+      rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
+      if (rc) return rc;
+    }
+    return make_plan(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+  } catch (...) {
+    return hip_failure("exception in skg_plan_gemm");
+  }
+}
+
+int skg_plan_wgrad(const skg_wgrad_args_t* a, skg_plan_t* out) {
+  try {
+    clear_error();
+    int rc = validate_wgrad(a);
+    if (rc) return rc;
+    if (!out) return unsupported("null output");
+    const TileDesc* t = tile_desc(a->tile_id);
+    int cus = 0, per_cu = 0;
+    if (a->ctas == -1) {
+      rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
+      if (rc) return rc;
+    }
+    return make_plan(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+  } catch (...) {
+    return hip_failure("exception in skg_plan_wgrad");
+  }
+}
+
+int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    int rc = validate_gemm(a);
+    if (rc) return rc;
+    if (!a->A || !a->B || !a->C) return unsupported("null A, B or C");
+    if (!aligned(a->A, 16) || !aligned(a->B, 16) || !aligned(a->C, 16))
+      return unsupported("A, B and C must be 16-byte aligned");
+    if ((a->scale_a && !aligned(a->scale_a, 16)) || (a->scale_b && !aligned(a->scale_b, 16)))
+      return unsupported("scales must be 16-byte aligned");
+    const TileDesc* t = tile_desc(a->tile_id);
+    GemmInst inst = gemm_instance(a->tile_id, a->dtype_ab);
+    if (!inst.launch) return unsupported("no GEMM instance for this tile and dtype");
+    int cus = 0, per_cu = 0;
+    rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
+    if (rc) return rc;
+    skg_plan_t pl;
+    rc = make_plan(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    if (rc) return rc;
+    rc = check_run(pl, ws, ws_bytes, cus, per_cu);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = reset_scratch(pl, ws, st);
+    if (rc) return rc;
+    if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {
+      hipError_t e = hipMemset2DAsync(a->C, (size_t)a->ldc * 4, 0, (size_t)a->N * 4, (size_t)a->M, st);
+      if (e != hipSuccess) return hip_failure(std::string("zeroing C: ") + hipGetErrorString(e));
+    }
+    GemmParams g;
+    g.A = static_cast<const char*>(a->A);
+    g.B = static_cast<const char*>(a->B);
+    g.C = static_cast<char*>(a->C);
+    g.M = (int)a->M;
+    g.N = (int)a->N;
+    g.K = (int)a->K;
+    g.lda_b = (uint32_t)(a->lda * elem_bytes(a->dtype_ab));
+    g.ldb_b = (uint32_t)(a->ldb * elem_bytes(a->dtype_ab));
+    g.ldc = (int)a->ldc;
+    g.sa = a->scale_a;
+    g.sb = a->scale_b;
+    g.dtype_c = a->dtype_c == SKG_F32 ? DT_F32 : (a->dtype_c == SKG_F16 ? DT_F16 : DT_BF16);
+    hipError_t e = inst.launch(g, to_kplan(pl), carve(pl, ws), st, g_ev_start, g_ev_stop);
+    if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
+    return SKG_OK;
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    int rc = validate_wgrad(a);
+    if (rc) return rc;
+    if (!a->x || !a->dy || !a->dw) return unsupported("null x, dy or dw");
+    if (!aligned(a->x, 16) || !aligned(a->dy, 16) || !aligned(a->dw, 16))
+      return unsupported("x, dy and dw must be 16-byte aligned");
+    const TileDesc* t = tile_desc(a->tile_id);
+    WgradInst inst = wgrad_instance(a->tile_id, a->dtype);
+    if (!inst.launch) return unsupported("no wgrad instance for this tile and dtype");
+    int cus = 0, per_cu = 0;
+    rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
+    if (rc) return rc;
+    skg_plan_t pl;
+    rc = make_plan(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    if (rc) return rc;
+    rc = check_run(pl, ws, ws_bytes, cus, per_cu);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = reset_scratch(pl, ws, st);
+    if (rc) return rc;
+    WgradParams w;
+    w.X = static_cast<const char*>(a->x);
+    w.dY = static_cast<const char*>(a->dy);
+    w.dW = a->dw;
+    w.N = a->n;
+    w.H = a->h;
+    w.W = a->w;
+    w.C = a->c;
+    w.K = a->k;
+    w.R = a->r;
+    w.S = a->s;
+    w.sh = a->stride_h;
+    w.sw = a->stride_w;
+    w.ph = a->pad_h;
+    w.pw = a->pad_w;
+    w.Ho = (a->h + 2 * a->pad_h - a->r) / a->stride_h + 1;
+    w.Wo = (a->w + 2 * a->pad_w - a->s) / a->stride_w + 1;
+    w.cpg = a->c / a->groups;
+    w.kpg = a->k / a->groups;
+    w.mt_per_group = (int)ceil_div(w.kpg, t->tm);
+    w.gemm_n = w.cpg * a->r * a->s;
+    w.kred = a->n * w.Ho * w.Wo;
+    w.x_bytes = (uint32_t)((int64_t)a->n * a->h * a->w * a->c * 2);
+    w.dy_bytes = (uint32_t)((int64_t)w.kred * a->k * 2);
+    w.div_howo = make_fastdiv((uint32_t)(w.Ho * w.Wo));
+    w.div_wo = make_fastdiv((uint32_t)w.Wo);
+    w.div_cpg = make_fastdiv((uint32_t)w.cpg);
+    w.div_s = make_fastdiv((uint32_t)a->s);
+    if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {
+      hipError_t e = hipMemsetAsync(a->dw, 0, (size_t)a->k * w.gemm_n * 4, st);
+      if (e != hipSuccess) return hip_failure(std::string("zeroing dW: ") + hipGetErrorString(e));
+    }
+    hipError_t e = inst.launch(w, to_kplan(pl), carve(pl, ws), st, g_ev_start, g_ev_stop);
+    if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
+    return SKG_OK;
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+}  // extern "C"

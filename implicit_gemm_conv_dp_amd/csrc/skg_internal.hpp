@@ -1,0 +1,50 @@
+// Host-side internals shared by the planner/validator (skg_host.cpp) and the
+// launch code (skg_api.hip).  No device code here.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "skgemm.h"
+
+namespace skg {
+
+// Per-thread reason for the last non-zero status.
+void set_error(const std::string& msg);
+void clear_error();
+
+// Returns -2 after recording msg.
+int unsupported(const std::string& msg);
+// Returns -1 after recording msg.
+int hip_failure(const std::string& msg);
+
+struct TileDesc {
+  int tm, tn, tk, n_waves;
+  int gemm_mask;   // 1 << skg_dtype accepted as GEMM A/B
+  int wgrad_mask;  // 1 << skg_dtype accepted as wgrad X/dY
+};
+
+const TileDesc* tile_desc(int tile_id);
+
+int elem_bytes(int dtype);
+
+// GEMM-shaped view of a problem: what the partitioner needs.
+struct GemmShape {
+  int64_t tiles_m, tiles_n, iters_per_tile;
+};
+
+// Resolves the plan of a GEMM-shaped problem.  pool_default_cus /
+// resident_per_cu are only read when ctas == -1.
+int make_plan(const GemmShape& g, const TileDesc& t, int mode, int reduction,
+              int ctas, int num_cus, int resident_per_cu, skg_plan_t* out);
+
+// Argument checks that need no device (a0 of the hot path).
+int validate_gemm(const skg_gemm_args_t* a);
+int validate_wgrad(const skg_wgrad_args_t* a);
+
+GemmShape gemm_shape(const skg_gemm_args_t* a, const TileDesc& t);
+GemmShape wgrad_shape(const skg_wgrad_args_t* a, const TileDesc& t);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace skg

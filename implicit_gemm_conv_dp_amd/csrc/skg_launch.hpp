@@ -1,0 +1,50 @@
+// Kernel instance table shared by the launch code and the instance units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "skg_kernels.hpp"
+
+namespace skg {
+
+struct GemmInst {
+  hipError_t (*launch)(const GemmParams&, const KPlan&, const Scratch&, hipStream_t, hipEvent_t,
+                       hipEvent_t);
+  hipError_t (*occupancy)(int*);
+};
+
+struct WgradInst {
+  hipError_t (*launch)(const WgradParams&, const KPlan&, const Scratch&, hipStream_t, hipEvent_t,
+                       hipEvent_t);
+  hipError_t (*occupancy)(int*);
+};
+
+// {nullptr, nullptr} when the (tile, dtype) pair has no compiled instance.
+GemmInst gemm_instance(int tile_id, int dtype);
+WgradInst wgrad_instance(int tile_id, int dtype);
+
+// Launches the stream-K kernel (bracketed by ev0 / ev1 when they are set)
+// and, for the workspace reduction, the second stage.
+template <class Cfg, class Prob>
+hipError_t launch_instance(const typename Prob::Params& prm, const KPlan& p, const Scratch& s,
+                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e;
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL((sk_kernel<Cfg, Prob>), dim3(p.grid), dim3(Cfg::THREADS), 0, st, prm, p, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
+  if (p.reduction == RED_WORKSPACE && p.sk_tiles > 0) {
+    const dim3 g2(p.sk_tiles, (Cfg::TM * Cfg::TN + 1023) / 1024);
+    hipLaunchKernelGGL((stage2_kernel<Cfg, Prob>), g2, dim3(256), 0, st, prm, p, s);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <class Cfg, class Prob>
+hipError_t occupancy_instance(int* out) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, sk_kernel<Cfg, Prob>, Cfg::THREADS, 0);
+}
+
+}  // namespace skg

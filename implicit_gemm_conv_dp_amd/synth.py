@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs for the tests, the smoke check and the benchmark.
+
+This module holds none of the engine's arithmetic: it draws numbers with
+numpy's PCG64 generator and stores them in the operand formats through
+torch's CPU casts (float32 -> float16 / bfloat16 / float8_e4m3fn, round to
+nearest even).  Both the HIP path and the CPU oracle read the same stored
+codes.
+
+Seeds: workload ``i`` (1..5) uses base seed ``1000 + i``; its operand streams
+are ``10 * base + 0`` (A, or dY for wgrad), ``+1`` (B, or X), ``+2`` (per-row
+scale of A) and ``+3`` (per-column scale of B).
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
+            "f32": torch.float32}
+CODE_DT = {"f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "f32": np.uint32}
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def draw(dist, n, seed):
+    """float64 draws: ``uniform`` U[-1, 1], ``normal`` N(0, 1), ``normal01``
+    N(0, 1) * 0.1, ``scale`` U[0.5, 2]."""
+    g = rng(seed)
+    if dist == "uniform":
+        return g.uniform(-1.0, 1.0, n)
+    if dist == "normal":
+        return g.standard_normal(n)
+    if dist == "normal01":
+        return g.standard_normal(n) * 0.1
+    if dist == "scale":
+        return g.uniform(0.5, 2.0, n)
+    raise ValueError(dist)
+
+
+def to_codes(values, fmt):
+    """Store float values in ``fmt`` via torch's CPU cast; returns the codes."""
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).to(TORCH_DT[fmt])
+    view = torch.uint8 if fmt == "e4m3" else (torch.int16 if fmt != "f32" else torch.int32)
+    return t.view(view).numpy().view(CODE_DT[fmt])
+
+
+def integer_codes(fmt, n, seed, density, vmax=2):
+    """Sparse small integers in [-vmax, vmax]: every product and partial sum
+    of such operands is exact in fp32."""
+    g = rng(seed)
+    v = g.integers(-vmax, vmax + 1, n).astype(np.float64)
+    v = np.where(g.random(n) < density, v, 0.0)
+    return to_codes(v, fmt)
+
+
+def pow2_scales(n, seed, lo=-2, hi=2):
+    """Power-of-two scales (products with them stay exact)."""
+    return (2.0 ** rng(seed).integers(lo, hi + 1, n)).astype(np.float32)
+
+
+@dataclass
+class GemmWorkload:
+    index: int
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype_ab: str
+    dtype_c: str
+    dist: str
+    tile: str
+    modes: tuple
+    reductions: tuple
+    ctas: int
+    scales: bool = False
+    op: str = "gemm"
+
+    @property
+    def seed(self):
+        return 1000 + self.index
+
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def inputs(self):
+        """dict with A (M*K codes), B (N*K codes, column-major), optional
+        scale_a / scale_b float32 vectors."""
+        s = self.seed * 10
+        out = {
+            "A": to_codes(draw(self.dist, self.M * self.K, s + 0), self.dtype_ab),
+            "B": to_codes(draw(self.dist, self.N * self.K, s + 1), self.dtype_ab),
+        }
+        if self.scales:
+            out["scale_a"] = draw("scale", self.M, s + 2).astype(np.float32)
+            out["scale_b"] = draw("scale", self.N, s + 3).astype(np.float32)
+        return out
+
+
+@dataclass
+class WgradWorkload:
+    index: int
+    name: str
+    n: int
+    h: int
+    w: int
+    c: int
+    k: int
+    r: int
+    s: int
+    stride: tuple
+    pad: tuple
+    groups: int
+    dtype: str
+    dist: str
+    tile: str
+    modes: tuple
+    reductions: tuple
+    ctas: int
+    op: str = "wgrad"
+
+    @property
+    def seed(self):
+        return 1000 + self.index
+
+    @property
+    def out_hw(self):
+        ho = (self.h + 2 * self.pad[0] - self.r) // self.stride[0] + 1
+        wo = (self.w + 2 * self.pad[1] - self.s) // self.stride[1] + 1
+        return ho, wo
+
+    def flops(self):
+        ho, wo = self.out_hw
+        return 2.0 * self.k * (self.c // self.groups) * self.r * self.s * self.n * ho * wo
+
+    def inputs(self):
+        ho, wo = self.out_hw
+        s = self.seed * 10
+        return {
+            "dy": to_codes(draw(self.dist, self.n * ho * wo * self.k, s + 0), self.dtype),
+            "x": to_codes(draw(self.dist, self.n * self.h * self.w * self.c, s + 1), self.dtype),
+        }
+
+
+# The five workloads.  Tiles for 1, 2 and 4 are the ones the workloads name;
+# 3 and 5 use the tiles measured fastest for them.
+WORKLOADS = {
+    1: GemmWorkload(1, "gemm_f16_256x256x4096_pool6_linear", 256, 256, 4096, "f16", "f16",
+                    "uniform", "128x128x32", ("dp_sk",), ("linear",), 6),
+    2: GemmWorkload(2, "gemm_bf16_4864x4096x4096_tree", 4864, 4096, 4096, "bf16", "bf16",
+                    "normal01", "256x256x64", ("dp_sk", "persistent"), ("tree",), 256),
+    3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
+                     (1, 1), (1, 1), 1, "f16", "uniform", "128x128x64",
+                     ("dp_sk", "persistent"), ("linear", "tree", "atomic", "workspace"), 256),
+    4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
+                     (2, 2), (1, 1), 32, "bf16", "uniform", "32x64x64", ("dp_sk",), ("linear",),
+                     256),
+    5: GemmWorkload(5, "gemm_e4m3_8192x8192x8192_rowcol_scales", 8192, 8192, 8192, "e4m3",
+                    "bf16", "normal", "256x256x128", ("persistent",), ("workspace",), 256,
+                    scales=True),
+}

@@ -1,0 +1,223 @@
+/*
+ * skgemm.h -- C ABI of the stream-K GEMM / conv-wgrad engine for gfx950.
+ *
+ * One library, libskgemm.so, serves two workloads with one tiled MFMA
+ * engine:
+ *   - GEMM in the "rcr" layout (row-major A, column-major B, row-major C) on
+ *     fp16, bf16 or OCP fp8 e4m3 inputs with optional per-row A and
+ *     per-column B fp32 scales, fp32 accumulation;
+ *   - backward-weight convolution (wgrad) of NHWC activations as an implicit
+ *     GEMM whose M is the output channels (conv groups folded into M per
+ *     group), N the filter taps times input channels of a group, and whose
+ *     reduction runs over every output pixel of every image.
+ *
+ * Output tiles are split by a host planner into a data-parallel set (whole
+ * waves of the CTA pool) and a stream-K remainder whose MAC iterations are
+ * spread as contiguous, balanced ranges over the pool (rocm-libraries PR
+ * #13151 "feat(rocke): stream-K for implicit-GEMM conv wgrad", Technical
+ * Details: Partitioner).  Tiles shared by several CTAs are fixed up in one of
+ * four ways (same PR, Technical Details: Wgrad kernel): linear and tree are
+ * deterministic hand-offs through per-(CTA, wave) flags with agent-scope
+ * release/acquire; atomic adds fp32 into a zeroed fp32 output; workspace adds
+ * fp32 into zeroed scratch followed by a second-stage reduce.
+ *
+ * Status codes follow the single-problem ABI of the stream-K GEMM bridge
+ * (composable_kernel commit "feat(ck-tile): stream-K GEMM TE to dispatcher
+ * bridge", Changes): 0 success, -1 a HIP error or C++ exception, -2 arguments
+ * the engine does not support.  A -2 is decided on the host before anything
+ * is enqueued, so outputs are untouched; skg_last_error() then names the
+ * reason.  After a -1, work already enqueued may have run.
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs, scales and the
+ * workspace) and every stream; the library allocates no device memory in the
+ * calls below.  Device pointers must be device memory of the current HIP
+ * device.  Calls are asynchronous: 0 means "enqueued on the stream".
+ *
+ * Thread safety: all calls may be made from several host threads; the last
+ * error string is per thread.  Two calls that share a workspace buffer must
+ * not overlap in time on the device.
+ */
+#ifndef SKGEMM_H
+#define SKGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKG_OK 0
+#define SKG_ERR_HIP (-1)
+#define SKG_ERR_UNSUPPORTED (-2)
+
+/* Element types. */
+enum skg_dtype {
+  SKG_F16 = 0,     /* IEEE binary16 */
+  SKG_BF16 = 1,    /* bfloat16 */
+  SKG_F8E4M3 = 2,  /* OCP fp8 E4M3 (bias 7, max 448, no inf), the gfx950 fp8 */
+  SKG_F32 = 3      /* IEEE binary32 (outputs only) */
+};
+
+/* Launch modes (PR #13151, Technical Details: Wgrad kernel, launch modes).
+ *   SKG_MODE_DP         every tile is data-parallel, grid = tiles (the
+ *                       comparator the stream-K launch is measured against);
+ *   SKG_MODE_DP_SK      grid = stream-K CTAs (block ids 0..sk_ctas-1) then
+ *                       one CTA per data-parallel tile;
+ *   SKG_MODE_PERSISTENT grid = the pool; each CTA runs its stream-K range,
+ *                       then data-parallel tiles b, b+grid, ... */
+enum skg_mode { SKG_MODE_DP = 0, SKG_MODE_DP_SK = 1, SKG_MODE_PERSISTENT = 2 };
+
+/* Fix-up of tiles shared by several stream-K CTAs (PR #13151, same section).
+ *   LINEAR     deterministic: the owner folds the contributors in CTA order;
+ *   TREE       deterministic: pairwise folds in ceil(log2 n) rounds;
+ *   ATOMIC     fp32 atomics into the output, which must be fp32 (the call
+ *              zeroes it first);
+ *   WORKSPACE  fp32 atomics into scratch, then a second-stage kernel applies
+ *              the epilogue and writes the output. */
+enum skg_reduction {
+  SKG_RED_LINEAR = 0,
+  SKG_RED_TREE = 1,
+  SKG_RED_ATOMIC = 2,
+  SKG_RED_WORKSPACE = 3
+};
+
+/* Compiled tile instances.  TM x TN x TK in elements; each instance exists
+ * for the operations and input types skg_tile_info reports. */
+enum skg_tile {
+  SKG_TILE_128x128x32 = 0,   /* f16/bf16 GEMM and wgrad, 4 waves */
+  SKG_TILE_256x256x64 = 1,   /* f16/bf16 GEMM, 4 waves */
+  SKG_TILE_256x256x128 = 2,  /* fp8 GEMM, 4 waves */
+  SKG_TILE_32x64x64 = 3,     /* f16/bf16 wgrad (small per-group M), 4 waves */
+  SKG_TILE_128x128x64 = 4,   /* f16/bf16 GEMM and wgrad, 4 waves */
+  SKG_TILE_256x128x64 = 5,   /* f16/bf16 GEMM and wgrad, 4 waves */
+  SKG_TILE_COUNT = 6
+};
+
+enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1 };
+
+typedef struct skg_tile_info {
+  int32_t tm, tn, tk;      /* tile in elements */
+  int32_t n_waves;         /* wave64s per CTA (one flag per CTA and wave) */
+  int32_t gemm_dtypes;     /* bit mask of 1 << skg_dtype accepted for GEMM A/B */
+  int32_t wgrad_dtypes;    /* bit mask accepted for wgrad X/dY (0: no wgrad) */
+} skg_tile_info_t;
+
+/* GEMM problem.  A is M x K row-major with leading dimension lda (elements),
+ * B is K x N column-major (column n is K contiguous elements at B + n*ldb),
+ * C is M x N row-major with leading dimension ldc.  scale_a (M floats) and
+ * scale_b (N floats) are optional (NULL means 1.0); the epilogue computes
+ * C[m][n] = round_to_nearest_even((acc * scale_a[m]) * scale_b[n]) in fp32
+ * ("gemm_rowcolquant dispatcher bridge" PR, final description: scales applied
+ * in the epilogue, fp32 accumulator narrowed only there).
+ * Alignment: A, B, C 16-byte aligned; lda, ldb multiples of 16 bytes; K a
+ * multiple of 16 bytes of input type. */
+typedef struct skg_gemm_args {
+  int64_t M, N, K;
+  int32_t dtype_ab;        /* SKG_F16, SKG_BF16 or SKG_F8E4M3 */
+  int32_t dtype_c;         /* SKG_F16, SKG_BF16 or SKG_F32 */
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  const float* scale_a;    /* device pointer (16-byte aligned) or NULL */
+  const float* scale_b;    /* device pointer (16-byte aligned) or NULL */
+  int32_t tile_id;         /* enum skg_tile */
+  int32_t mode;            /* enum skg_mode */
+  int32_t reduction;       /* enum skg_reduction */
+  int32_t ctas;            /* stream-K pool; -1 = default pool; 0 or < -1 rejected */
+} skg_gemm_args_t;
+
+/* wgrad problem (PR #13151, Motivation and Technical Details).  X is the
+ * forward input, NHWC (n, h, w, c); dY the output gradient, NHWC with
+ * Ho = (h + 2*pad_h - r)/stride_h + 1 and Wo likewise (dilation 1); dW the
+ * filter gradient, fp32, K x R x S x (C/groups) row-major.  Group g maps input
+ * channels [g*C/groups, (g+1)*C/groups) to output channels
+ * [g*K/groups, (g+1)*K/groups).  C/groups must be a multiple of 8 and
+ * K/groups a multiple of 8; X, dY, dW 16-byte aligned. */
+typedef struct skg_wgrad_args {
+  int32_t n, h, w, c, k, r, s;
+  int32_t stride_h, stride_w, pad_h, pad_w, groups;
+  int32_t dtype;           /* SKG_F16 or SKG_BF16 (X and dY) */
+  const void* x;
+  const void* dy;
+  float* dw;
+  int32_t tile_id, mode, reduction, ctas;
+} skg_wgrad_args_t;
+
+/* Resolved launch plan, returned by value so that no derived quantity is
+ * recomputed elsewhere with different rounding (PR #13151, commit adding the
+ * iteration partitioner).  Iterations are MAC iterations: one TM x TN x TK
+ * block of one output tile. */
+typedef struct skg_plan {
+  int32_t tm, tn, tk, n_waves;
+  int32_t mode, reduction;
+  int64_t tiles_m, tiles_n, tiles;
+  int64_t iters_per_tile;
+  int64_t pool;
+  int64_t dp_tiles, sk_tiles, sk_ctas, sk_iters;
+  int64_t iters_per_sk_cta;  /* clamped to >= 1, also for all-DP plans */
+  int64_t extra_iters;       /* the first extra_iters stream-K CTAs run one more */
+  int64_t grid;
+  int64_t max_contrib;       /* most CTAs sharing one tile (1 when all-DP) */
+  int64_t linear_partners;   /* max_contrib - 1 */
+  int64_t tree_rounds;       /* ceil(log2(max_contrib)) */
+  int64_t flags_bytes;       /* 4 * sk_ctas * n_waves rounded up to 256 (linear/tree) */
+  int64_t partials_bytes;    /* sk_ctas * TM * TN * 4 (linear/tree) */
+  int64_t workspace_bytes;   /* bytes the caller must pass as ws */
+} skg_plan_t;
+
+/* Reason for the last non-zero status on this thread ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char* skg_last_error(void);
+
+/* Tile instance table.  -2 for an unknown tile id. */
+int skg_tile_info(int32_t tile_id, skg_tile_info_t* out);
+
+/* Default pool for ctas = -1 (PR #13151, commits sizing the default pool):
+ * one CTA per CU for linear/tree, whose CTAs wait on later CTAs; four per CU
+ * for atomic/workspace, which never wait; never more per CU than
+ * resident_per_cu.  Pure host function.  -2 on an unknown reduction or
+ * non-positive counts. */
+int skg_default_pool(int32_t reduction, int32_t num_cus, int32_t resident_per_cu,
+                     int32_t* out);
+
+/* Compute units of the current device and how many CTAs of the given kernel
+ * instance stay resident per CU.  -1 if no HIP device is usable, -2 for an
+ * unknown instance or a device that is not gfx950. */
+int skg_device_info(int32_t op, int32_t tile_id, int32_t dtype_ab,
+                    int32_t* num_cus, int32_t* resident_per_cu);
+
+/* Plans.  Pure host functions except for ctas = -1, which asks the current
+ * device for its CU count (skg_device_info).  Pointers in args are ignored.
+ * 0, -1 (device query failed) or -2 (arguments unsupported, reason in
+ * skg_last_error). */
+int skg_plan_gemm(const skg_gemm_args_t* args, skg_plan_t* out);
+int skg_plan_wgrad(const skg_wgrad_args_t* args, skg_plan_t* out);
+
+/* Run.  ws must point to at least plan.workspace_bytes of device memory
+ * (may be NULL when that is 0); the call resets on the stream whatever the
+ * reduction accumulates into: the flags (linear/tree), the scratch
+ * (workspace) or C itself (atomic).  Partials and, for linear/tree, C are
+ * never pre-zeroed.  Linear and tree results are bit-identical from launch to
+ * launch.  For linear/tree the stream-K CTAs must all be resident at once, so
+ * a pool larger than the device's resident capacity for the instance is
+ * rejected with -2.  stream is a hipStream_t (NULL: the null stream). */
+int skg_run_gemm(const skg_gemm_args_t* args, void* ws, size_t ws_bytes, void* stream);
+int skg_run_wgrad(const skg_wgrad_args_t* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Timing hook for measurement: while set on the calling thread, every run
+ * call records `start` (a hipEvent_t) on its stream immediately before the
+ * stream-K kernel and `stop` immediately after it -- after the resets and
+ * before any second stage -- so the pair times that kernel alone.  Both NULL
+ * clears the hook; passing only one is -2.  The events stay owned by the
+ * caller. */
+int skg_profile_events(void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKGEMM_H */

@@ -1,0 +1,167 @@
+"""GPU parity of the GEMM path against the oracle (through the C ABI).
+
+* Every tile instance x launch mode x fix-up on ragged shapes that span
+  several tiles and split tiles between up to four stream-K CTAs, on random
+  data (tolerance 5e-3 for fp16/bf16 inputs, 2e-2 for fp8) and on
+  integer-exact data (bit-exact: every product and fp32 partial sum is exact,
+  so any missed or repeated MAC iteration shows).
+* The five workloads' GEMMs at full size in the launch configuration the
+  benchmark times, checked on sampled entries computed one by one by the
+  oracle, plus the whole output scanned for unwritten rows.
+* Unsupported arguments come back as -2 with the output untouched.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_conv_dp_amd as skg
+from implicit_gemm_conv_dp_amd import synth
+from oracle import codecs
+from oracle.gemm import gemm as oracle_gemm, gemm_entry
+
+from helpers import TOL, assert_close, decode_out, out_buffer, rel_err, to_dev, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["dp", "dp_sk", "persistent"]
+REDS = ["linear", "tree", "atomic", "workspace"]
+TILE_DT = [("128x128x32", "f16"), ("128x128x32", "bf16"), ("256x256x64", "bf16"),
+           ("256x256x64", "f16"), ("128x128x64", "bf16"), ("256x128x64", "f16"),
+           ("256x256x128", "e4m3")]
+
+
+def run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa=None, sb=None, ws=None, C=None):
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    dC = C if C is not None else out_buffer(fmt_c, M * N)
+    dsa = to_dev_f32(sa) if sa is not None else None
+    dsb = to_dev_f32(sb) if sb is not None else None
+    plan = skg.gemm(dA, dB, dC, dsa, dsb, workspace=ws, M=M, N=N, K=K, dtype_ab=fmt,
+                    dtype_c=fmt_c, tile=tile, mode=mode, reduction=red, ctas=ctas)
+    torch.cuda.synchronize()
+    return decode_out(dC, fmt_c).reshape(M, N), plan
+
+
+def shape_for(tile):
+    tm, tn, tk = map(int, tile.split("x"))
+    # 3 x 2 tiles with ragged last row and column of tiles, 24 MAC iterations.
+    return 2 * tm + tm // 3 + 8, tn + tn // 2 + 8, 24 * tk
+
+
+@pytest.mark.parametrize("tile,fmt", TILE_DT)
+def test_random_all_modes_and_fixups(tile, fmt):
+    M, N, K = shape_for(tile)
+    g = synth.rng(11)
+    dist = "normal" if fmt == "e4m3" else "uniform"
+    A = synth.to_codes(synth.draw(dist, M * K, 1), fmt)
+    B = synth.to_codes(synth.draw(dist, N * K, 2), fmt)
+    sa = synth.draw("scale", M, 3).astype(np.float32)
+    sb = synth.draw("scale", N, 4).astype(np.float32)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            for ctas in (4, 7, 13):
+                fmt_c = "f32" if red == "atomic" else ("bf16" if int(g.integers(2)) else "f16")
+                if fmt_c == "f16" and fmt == "e4m3":
+                    fmt_c = "bf16"
+                Y, plan = run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa, sb)
+                assert_close(Y, R, fmt, "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas))
+                if mode == "dp":
+                    break
+
+
+@pytest.mark.parametrize("tile,fmt", TILE_DT)
+def test_integer_exact_all_modes_and_fixups(tile, fmt):
+    M, N, K = shape_for(tile)
+    A = synth.integer_codes(fmt, M * K, 21, 0.3)
+    B = synth.integer_codes(fmt, N * K, 22, 0.3)
+    sa = synth.pow2_scales(M, 23)
+    sb = synth.pow2_scales(N, 24)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
+    assert np.max(np.abs(R)) < 2048 / 16      # exact in every output format
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            for ctas in (5, 13):
+                fmt_c = "f32" if red == "atomic" else "bf16"
+                Y, plan = run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa, sb)
+                label = "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas)
+                assert np.array_equal(Y, R), label + ": not bit-exact (max diff %g)" % np.nanmax(np.abs(Y - R))
+
+
+def test_plan_reaches_four_contributors():
+    # The random/integer matrix above must exercise folds of up to four CTAs.
+    M, N, K = shape_for("128x128x32")
+    plan = skg.plan_gemm(M=M, N=N, K=K, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                         mode="dp_sk", reduction="tree", ctas=13)
+    assert plan["max_contrib"] >= 3 and plan["tree_rounds"] >= 2
+
+
+def test_unsupported_args_leave_output_untouched():
+    M, N, K = 64, 64, 64
+    A = synth.to_codes(synth.draw("uniform", M * K, 1), "f16")
+    dA, dB = to_dev(A, "f16"), to_dev(A, "f16")
+    dC = out_buffer("f16", M * N)
+    before = dC.clone()
+    bad = [dict(reduction="atomic"),                  # atomic needs an fp32 C
+           dict(ctas=0), dict(ctas=-3), dict(K=60),   # K not 16-byte multiple
+           dict(tile="256x256x128"),                  # fp8-only tile
+           dict(mode=7)]
+    for b in bad:
+        kw = dict(M=M, N=N, K=K, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                  mode="dp_sk", reduction="linear", ctas=4)
+        kw.update(b)
+        with pytest.raises(skg.SkgError) as ei:
+            skg.gemm(dA, dB, dC, workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"),
+                     **kw)
+        assert ei.value.status == -2, b
+    torch.cuda.synchronize()
+    assert torch.equal(before, dC)
+    # a workspace smaller than the plan needs
+    with pytest.raises(skg.SkgError) as ei:
+        skg.gemm(dA, dB, dC, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"), M=M,
+                 N=N, K=K, dtype_ab="f16", dtype_c="f16", tile="128x128x32", mode="dp_sk",
+                 reduction="linear", ctas=3)
+    assert ei.value.status == -2
+
+
+def test_default_pool_and_device():
+    cus, per_cu = skg.skg_device_info(0, skg.TILES["256x256x64"], skg.DTYPES["bf16"])
+    assert cus >= 1 and per_cu >= 1
+    plan = skg.plan_gemm(M=4864, N=4096, K=4096, dtype_ab="bf16", dtype_c="bf16",
+                         tile="256x256x64", mode="dp_sk", reduction="tree", ctas=-1)
+    assert plan["pool"] == cus
+    plan = skg.plan_gemm(M=4864, N=4096, K=4096, dtype_ab="bf16", dtype_c="bf16",
+                         tile="256x256x64", mode="dp_sk", reduction="workspace", ctas=-1)
+    assert plan["pool"] == cus * min(4, per_cu)
+
+
+def sampled_check(Y, wl, inp, n=1500):
+    g = synth.rng(99)
+    ms = g.integers(0, wl.M, n)
+    ns = g.integers(0, wl.N, n)
+    ref = np.array([gemm_entry(wl.dtype_ab, inp["A"], inp["B"], int(m), int(c), wl.K,
+                               scale_a=inp.get("scale_a"), scale_b=inp.get("scale_b"))
+                    for m, c in zip(ms, ns)])
+    got = Y[ms, ns]
+    return rel_err(got, ref)
+
+
+@pytest.mark.parametrize("index", [1, 2, 5])
+def test_workload_full_size(index):
+    wl = synth.WORKLOADS[index]
+    inp = wl.inputs()
+    for mode in wl.modes:
+        for red in wl.reductions:
+            Y, plan = run(inp["A"], inp["B"], wl.M, wl.N, wl.K, wl.dtype_ab, wl.dtype_c, wl.tile,
+                          mode, red, wl.ctas, inp.get("scale_a"), inp.get("scale_b"))
+            assert not np.isnan(Y).any(), "unwritten outputs"
+            if index == 1:
+                R = oracle_gemm(wl.dtype_ab, inp["A"], inp["B"], wl.M, wl.N, wl.K)
+                assert_close(Y, R, wl.dtype_ab, wl.name)
+            else:
+                err = sampled_check(Y, wl, inp)
+                assert err <= TOL[wl.dtype_ab], "%s %s %s: %.3e" % (wl.name, mode, red, err)

@@ -1,0 +1,278 @@
+"""CPU tests of the HIP library's host side (no GPU needed, no compute calls).
+
+* libskgemm.so loads and exports every function include/skgemm.h declares.
+* The C++ planner equals the oracle partitioner field by field over a sweep
+  of GEMM and wgrad shapes, tiles, modes, reductions and pools.
+* Unsupported arguments are rejected with -2 and a reason.
+* The built gfx950 code object orders the flag hand-off as the AMDGPU memory
+  model prescribes: L2 write-back before the flag store of a publish, an
+  agent-coherent poll and an L2 invalidate after it (rocm-libraries PR #13151,
+  test plan: flag ordering pinned in the ISA).
+"""
+
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import implicit_gemm_conv_dp_amd as skg
+from implicit_gemm_conv_dp_amd import _lib
+from oracle import partition as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skgemm.h")
+TILES = {name: tuple(map(int, name.split("x"))) for name in skg.TILES}
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(skg_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert {"skg_run_gemm", "skg_run_wgrad", "skg_plan_gemm", "skg_plan_wgrad",
+            "skg_last_error", "skg_default_pool", "skg_device_info", "skg_tile_info"} <= set(names)
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
+
+
+def test_tile_table():
+    for name, tid in skg.TILES.items():
+        info = skg.skg_tile_info(tid)
+        assert (info.tm, info.tn, info.tk) == TILES[name]
+        assert info.n_waves == 4
+    with pytest.raises(skg.SkgError) as ei:
+        skg.skg_tile_info(99)
+    assert ei.value.status == -2
+
+
+def test_default_pool_matches_oracle_and_pages():
+    # 304 CUs x 4 = 1216 for the atomic / workspace reductions.
+    assert skg.skg_default_pool(_lib.RED_WORKSPACE, 304, 8) == 1216
+    for red, name in [(0, "linear"), (1, "tree"), (2, "atomic"), (3, "workspace")]:
+        for cus in (1, 80, 256, 304):
+            for per in (1, 2, 3, 8):
+                assert skg.skg_default_pool(red, cus, per) == P.default_pool(name, cus, per)
+    for bad in [(7, 256, 1), (0, 0, 1), (0, 256, 0)]:
+        with pytest.raises(skg.SkgError) as ei:
+            skg.skg_default_pool(*bad)
+        assert ei.value.status == -2
+
+
+FIELDS = ["tiles_m", "tiles_n", "tiles", "iters_per_tile", "pool", "dp_tiles", "sk_tiles",
+          "sk_ctas", "sk_iters", "iters_per_sk_cta", "extra_iters", "grid", "max_contrib",
+          "linear_partners", "tree_rounds", "flags_bytes", "partials_bytes", "workspace_bytes"]
+
+
+def same_plan(c, o):
+    for f in FIELDS:
+        ov = getattr(o, f)
+        assert c[f] == ov, (f, c[f], ov)
+
+
+GEMM_TILE_DT = [("128x128x32", "f16"), ("256x256x64", "bf16"), ("256x256x128", "e4m3"),
+                ("128x128x64", "bf16"), ("256x128x64", "f16")]
+
+
+@pytest.mark.parametrize("tile,dt", GEMM_TILE_DT)
+def test_gemm_plan_equals_oracle(tile, dt):
+    tm, tn, tk = TILES[tile]
+    n = 0
+    for M in (1, tm - 1, tm, 3 * tm + 5, 4864):
+        for N in (16, tn, 2 * tn + 8, 4096):
+            for K in (tk, 5 * tk, 4096 + tk):
+                for mode in ("dp", "dp_sk", "persistent"):
+                    for red in ("linear", "tree", "atomic", "workspace"):
+                        for ctas in (1, 6, 77, 256, 1216):
+                            dtc = "f32" if red == "atomic" else "bf16"
+                            c = skg.plan_gemm(M=M, N=N, K=K, dtype_ab=dt, dtype_c=dtc, tile=tile,
+                                              mode=mode, reduction=red, ctas=ctas)
+                            tiles = P.gemm_tiles(M, N, K, tm, tn, tk)
+                            o = P.plan(*tiles, tm, tn, 4, mode, red, ctas)
+                            same_plan(c, o)
+                            n += 1
+    assert n > 1000
+
+
+def test_workload_plans():
+    # 256x256x4096 fp16 over a 6-CTA pool: the survey's straddling ranges.
+    c = skg.plan_gemm(M=256, N=256, K=4096, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                      mode="dp_sk", reduction="linear", ctas=6)
+    assert (c["sk_ctas"], c["iters_per_sk_cta"], c["extra_iters"], c["max_contrib"]) == (6, 85, 2, 3)
+    c = skg.plan_gemm(M=4864, N=4096, K=4096, dtype_ab="bf16", dtype_c="bf16", tile="256x256x64",
+                      mode="dp_sk", reduction="tree", ctas=256)
+    assert (c["dp_tiles"], c["sk_tiles"], c["iters_per_sk_cta"], c["tree_rounds"],
+            c["flags_bytes"]) == (256, 48, 12, 3, 4096)
+    c = skg.plan_gemm(M=8192, N=8192, K=8192, dtype_ab="e4m3", dtype_c="bf16", tile="256x256x128",
+                      mode="persistent", reduction="workspace", ctas=256)
+    assert c["sk_ctas"] == 0 and c["grid"] == 256 and c["workspace_bytes"] == 0
+
+
+WGRAD_SHAPES = [
+    (32, 56, 56, 256, 256, 3, 3, (1, 1), (1, 1), 1),
+    (64, 28, 28, 512, 512, 3, 3, (2, 2), (1, 1), 32),
+    (2, 9, 9, 16, 24, 3, 3, (1, 1), (1, 1), 1),
+    (3, 11, 10, 32, 16, 3, 3, (2, 2), (1, 1), 1),
+    (2, 12, 12, 64, 32, 3, 3, (2, 2), (1, 1), 4),
+    (1, 17, 15, 144, 40, 3, 2, (1, 2), (1, 0), 1),
+]
+
+
+@pytest.mark.parametrize("tile", ["128x128x32", "32x64x64", "128x128x64", "256x128x64"])
+def test_wgrad_plan_equals_oracle(tile):
+    tm, tn, tk = TILES[tile]
+    for (n, h, w, c, k, r, s, st, pd, g) in WGRAD_SHAPES:
+        for mode in ("dp", "dp_sk", "persistent"):
+            for red in ("linear", "tree", "atomic", "workspace"):
+                for ctas in (3, 7, 11, 256, 1024):
+                    cp = skg.plan_wgrad(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st, pad=pd,
+                                        groups=g, dtype="bf16", tile=tile, mode=mode,
+                                        reduction=red, ctas=ctas)
+                    tiles = P.wgrad_tiles(n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g,
+                                          tm, tn, tk)
+                    same_plan(cp, P.plan(*tiles, tm, tn, 4, mode, red, ctas))
+
+
+def rejected(fn, **kw):
+    with pytest.raises(skg.SkgError) as ei:
+        fn(**kw)
+    assert ei.value.status == -2
+    assert ei.value.msg
+    return ei.value.msg
+
+
+def test_gemm_validation_rejects():
+    base = dict(M=256, N=256, K=256, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                mode="dp_sk", reduction="linear", ctas=8)
+
+    def bad(**over):
+        kw = dict(base)
+        kw.update(over)
+        return rejected(skg.plan_gemm, **kw)
+
+    assert "atomic" in bad(reduction="atomic")
+    assert "ctas" in bad(ctas=0)
+    assert "ctas" in bad(ctas=-5)
+    assert "mode" in bad(mode=9)
+    assert "reduction" in bad(reduction=9)
+    assert "tile" in bad(tile=17)
+    assert "instance" in bad(tile="256x256x128")
+    assert "instance" in bad(dtype_ab="e4m3")
+    assert "dtype" in bad(dtype_c="e4m3")
+    assert "positive" in bad(M=0)
+    assert "16 bytes" in bad(K=100)
+    assert "leading" in bad(lda=128)
+    assert "16 bytes" in bad(ldc=257)
+
+
+def test_wgrad_validation_rejects():
+    base = dict(n=2, h=9, w=9, c=16, k=24, r=3, s=3, stride=(1, 1), pad=(1, 1), groups=1,
+                dtype="bf16", tile="128x128x64", mode="dp_sk", reduction="linear", ctas=8)
+
+    def bad(**over):
+        kw = dict(base)
+        kw.update(over)
+        return rejected(skg.plan_wgrad, **kw)
+
+    assert "groups" in bad(groups=3)
+    assert "multiples of 8" in bad(c=12)
+    assert "dtype" in bad(dtype="e4m3")
+    assert "instance" in bad(tile="256x256x64")
+    assert "empty" in bad(h=1, pad=(0, 0))
+    assert "stride" in bad(stride=(0, 1))
+    assert "ctas" in bad(ctas=0)
+
+
+def test_default_pool_needs_a_device():
+    # Without a GPU the default pool cannot be resolved: -1 (HIP error), and
+    # the library stays usable.
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    with pytest.raises(skg.SkgError) as ei:
+        skg.plan_gemm(M=256, N=256, K=256, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                      mode="dp_sk", reduction="linear", ctas=-1)
+    assert ei.value.status == -1
+    assert skg.plan_gemm(M=256, N=256, K=256, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+                         mode="dp_sk", reduction="linear", ctas=4)["pool"] == 4
+
+
+# --- flag ordering in the built code object -------------------------------
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def code_objects(tmp):
+    """Disassembly of every gfx950 code object bundled in the library."""
+    fat = os.path.join(tmp, "fatbin")
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section",
+                    ".hip_fatbin=" + fat, _lib.LIB_PATH, os.path.join(tmp, "lib.copy")],
+                   check=True, capture_output=True)
+    data = open(fat, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+    out = []
+    for i, s in enumerate(starts):
+        e = starts[i + 1] if i + 1 < len(starts) else len(data)
+        part = os.path.join(tmp, "b%d" % i)
+        open(part, "wb").write(data[s:e])
+        co = part + ".co"
+        r = subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--type=o", "--unbundle",
+                            "--input=" + part, "--output=" + co,
+                            "--targets=hipv4-amdgcn-amd-amdhsa--gfx950"], capture_output=True)
+        if r.returncode != 0 or not os.path.getsize(co):
+            continue
+        dis = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", co], check=True,
+                             capture_output=True, text=True).stdout
+        out.append(dis)
+    return out
+
+
+def kernels(dis):
+    parts = re.split(r"\n[0-9a-f]+ <(\w+)>:\n", dis)
+    return {parts[i]: parts[i + 1] for i in range(1, len(parts) - 1, 2)}
+
+
+def instrs(body):
+    res = []
+    for line in body.split("\n"):
+        t = line.strip()
+        if not t or t.startswith(";"):
+            continue
+        res.append(t.split("//")[0].strip())
+    return res
+
+
+def test_flag_ordering_in_isa():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = code_objects(tmp)
+    assert objs, "no gfx950 code object in the library"
+    n_kernels = 0
+    for dis in objs:
+        for name, body in kernels(dis).items():
+            if "sk_kernel" not in name:
+                continue
+            n_kernels += 1
+            ins = instrs(body)
+            wbl2 = [i for i, x in enumerate(ins) if x.startswith("buffer_wbl2 sc1")]
+            inv = [i for i, x in enumerate(ins) if x.startswith("buffer_inv sc1")]
+            assert wbl2 and inv, name
+            for i in wbl2:
+                # all earlier stores complete, L2 written back, then the flag store
+                assert any(x.startswith("s_waitcnt vmcnt(0)") for x in ins[max(0, i - 4):i]), name
+                nxt = [x for x in ins[i + 1:i + 4] if not x.startswith("s_")]
+                assert nxt and nxt[0].startswith("global_store_dword") and nxt[0].endswith("sc1"), name
+            for i in inv:
+                assert ins[i - 1].startswith("s_waitcnt vmcnt(0)"), name
+            polls = [x for x in ins if x.startswith("global_load_dword ") and x.endswith("sc1")]
+            assert polls, name + ": no agent-coherent poll"
+    assert n_kernels >= 17
