@@ -16,13 +16,13 @@ element type is ``dtype_ab`` / ``dtype_c``.  ``wgrad`` takes NHWC ``x`` and
 
 from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
-                   skg_plan_wgrad, skg_run_gemm, skg_run_wgrad, skg_tile_info, MODES,
-                   REDUCTIONS, DTYPES, TILES)
+                   skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
+                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES)
 
 __all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
            "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
-           "skg_run_gemm", "skg_run_wgrad", "skg_tile_info"]
+           "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events"]
 
 
 def _enum(table, v, what):

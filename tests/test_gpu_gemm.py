@@ -72,23 +72,32 @@ def test_random_all_modes_and_fixups(tile, fmt):
                     break
 
 
+def exact_in(fmt_c, R):
+    if fmt_c == "f32":
+        return np.array_equal(R.astype(np.float32).astype(np.float64), R)
+    return np.array_equal(codecs.decode(fmt_c, codecs.encode(fmt_c, R)), R)
+
+
 @pytest.mark.parametrize("tile,fmt", TILE_DT)
 def test_integer_exact_all_modes_and_fixups(tile, fmt):
     M, N, K = shape_for(tile)
-    A = synth.integer_codes(fmt, M * K, 21, 0.3)
-    B = synth.integer_codes(fmt, N * K, 22, 0.3)
+    A = synth.integer_codes(fmt, M * K, 21, 0.15)
+    B = synth.integer_codes(fmt, N * K, 22, 0.15)
     sa = synth.pow2_scales(M, 23)
     sb = synth.pow2_scales(N, 24)
     R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
-    assert np.max(np.abs(R)) < 2048 / 16      # exact in every output format
+    outs = [f for f in ("f16", "bf16", "f32") if exact_in(f, R)]
+    assert "f32" in outs and len(outs) >= 2, outs
+    k = 0
     for mode in MODES:
         for red in REDS:
             if mode == "dp" and red != "linear":
                 continue
             for ctas in (5, 13):
-                fmt_c = "f32" if red == "atomic" else "bf16"
+                fmt_c = "f32" if red == "atomic" else outs[k % len(outs)]
+                k += 1
                 Y, plan = run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa, sb)
-                label = "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas)
+                label = "%s %s %s %s ctas=%d -> %s" % (tile, fmt, mode, red, ctas, fmt_c)
                 assert np.array_equal(Y, R), label + ": not bit-exact (max diff %g)" % np.nanmax(np.abs(Y - R))
 
 
@@ -120,12 +129,19 @@ def test_unsupported_args_leave_output_untouched():
         assert ei.value.status == -2, b
     torch.cuda.synchronize()
     assert torch.equal(before, dC)
-    # a workspace smaller than the plan needs
+    # a workspace smaller than the plan needs (one tile of 20 iterations
+    # over 3 stream-K CTAs needs flags and partials)
+    K2 = 640
+    A2 = synth.to_codes(synth.draw("uniform", M * K2, 1), "f16")
+    dA2 = to_dev(A2, "f16")
+    kw = dict(M=M, N=N, K=K2, dtype_ab="f16", dtype_c="f16", tile="128x128x32", mode="dp_sk",
+              reduction="linear", ctas=3)
+    assert skg.plan_gemm(**kw)["workspace_bytes"] > 16
     with pytest.raises(skg.SkgError) as ei:
-        skg.gemm(dA, dB, dC, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"), M=M,
-                 N=N, K=K, dtype_ab="f16", dtype_c="f16", tile="128x128x32", mode="dp_sk",
-                 reduction="linear", ctas=3)
-    assert ei.value.status == -2
+        skg.gemm(dA2, dA2, dC, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"), **kw)
+    assert ei.value.status == -2 and "workspace" in ei.value.msg
+    torch.cuda.synchronize()
+    assert torch.equal(before, dC)
 
 
 def test_default_pool_and_device():
