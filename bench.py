@@ -43,7 +43,23 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the measured HBM bytes per launch of the kernel")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the workload, run a plain device copy of MIB MiB "
+                         "(the reference for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": steps}), flush=True)
 
 
 def alg_bytes(wl):
@@ -101,6 +117,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import numpy as np
     import torch

@@ -38,6 +38,21 @@ SKG_DEV i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+// 16 bytes per lane from buffer offset voff straight into LDS: lane i lands
+// at LDS byte address lds_base + 16*i (lds_base is wave-uniform).  Written
+// as assembly so that the compiler does not track it: its own conservative
+// wait before every later LDS read would serialise the pipeline, and the
+// engine orders these loads with explicit vmcnt waits and barriers instead.
+// (Loads the compiler cannot see only make its own vmcnt waits stricter.)
+SKG_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds_base), "s"(r)
+               : "memory", "m0");
+}
+
+SKG_DEV uint32_t lds_addr(const SKG_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
 // ---------------------------------------------------------------------------
 // Cross-CTA hand-off (rocm-libraries PR #13151, commit adding the fence and
 // flag leaf ops): a contributor's release store at agent scope makes its
@@ -96,62 +111,76 @@ template <>
 struct Mfma<DT_F16, 32> {
   static constexpr int OPB = 16, KB = 32, NACC = 16;
   typedef f32x16 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
-                                               __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+  typedef i32x4 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 };
 template <>
 struct Mfma<DT_BF16, 32> {
   static constexpr int OPB = 16, KB = 32, NACC = 16;
   typedef f32x16 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  typedef i32x4 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
 template <>
 struct Mfma<DT_F16, 16> {
   static constexpr int OPB = 16, KB = 64, NACC = 4;
   typedef f32x4 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[0]),
-                                               __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+  typedef i32x4 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 };
 template <>
 struct Mfma<DT_BF16, 16> {
   static constexpr int OPB = 16, KB = 64, NACC = 4;
   typedef f32x4 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  typedef i32x4 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
 // fp8 (OCP E4M3 on gfx950): the f8f6f4 family with K = 64 (32x32) or 128
-// (16x16) per instruction; format code 0 selects E4M3 for both operands and
-// the e8m0 block scales are fixed at 127 (2^0): the row and column scales are
-// applied in the epilogue instead.
+// (16x16) per instruction; format code 0 selects E4M3 for both operands.
+// Zero scale operands select the unscaled instruction (no block scales, and
+// it keeps its accumulator in AGPRs); the row and column scales are applied
+// in the epilogue instead.
 template <>
 struct Mfma<DT_F8, 32> {
   static constexpr int OPB = 32, KB = 64, NACC = 16;
   typedef f32x16 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    const i32x8 av = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
-    const i32x8 bv = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
-    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+  typedef i32x8 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
 template <>
 struct Mfma<DT_F8, 16> {
   static constexpr int OPB = 32, KB = 128, NACC = 4;
   typedef f32x4 acc_t;
-  SKG_DEV static void run(acc_t& c, const i32x4* a, const i32x4* b) {
-    const i32x8 av = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
-    const i32x8 bv = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+  typedef i32x8 frag_t;
+  SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
+
+// One operand fragment from two 16-byte LDS reads (OPB = 32) or one.
+template <class FragT>
+SKG_DEV FragT frag_from(const SKG_LDS char* p0, const SKG_LDS char* p1) {
+  if constexpr (sizeof(FragT) == 32) {
+    const i32x4 lo = *(const SKG_LDS i32x4*)p0, hi = *(const SKG_LDS i32x4*)p1;
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return *(const SKG_LDS FragT*)p0;
+  }
+}
 
 // The engine calls the MFMA with the B fragment first, so it computes the
 // transposed block: accumulator element e of lane l is output row l % MN and
@@ -181,8 +210,35 @@ SKG_DEV uint32_t lds_off<128>(int row, int chunk) {
 }
 template <>
 SKG_DEV uint32_t lds_off<64>(int row, int chunk) {
-  return (uint32_t)(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4));
+  return (uint32_t)(row * 64 + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4));
 }
+// Inverse of lds_off<RB>: the (row, chunk) stored in 16-byte slot s of a
+// stage (both permutations are involutions).
+template <int RB>
+SKG_DEV void lds_slot(int s, int& row, int& chunk);
+template <>
+SKG_DEV void lds_slot<64>(int s, int& row, int& chunk) {
+  row = s >> 2;
+  chunk = (s & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+}
+template <>
+SKG_DEV void lds_slot<128>(int s, int& row, int& chunk) {
+  const int prow = s >> 3;
+  row = prow ^ ((prow >> 3) & 1);
+  chunk = (s & 7) ^ (row & 7);
+}
+
+// Waits written as inline assembly with a memory clobber, so the compiler
+// neither moves memory operations across them nor adds waits of its own:
+// wait_vm<n>() returns once at most n vector memory operations of this wave
+// are outstanding; lds_barrier() completes this wave's LDS reads and then
+// synchronises the workgroup.
+template <int N>
+SKG_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+SKG_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // Conversions used by the epilogue (round to nearest even).

@@ -25,7 +25,7 @@ GemmInst gemm_instance(int tile_id, int dtype) {
   if (dtype == SKG_F16) return by_tile<DT_F16>(tile_id);
   if (dtype == SKG_BF16) return by_tile<DT_BF16>(tile_id);
   if (dtype == SKG_F8E4M3 && tile_id == SKG_TILE_256x256x128)
-    return make<TileCfg<DT_F8, 256, 256, 128, 2, 2, 32>>();
+    return make<TileCfg<DT_F8, 256, 256, 128, 2, 2, 32, 128>>();
   return {nullptr, nullptr};
 }
 

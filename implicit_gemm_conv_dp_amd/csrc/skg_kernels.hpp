@@ -69,7 +69,7 @@ struct WgradParams {
 };
 
 // ---------------------------------------------------------------------------
-template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_>
+template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64>
 struct TileCfg {
   static constexpr int DT = DT_, TM = TM_, TN = TN_, TK = TK_, WM = WM_, WN = WN_, MN = MN_;
   static constexpr int ESZ = DT == DT_F8 ? 1 : 2;
@@ -91,6 +91,15 @@ struct TileCfg {
   static constexpr int EPI_BYTES = WTM * EPI_PITCH32;
   static constexpr int LDS = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
   static constexpr int ACC4 = FM * FN * NACC / 4;  // float4 slots per lane
+  // Direct-to-LDS pipeline (GEMM): a MAC iteration is cut into SUBS
+  // sub-stages of RBS bytes of K per row, held in a ring of NST sub-stage
+  // buffers.
+  static constexpr int RBS = RBS_;
+  static constexpr int SUBS = RB / RBS;
+  static constexpr int KSS = RBS / Op::KB;  // MFMA k-steps per sub-stage
+  static constexpr int SST = (TM + TN) * RBS;
+  static constexpr int NST = (4 * SST <= 128 * 1024) ? 4 : 2;
+  static constexpr int LDS_DMA = NST * SST > EPI_BYTES ? NST * SST : EPI_BYTES;
   static_assert(RB == 64 || RB == 128, "LDS row layout");
   static_assert(FM >= 1 && FN >= 1 && WTM % MN == 0 && WTN % MN == 0, "wave tile");
   static_assert(KSTEPS >= 1 && RB % Op::KB == 0, "k steps");
@@ -102,6 +111,7 @@ struct TileCfg {
 // i.e. column-major B) are K-contiguous; each thread moves 16-byte chunks.
 template <class Cfg>
 struct GemmLoader {
+  static constexpr bool kDma = false;
   // Chunk j = tid + THREADS*u sits at row j / CPR, chunk j % CPR; THREADS is
   // a multiple of CPR, so unit u only moves the row by u * RSTEP.
   static constexpr int UA = (Cfg::TM * Cfg::CPR) / Cfg::THREADS;
@@ -156,6 +166,63 @@ struct GemmLoader {
   }
 };
 
+// GEMM operand loader, direct to LDS.  One sub-stage holds RBS bytes of K
+// for every row of the A and B tiles; each wave-instruction fills 1024
+// contiguous bytes of LDS (lane i at +16*i), so a thread fetches the global
+// chunk that the swizzled layout lds_off<RBS> keeps in its LDS slot.
+template <class Cfg>
+struct GemmDmaLoader {
+  static constexpr bool kDma = true;
+  static constexpr int CPRS = Cfg::RBS / 16;                // chunks per row
+  static constexpr int UA = Cfg::TM * CPRS / Cfg::THREADS;  // instructions per thread, A
+  static constexpr int UB = Cfg::TN * CPRS / Cfg::THREADS;
+  static constexpr int LPS = UA + UB;                       // per sub-stage
+  static_assert(UA * Cfg::THREADS == Cfg::TM * CPRS && UB * Cfg::THREADS == Cfg::TN * CPRS,
+                "DMA mapping");
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t offa[UA], offb[UB];  // row byte offset + chunk byte, or kOOB
+  uint32_t lima[UA], limb[UB];  // K bytes this chunk may reach before the tail
+  int wave;
+
+  SKG_DEV void init(const GemmParams& g, int m0, int n0, int tid) {
+    const int rows_a = g.M - m0, rows_b = g.N - n0;
+    ra = make_rsrc(g.A + (size_t)m0 * g.lda_b, (uint32_t)min((int64_t)rows_a * g.lda_b, (int64_t)0x7fffffff));
+    rb = make_rsrc(g.B + (size_t)n0 * g.ldb_b, (uint32_t)min((int64_t)rows_b * g.ldb_b, (int64_t)0x7fffffff));
+    const uint32_t kbytes = (uint32_t)g.K * Cfg::ESZ;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      int row, chunk;
+      lds_slot<Cfg::RBS>(u * Cfg::THREADS + tid, row, chunk);
+      offa[u] = row < rows_a ? (uint32_t)row * g.lda_b + chunk * 16 : kOOB;
+      lima[u] = kbytes - chunk * 16;
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      int row, chunk;
+      lds_slot<Cfg::RBS>(u * Cfg::THREADS + tid, row, chunk);
+      offb[u] = row < rows_b ? (uint32_t)row * g.ldb_b + chunk * 16 : kOOB;
+      limb[u] = kbytes - chunk * 16;
+    }
+  }
+
+  // Sub-stage q (K bytes [q*RBS, (q+1)*RBS) of the tile) into `stage`.
+  SKG_DEV void issue(int q, SKG_LDS char* stage) const {
+    const uint32_t kb = (uint32_t)q * Cfg::RBS;
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const uint32_t v = (offa[u] != kOOB && kb < lima[u]) ? offa[u] + kb : kOOB;
+      dma16(ra, lds_addr(stage + u * Cfg::THREADS * 16 + wave * 1024), v);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const uint32_t v = (offb[u] != kOOB && kb < limb[u]) ? offb[u] + kb : kOOB;
+      dma16(rb, lds_addr(stage + Cfg::TM * Cfg::RBS + u * Cfg::THREADS * 16 + wave * 1024), v);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // wgrad operand loader.  GEMM-A = dY^T (row m = output channel of the group,
 // K index q = (image, ho, wo)); GEMM-B^T = im2col(X) (row = (r, s, c') with c'
@@ -166,6 +233,7 @@ struct GemmLoader {
 // from out-of-range buffer offsets.
 template <class Cfg>
 struct WgradLoader {
+  static constexpr bool kDma = false;
   static_assert(Cfg::ESZ == 2, "wgrad runs on 16-bit inputs");
   static constexpr int QB = Cfg::TK / 8;             // 8-wide q blocks per K step
   static constexpr int NA = (Cfg::TM / 8) * QB;      // blocks of the A tile
@@ -278,7 +346,7 @@ struct WgradLoader {
 template <class Cfg>
 struct GemmProblem {
   typedef GemmParams Params;
-  typedef GemmLoader<Cfg> Loader;
+  typedef GemmDmaLoader<Cfg> Loader;
 
   SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
@@ -300,7 +368,6 @@ struct GemmProblem {
     o.cols = g.N - n0;
     return o;
   }
-  SKG_DEV static void load(const Params&, Loader& ld, int it) { ld.load(it); }
   SKG_DEV static int dtype_c(const Params& g) { return g.dtype_c; }
 };
 
@@ -343,8 +410,9 @@ struct Engine {
   typedef typename Cfg::acc_t acc_t;
   typedef typename Prob::Params Params;
   typedef typename Prob::Loader Loader;
-  typedef i32x4 FragA[Cfg::FM][Cfg::OPC];
-  typedef i32x4 FragB[Cfg::FN][Cfg::OPC];
+  typedef typename Cfg::Op::frag_t Frag;
+  typedef Frag FragA[Cfg::FM];
+  typedef Frag FragB[Cfg::FN];
 
   const Params& prm;
   const KPlan& p;
@@ -371,30 +439,37 @@ struct Engine {
         for (int i = 0; i < Cfg::NACC; ++i) acc[f][g][i] = 0.f;
   }
 
-  // Operand fragments of k-step ks.  The rows of one wave's blocks differ by
+  // Operand fragments of k-step ks from a stage whose rows are RBX bytes (A
+  // rows first, then B rows).  The rows of one wave's blocks differ by
   // multiples of 32, which leaves the swizzle unchanged, so each block is a
   // constant offset from the first.
+  template <int RBX>
   SKG_DEV void load_frags(FragA& fa, FragB& fb, const SKG_LDS char* stage, int ks) const {
+    static_assert(RBX == 128 || Cfg::MN == 32, "block offsets keep the 64-byte swizzle");
     const int lrow = lane % Cfg::MN, lk = (lane / Cfg::MN) * Cfg::Op::OPB;
     const int chunk0 = (ks * Cfg::Op::KB + lk) >> 4;
-#pragma unroll
-    for (int h = 0; h < Cfg::OPC; ++h) {
-      const uint32_t oa = lds_off<Cfg::RB>(wm * Cfg::WTM + lrow, chunk0 + h);
-      const uint32_t ob = lds_off<Cfg::RB>(wn * Cfg::WTN + lrow, chunk0 + h);
-#pragma unroll
-      for (int f = 0; f < Cfg::FM; ++f)
-        fa[f][h] = *(const SKG_LDS i32x4*)(stage + oa + f * Cfg::MN * Cfg::RB);
-#pragma unroll
-      for (int g = 0; g < Cfg::FN; ++g)
-        fb[g][h] = *(const SKG_LDS i32x4*)(stage + Cfg::A_BYTES + ob + g * Cfg::MN * Cfg::RB);
-    }
-  }
-
-  SKG_DEV void mma(const FragA& fa, const FragB& fb) {
+    const int h1 = Cfg::OPC - 1;  // second chunk of a 32-byte operand
+    const uint32_t oa0 = lds_off<RBX>(wm * Cfg::WTM + lrow, chunk0);
+    const uint32_t oa1 = lds_off<RBX>(wm * Cfg::WTM + lrow, chunk0 + h1);
+    const uint32_t ob0 = lds_off<RBX>(wn * Cfg::WTN + lrow, chunk0);
+    const uint32_t ob1 = lds_off<RBX>(wn * Cfg::WTN + lrow, chunk0 + h1);
+    const SKG_LDS char* sb = stage + Cfg::TM * RBX;
 #pragma unroll
     for (int f = 0; f < Cfg::FM; ++f)
+      fa[f] = frag_from<Frag>(stage + oa0 + f * Cfg::MN * RBX, stage + oa1 + f * Cfg::MN * RBX);
 #pragma unroll
-      for (int g = 0; g < Cfg::FN; ++g) Cfg::Op::run(acc[f][g], fb[g], fa[f]);  // transposed block
+    for (int g = 0; g < Cfg::FN; ++g)
+      fb[g] = frag_from<Frag>(sb + ob0 + g * Cfg::MN * RBX, sb + ob1 + g * Cfg::MN * RBX);
+  }
+
+  SKG_DEV void mma(const FragA& fa, const FragB& fb) { mma_rows(fa, fb, 0, Cfg::FM); }
+
+  SKG_DEV void mma_rows(const FragA& fa, const FragB& fb, int f0, int f1) {
+#pragma unroll
+    for (int f = 0; f < Cfg::FM; ++f)
+      if (f >= f0 && f < f1)
+#pragma unroll
+        for (int g = 0; g < Cfg::FN; ++g) Cfg::Op::run(acc[f][g], fb[g], fa[f]);  // transposed block
   }
 
   // acc += A_tile * B_tile for the stage in LDS.  Fragments are double
@@ -404,10 +479,10 @@ struct Engine {
   SKG_DEV void compute(const SKG_LDS char* stage) {
     FragA fa[2];
     FragB fb[2];
-    load_frags(fa[0], fb[0], stage, 0);
+    load_frags<Cfg::RB>(fa[0], fb[0], stage, 0);
 #pragma unroll
     for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
-      if (ks + 1 < Cfg::KSTEPS) load_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], stage, ks + 1);
+      if (ks + 1 < Cfg::KSTEPS) load_frags<Cfg::RB>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], stage, ks + 1);
       mma(fa[ks & 1], fb[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -415,6 +490,86 @@ struct Engine {
 
   // MAC iterations [k0, k1) of one tile into acc.
   SKG_DEV void mainloop(Loader& ld, int k0, int k1) {
+    if constexpr (Loader::kDma)
+      mainloop_dma(ld, k0, k1);
+    else
+      mainloop_regs(ld, k0, k1);
+  }
+
+  // Direct-to-LDS pipeline.  Sub-stage q of the segment lives in ring slot
+  // q % NST; NST sub-stages are in flight ahead of the one being consumed.
+  // In sub-stage q the MFMAs of its last k-step are split around the
+  // synchronisation point, where the wave (1) waits for its own loads of
+  // sub-stage q+1 and for its LDS reads of sub-stage q, (2) meets the other
+  // waves at the barrier -- after which sub-stage q+1 is complete in LDS and
+  // nobody reads slot q % NST any more -- (3) refills slot q % NST with
+  // sub-stage q + NST and (4) reads the first fragments of sub-stage q+1.
+  SKG_DEV SKG_LDS char* ring(int q) const { return lds + (q % Cfg::NST) * Cfg::SST; }
+
+  SKG_DEV static void wait_loads(int younger) {
+    constexpr int L = Loader::LPS;
+    static_assert(Cfg::NST <= 4, "wait table");
+    if (younger <= 0)
+      wait_vm<0>();
+    else if (younger == 1)
+      wait_vm<L>();
+    else if (younger == 2)
+      wait_vm<2 * L>();
+    else
+      wait_vm<3 * L>();
+  }
+
+  template <int CB>
+  SKG_DEV void last_kstep(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int q, int Q, int q0) {
+    mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2);
+    if (q + 1 < Q) {
+      wait_loads(min(Cfg::NST - 2, Q - 2 - q));
+      lds_barrier();
+      if (q + Cfg::NST < Q) ld.issue(q0 + q + Cfg::NST, ring(q));
+      load_frags<Cfg::RBS>(fa[CB ^ 1], fb[CB ^ 1], ring(q + 1), 0);
+    }
+    mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
+  }
+
+  template <int FB>
+  SKG_DEV void dma_substage(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int q, int Q, int q0) {
+    static_assert(Cfg::KSS == 1 || Cfg::KSS == 2, "k-steps per sub-stage");
+    if constexpr (Cfg::KSS == 1) {
+      last_kstep<FB>(fa, fb, ld, q, Q, q0);
+    } else {
+      load_frags<Cfg::RBS>(fa[FB ^ 1], fb[FB ^ 1], ring(q), 1);
+      mma(fa[FB], fb[FB]);
+      last_kstep<FB ^ 1>(fa, fb, ld, q, Q, q0);
+    }
+  }
+
+  SKG_DEV void mainloop_dma(const Loader& ld, int k0, int k1) {
+    // Nothing is outstanding here; saying so lets the compiler drop the
+    // waits it would otherwise place inside the loop for loads of earlier
+    // segments.  The loop itself only issues loads the compiler cannot see.
+    __builtin_amdgcn_s_waitcnt(0);
+    zero_acc();
+    const int q0 = k0 * Cfg::SUBS, Q = (k1 - k0) * Cfg::SUBS;
+#pragma unroll
+    for (int j = 0; j < Cfg::NST; ++j)
+      if (j < Q) ld.issue(q0 + j, ring(j));
+    wait_loads(min(Cfg::NST - 1, Q - 1));
+    lds_barrier();
+    FragA fa[2];
+    FragB fb[2];
+    load_frags<Cfg::RBS>(fa[0], fb[0], ring(0), 0);
+    if constexpr (Cfg::KSS % 2 == 0) {
+      for (int q = 0; q < Q; ++q) dma_substage<0>(fa, fb, ld, q, Q, q0);
+    } else {
+      for (int q = 0; q < Q; q += 2) {
+        dma_substage<0>(fa, fb, ld, q, Q, q0);
+        if (q + 1 < Q) dma_substage<1>(fa, fb, ld, q + 1, Q, q0);
+      }
+    }
+    __syncthreads();  // every wave is done with the ring before LDS is reused
+  }
+
+  SKG_DEV void mainloop_regs(Loader& ld, int k0, int k1) {
     zero_acc();
     Prob::load(prm, ld, k0);
     ld.store(lds, tid);
@@ -453,33 +608,165 @@ struct Engine {
 
   // Writes the accumulator tile out, one wave-row (WTM rows) at a time: the
   // owning waves stage it in LDS as fp32, then every thread takes a fixed
-  // 4-column chunk of the staged rows, adds the partners' partials and
+  // 8-column chunk of the staged rows, adds the partners' partials and
   //   OUT_STORE:     C = cvt((v * sa[row]) * sb[col]), round to nearest even;
   //   OUT_ATOMIC:    fp32 atomic add of (v * sa[row]) * sb[col] into C;
   //   OUT_WORKSPACE: fp32 atomic add of v into the tile's scratch wsp;
   //   OUT_PUBLISH:   stores v as this CTA's partial.
-  // A wave reads and writes partials only in the rows its threads own, so
-  // one flag per (CTA, wave) orders each hand-off: the producer's wave w
-  // releases its flag after its last partial store; the consumer's wave w
-  // acquires that flag before its first partial load.
-  SKG_DEV void write_out(const OutTile& o, const Fix& fx, float* wsp) {
-    constexpr int PITCH = Cfg::EPI_PITCH32;
-    constexpr int CPRO = Cfg::TN / 4;                // 4-column chunks per row
-    constexpr int RSTEP = Cfg::THREADS / CPRO;       // rows between a thread's chunks
-    static_assert(Cfg::THREADS % CPRO == 0 && 64 % CPRO == 0, "copy-out mapping");
-    const int dt = Prob::dtype_c(prm);
-    const int ch = tid % CPRO, col = ch * 4;
-    const bool col_ok = col < o.cols;
-    const bool scaled = fx.how == OUT_STORE || fx.how == OUT_ATOMIC;
-    f32x4 sb = {1.f, 1.f, 1.f, 1.f};
-    if (scaled && o.sb && col_ok) {
-      if (col + 4 <= o.cols) {
-        sb = *(const f32x4*)(o.sb + col);
+  // A wave reads and writes partials only in the rows its threads own (the
+  // same rows in every CTA), so one flag per (CTA, wave) orders each
+  // hand-off: the producer's wave w releases its flag after its last partial
+  // store; the consumer's wave w acquires that flag before its first partial
+  // load.
+  static constexpr int VC = 8;                      // columns per thread chunk
+  static constexpr int CPRO = Cfg::TN / VC;         // chunks per row
+  static constexpr int RSTEP = Cfg::THREADS / CPRO; // rows between a thread's rows
+  static constexpr int NR = (Cfg::WTM + RSTEP - 1) / RSTEP;  // rows per thread per pass
+
+  struct Row {   // one thread's 8 columns of one row, fp32
+    f32x4 v0, v1;
+  };
+
+  SKG_DEV Row staged(int lr, int col) const {
+    const SKG_LDS char* p = lds + lr * Cfg::EPI_PITCH32 + col * 4;
+    return Row{*(const SKG_LDS f32x4*)p, *(const SKG_LDS f32x4*)(p + 16)};
+  }
+
+  SKG_DEV void add_partials(Row& r, const Fix& fx, int tofs) const {
+    for (int k = 0; k < fx.nfold; ++k) {
+      const f32x4* q = (const f32x4*)(partial(fx.partner(k)) + tofs);
+      r.v0 += q[0];
+      r.v1 += q[1];
+    }
+  }
+
+  template <int HOW, int DTC>
+  SKG_DEV void emit_full(const Row& r, const OutTile& o, const Fix& fx, float* wsp, int row, int col,
+                         int tofs, float sa, const f32x4& sb0, const f32x4& sb1) const {
+    if constexpr (HOW == OUT_PUBLISH) {
+      f32x4* q = (f32x4*)(partial(fx.cta) + tofs);
+      q[0] = r.v0;
+      q[1] = r.v1;
+    } else if constexpr (HOW == OUT_WORKSPACE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        unsafeAtomicAdd(wsp + tofs + e, r.v0[e]);
+        unsafeAtomicAdd(wsp + tofs + 4 + e, r.v1[e]);
+      }
+    } else {
+      const f32x4 w0 = (r.v0 * sa) * sb0, w1 = (r.v1 * sa) * sb1;
+      const size_t idx = (size_t)row * o.ld + col;
+      if constexpr (HOW == OUT_ATOMIC) {
+        float* dst = (float*)o.base + idx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          unsafeAtomicAdd(dst + e, w0[e]);
+          unsafeAtomicAdd(dst + 4 + e, w1[e]);
+        }
+      } else if constexpr (DTC == DT_F32) {
+        f32x4* dst = (f32x4*)((float*)o.base + idx);
+        dst[0] = w0;
+        dst[1] = w1;
       } else {
-        for (int e = 0; e < o.cols - col; ++e) sb[e] = o.sb[col + e];
+        i32x4 h;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float a0 = w0[2 * e], a1 = w0[2 * e + 1], b0 = w1[2 * e], b1 = w1[2 * e + 1];
+          if constexpr (DTC == DT_F16) {
+            h[e] = (int)(to_f16_bits(a0) | ((uint32_t)to_f16_bits(a1) << 16));
+            h[e + 2] = (int)(to_f16_bits(b0) | ((uint32_t)to_f16_bits(b1) << 16));
+          } else {
+            h[e] = (int)(to_bf16_bits(a0) | ((uint32_t)to_bf16_bits(a1) << 16));
+            h[e + 2] = (int)(to_bf16_bits(b0) | ((uint32_t)to_bf16_bits(b1) << 16));
+          }
+        }
+        *(i32x4*)((uint16_t*)o.base + idx) = h;
+      }
+    }
+  }
+
+  // Copy-out of one pass of a full tile: no bounds checks.
+  template <int HOW, int DTC>
+  SKG_DEV void copy_full(const OutTile& o, const Fix& fx, float* wsp, int pass, int col,
+                         const f32x4& sb0, const f32x4& sb1) const {
+    const int lr0 = tid / CPRO;
+    if (RSTEP > Cfg::WTM && lr0 >= Cfg::WTM) return;  // fewer rows than threads
+#pragma unroll 4
+    for (int i = 0; i < NR; ++i) {
+      const int lr = lr0 + i * RSTEP, row = pass * Cfg::WTM + lr;
+      Row r = staged(lr, col);
+      const int tofs = row * Cfg::TN + col;
+      add_partials(r, fx, tofs);
+      const float sa = (HOW == OUT_STORE || HOW == OUT_ATOMIC) && o.sa ? o.sa[row] : 1.f;
+      emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sa, sb0, sb1);
+    }
+  }
+
+  // Copy-out of one pass of a ragged tile (rows or columns cut by the
+  // problem edge): element-wise bounds checks.
+  SKG_DEV void copy_ragged(const OutTile& o, const Fix& fx, float* wsp, int pass, int col,
+                           const f32x4& sb0, const f32x4& sb1) const {
+    const int dt = Prob::dtype_c(prm);
+    const int ncol = o.cols - col < VC ? o.cols - col : VC;
+    if (ncol <= 0) return;
+    for (int lr = tid / CPRO; lr < Cfg::WTM; lr += RSTEP) {
+      const int row = pass * Cfg::WTM + lr;
+      if (row >= o.rows) break;
+      Row r = staged(lr, col);
+      const int tofs = row * Cfg::TN + col;
+      add_partials(r, fx, tofs);
+      float v[VC];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = r.v0[e];
+        v[4 + e] = r.v1[e];
+      }
+      if (fx.how == OUT_PUBLISH) {
+        float* q = partial(fx.cta) + tofs;
+        for (int e = 0; e < ncol; ++e) q[e] = v[e];
+        continue;
+      }
+      if (fx.how == OUT_WORKSPACE) {
+        for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
+        continue;
+      }
+      const float sa = o.sa ? o.sa[row] : 1.f;
+      const size_t idx = (size_t)row * o.ld + col;
+      for (int e = 0; e < ncol; ++e) {
+        const float w = (v[e] * sa) * (e < 4 ? sb0[e] : sb1[e - 4]);
+        if (fx.how == OUT_ATOMIC)
+          unsafeAtomicAdd((float*)o.base + idx + e, w);
+        else if (dt == DT_F32)
+          ((float*)o.base)[idx + e] = w;
+        else if (dt == DT_F16)
+          ((uint16_t*)o.base)[idx + e] = to_f16_bits(w);
+        else
+          ((uint16_t*)o.base)[idx + e] = to_bf16_bits(w);
+      }
+    }
+  }
+
+  SKG_DEV void write_out(const OutTile& o, const Fix& fx, float* wsp) {
+    static_assert(Cfg::TN % VC == 0 && Cfg::THREADS % CPRO == 0 && 64 % CPRO == 0 &&
+                      (Cfg::WTM % RSTEP == 0 || RSTEP % Cfg::WTM == 0),
+                  "copy-out mapping");
+    const int col = (tid % CPRO) * VC;
+    const bool full = o.rows >= Cfg::TM && o.cols >= Cfg::TN;  // CTA-uniform
+    const bool scaled = fx.how == OUT_STORE || fx.how == OUT_ATOMIC;
+    f32x4 sb0 = {1.f, 1.f, 1.f, 1.f}, sb1 = sb0;
+    if (scaled && o.sb) {
+      if (col + VC <= o.cols) {
+        sb0 = *(const f32x4*)(o.sb + col);
+        sb1 = *(const f32x4*)(o.sb + col + 4);
+      } else {
+        for (int e = 0; e < 4; ++e) {
+          if (col + e < o.cols) sb0[e] = o.sb[col + e];
+          if (col + 4 + e < o.cols) sb1[e] = o.sb[col + 4 + e];
+        }
       }
     }
     for (int k = 0; k < fx.nfold; ++k) flag_wait(s.flags + fx.partner(k) * Cfg::NW + wave);
+    const int dt = Prob::dtype_c(prm);
 #pragma unroll
     for (int pass = 0; pass < Cfg::WM; ++pass) {
       if (wm == pass) {
@@ -492,52 +779,26 @@ struct Engine {
             for (int q = 0; q < Cfg::NACC / 4; ++q) {
               const f32x4 v = {acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
                                acc[f][g][4 * q + 3]};
-              *(SKG_LDS f32x4*)(lds + lrow * PITCH + col_of(g, q) * 4) = v;
+              *(SKG_LDS f32x4*)(lds + lrow * Cfg::EPI_PITCH32 + col_of(g, q) * 4) = v;
               if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
       }
       __syncthreads();
-      if (col_ok) {
-        for (int lr = tid / CPRO; lr < Cfg::WTM; lr += RSTEP) {
-          const int row = pass * Cfg::WTM + lr;
-          if (row >= o.rows) break;
-          f32x4 v = *(const SKG_LDS f32x4*)(lds + lr * PITCH + col * 4);
-          const int tofs = row * Cfg::TN + col;
-          for (int k = 0; k < fx.nfold; ++k) v += *(const f32x4*)(partial(fx.partner(k)) + tofs);
-          const int ncol = o.cols - col < 4 ? o.cols - col : 4;
-          if (fx.how == OUT_PUBLISH) {
-            *(f32x4*)(partial(fx.cta) + tofs) = v;
-            continue;
-          }
-          if (fx.how == OUT_WORKSPACE) {
-            for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
-            continue;
-          }
-          const float sa = o.sa ? o.sa[row] : 1.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (v[e] * sa) * sb[e];
-          const size_t idx = (size_t)row * o.ld + col;
-          if (fx.how == OUT_ATOMIC) {
-            float* dst = (float*)o.base + idx;
-            for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(dst + e, v[e]);
-          } else if (dt == DT_F32) {
-            float* dst = (float*)o.base + idx;
-            if (ncol == 4)
-              *(f32x4*)dst = v;
-            else
-              for (int e = 0; e < ncol; ++e) dst[e] = v[e];
-          } else {
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = dt == DT_F16 ? to_f16_bits(v[e]) : to_bf16_bits(v[e]);
-            uint16_t* dst = (uint16_t*)o.base + idx;
-            if (ncol == 4)
-              *(uint2*)dst = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-            else
-              for (int e = 0; e < ncol; ++e) dst[e] = h[e];
-          }
-        }
+      if (!full) {
+        copy_ragged(o, fx, wsp, pass, col, sb0, sb1);
+      } else if (fx.how == OUT_PUBLISH) {
+        copy_full<OUT_PUBLISH, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+      } else if (fx.how == OUT_WORKSPACE) {
+        copy_full<OUT_WORKSPACE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+      } else if (fx.how == OUT_ATOMIC) {
+        copy_full<OUT_ATOMIC, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+      } else if (dt == DT_F32) {
+        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+      } else if (dt == DT_F16) {
+        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1);
+      } else {
+        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1);
       }
       __syncthreads();
     }
@@ -648,7 +909,8 @@ struct Engine {
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS];
+  constexpr int kLds = Prob::Loader::kDma ? Cfg::LDS_DMA : Cfg::LDS;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   Engine<Cfg, Prob> e(prm, p, s, (SKG_LDS char*)lds);
   e.run();
 }

@@ -42,10 +42,11 @@ def run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa=None, sb=None, ws=N
     return decode_out(dC, fmt_c).reshape(M, N), plan
 
 
-def shape_for(tile):
+def shape_for(tile, k_tail=False):
     tm, tn, tk = map(int, tile.split("x"))
-    # 3 x 2 tiles with ragged last row and column of tiles, 24 MAC iterations.
-    return 2 * tm + tm // 3 + 8, tn + tn // 2 + 8, 24 * tk
+    # 3 x 2 tiles with ragged last row and column of tiles, 24 MAC iterations
+    # (plus a partial 25th with k_tail: 16 more K elements).
+    return 2 * tm + tm // 3 + 8, tn + tn // 2 + 8, 24 * tk + (16 if k_tail else 0)
 
 
 @pytest.mark.parametrize("tile,fmt", TILE_DT)
@@ -78,9 +79,10 @@ def exact_in(fmt_c, R):
     return np.array_equal(codecs.decode(fmt_c, codecs.encode(fmt_c, R)), R)
 
 
+@pytest.mark.parametrize("k_tail", [False, True])
 @pytest.mark.parametrize("tile,fmt", TILE_DT)
-def test_integer_exact_all_modes_and_fixups(tile, fmt):
-    M, N, K = shape_for(tile)
+def test_integer_exact_all_modes_and_fixups(tile, fmt, k_tail):
+    M, N, K = shape_for(tile, k_tail)
     A = synth.integer_codes(fmt, M * K, 21, 0.15)
     B = synth.integer_codes(fmt, N * K, 22, 0.15)
     sa = synth.pow2_scales(M, 23)
