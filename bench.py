@@ -41,8 +41,10 @@ def parse():
     ap.add_argument("--tile", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample (0 disables it)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with the measured HBM bytes per launch of the kernel")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="JSON file of HBM bytes per launch measured with rocprofv3 byte "
+                         "counters; used only while the kernel sources still hash to the "
+                         "value recorded with them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain device copy of MIB MiB "
                          "(the reference for scaling HBM byte counters)")
@@ -60,6 +62,34 @@ def copy_calibration(mib, steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                       "launches": steps}), flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources, so that counters taken on other code are not used."""
+    import hashlib
+    d = os.path.join(ROOT, "implicit_gemm_conv_dp_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path, name, tile, mode, red, ctas):
+    """HBM bytes per launch from the counter file, or None when the file is
+    missing, was taken on other kernel sources or on another launch."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("workloads", {}).get(name)
+    if not e or (e["tile"], e["mode"], e["reduction"], e["ctas"]) != (tile, mode, red, ctas):
+        return None
+    return e["bytes_per_launch"]
 
 
 def alg_bytes(wl):
@@ -98,11 +128,18 @@ def cpu_baseline(wl, inp, target_s):
             flops = wl.flops() * imgs / wl.n
         return time.perf_counter() - t0, flops
 
+    # One small warm-up run, then grow the sample (at most 8x per step, by
+    # the measured rate) until it takes half the target time or covers the
+    # whole workload.
     full = wl.M if wl.op == "gemm" else wl.n
-    unit = max(1, full // 64)
-    t, _ = run(unit)
-    units = int(min(full, max(unit, unit * target_s / max(t, 1e-3))))
-    t, flops = run(units)
+    units = max(1, full // 64)
+    run(units)
+    while True:
+        t, flops = run(units)
+        if t >= target_s / 2 or units >= full:
+            break
+        grow = min(8.0, max(2.0, target_s / max(t, 1e-3)))
+        units = min(full, int(units * grow))
     threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
     what = ("rows [0, %d) of the %d-row output" % (units, full)) if wl.op == "gemm" else \
         ("images [0, %d) of %d" % (units, full))
@@ -196,10 +233,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = MFMA_PEAK[dtype]
     hbm_bound = args.workload == 4
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic, wl.name, tile, mode, red, ctas)
     if hbm_bound:
         achieved = alg_bytes(wl) / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -16,7 +16,7 @@ than the pool leaves no stream-K CTAs).
 
 Vocabulary: a *MAC iteration* is one TM x TN x TK block of multiply-adds of one
 output tile; a tile has ``ipt = ceil(Kred / TK)`` of them.  ``P`` is the CTA
-pool.  Readings where the page leaves a step open (the design doc lists them):
+pool.  Readings where the page leaves a step open:
 
 * DP/SK split: ``dp_tiles = (T // P) * P`` -- whole waves of the pool;
 * if the remainder has fewer MAC iterations than the pool the plan is all-DP;

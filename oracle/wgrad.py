@@ -6,7 +6,7 @@ Follows the wgrad problem of rocm-libraries PR #13151 ("feat(rocke): stream-K
 for implicit-GEMM conv wgrad": Motivation, and the commit porting stream-K to
 the backward-weight convolution): the filter gradient has the filter's size
 while the reduction runs over every output pixel of every image.  Readings we
-take where the page is silent (all listed in the design doc):
+take where the page is silent:
 
 * activations are NHWC: ``X[n][h][w][c]`` and ``dY[n][ho][wo][k]``;
 * output size ``Ho = (H + 2*pad_h - R) // stride_h + 1`` (likewise ``Wo``),
