@@ -55,22 +55,39 @@ SKG_DEV uint32_t lds_addr(const SKG_LDS void* p) { return (uint32_t)(uintptr_t)p
 
 // ---------------------------------------------------------------------------
 // Cross-CTA hand-off (rocm-libraries PR #13151, commit adding the fence and
-// flag leaf ops): a contributor's release store at agent scope makes its
-// partial visible across the per-XCD L2s (the compiler emits the L2
-// write-back before the store); the consumer polls with relaxed agent-scope
-// loads and then takes an agent-scope acquire fence (the L2 invalidate)
-// before it reads the partial.  Every lane of the wave performs the store and
-// the poll on the same flag word.
+// flag leaf ops: a release publish, an acquire wait, both at agent scope).
+// The L2 caches of the eight XCDs are not coherent with one another, so the
+// partial tiles themselves are stored and loaded at device scope (cache
+// policy sc1: the stores write through to, and the loads read from, the
+// level every XCD sees).  A contributor then only has to wait for its own
+// partial stores to complete before it stores the flag (device scope); the
+// consumer polls the flag with device-scope loads and reads the partials
+// with device-scope loads.  This gives the release/acquire ordering of the
+// hand-off without writing back or invalidating a whole L2, which would
+// also throw away every other CTA's cached operands.  Every lane of the
+// wave performs the store and the poll on the same flag word.
 //
 // The poll is bounded: after kSpinLimit polls (a fraction of a second) the wave gives
 // up, counts the event in g_skg_wait_timeouts and continues, so a broken plan
 // produces wrong numbers rather than a hung device.
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kDeviceScope = 16;  // cache-policy bits of a buffer access: sc1
 
 static __device__ uint32_t g_skg_wait_timeouts = 0;
 
+SKG_DEV void store_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, kDeviceScope);
+}
+SKG_DEV void store_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, kDeviceScope);
+}
+SKG_DEV f32x4 load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+
 SKG_DEV void flag_publish(uint32_t* flag) {
-  __hip_atomic_store(flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are done
+  __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 SKG_DEV void flag_wait(const uint32_t* flag) {
@@ -82,7 +99,7 @@ SKG_DEV void flag_wait(const uint32_t* flag) {
       break;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  asm volatile("" ::: "memory");  // partial loads stay after the poll
 }
 
 // ---------------------------------------------------------------------------

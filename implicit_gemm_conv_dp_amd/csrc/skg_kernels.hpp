@@ -17,6 +17,8 @@
 // LDS always holds K-contiguous rows.
 #pragma once
 
+#include <type_traits>
+
 #include "skg_device.hpp"
 
 namespace skg {
@@ -100,6 +102,15 @@ struct TileCfg {
   static constexpr int SST = (TM + TN) * RBS;
   static constexpr int NST = (4 * SST <= 128 * 1024) ? 4 : 2;
   static constexpr int LDS_DMA = NST * SST > EPI_BYTES ? NST * SST : EPI_BYTES;
+  // Grouped direct-to-LDS pipeline (128-byte rows, i.e. whole cache lines
+  // per row and MAC iteration): each ring slot holds one operand tile (A or
+  // B) of one MAC iteration.  Large tiles take the whole LDS; 128-row tiles
+  // stay within half of it so that two CTAs fit on a CU.
+  static constexpr int SLOT = (TM > TN ? TM : TN) * RB;
+  static constexpr int LDS_BUDGET = TM * TN >= 256 * 128 ? 160 * 1024 : 80 * 1024;
+  static constexpr int NSLOT = LDS_BUDGET / SLOT > 8 ? 8 : LDS_BUDGET / SLOT;
+  static constexpr bool GROUPED = RB == 128 && NSLOT >= 4 && KSTEPS % 2 == 0;
+  static constexpr int LDS_GRP = NSLOT * SLOT > EPI_BYTES ? NSLOT * SLOT : EPI_BYTES;
   static_assert(RB == 64 || RB == 128, "LDS row layout");
   static_assert(FM >= 1 && FN >= 1 && WTM % MN == 0 && WTN % MN == 0, "wave tile");
   static_assert(KSTEPS >= 1 && RB % Op::KB == 0, "k steps");
@@ -111,7 +122,7 @@ struct TileCfg {
 // i.e. column-major B) are K-contiguous; each thread moves 16-byte chunks.
 template <class Cfg>
 struct GemmLoader {
-  static constexpr bool kDma = false;
+  static constexpr bool kDma = false, kGrouped = false;
   // Chunk j = tid + THREADS*u sits at row j / CPR, chunk j % CPR; THREADS is
   // a multiple of CPR, so unit u only moves the row by u * RSTEP.
   static constexpr int UA = (Cfg::TM * Cfg::CPR) / Cfg::THREADS;
@@ -166,60 +177,88 @@ struct GemmLoader {
   }
 };
 
-// GEMM operand loader, direct to LDS.  One sub-stage holds RBS bytes of K
-// for every row of the A and B tiles; each wave-instruction fills 1024
+// GEMM operand loaders, direct to LDS.  Each wave-instruction fills 1024
 // contiguous bytes of LDS (lane i at +16*i), so a thread fetches the global
-// chunk that the swizzled layout lds_off<RBS> keeps in its LDS slot.
-template <class Cfg>
-struct GemmDmaLoader {
-  static constexpr bool kDma = true;
-  static constexpr int CPRS = Cfg::RBS / 16;                // chunks per row
-  static constexpr int UA = Cfg::TM * CPRS / Cfg::THREADS;  // instructions per thread, A
-  static constexpr int UB = Cfg::TN * CPRS / Cfg::THREADS;
-  static constexpr int LPS = UA + UB;                       // per sub-stage
-  static_assert(UA * Cfg::THREADS == Cfg::TM * CPRS && UB * Cfg::THREADS == Cfg::TN * CPRS,
-                "DMA mapping");
+// chunk that the swizzled layout keeps in its LDS slot.  For slot
+// u*THREADS + tid the row is row(tid) + u*(THREADS/CPR) and the chunk does
+// not depend on u, so a thread keeps one offset per operand, the row step
+// is uniform, and one K limit serves all its chunks.  Rows past the edge of
+// the matrix lie past the end of the buffer resource and read as zero, as
+// do chunks past K (sent to an out-of-range offset).
+template <class Cfg, int RBX>
+struct DmaRows {
+  static constexpr int CPR = RBX / 16;              // chunks per row
+  static constexpr int STEP = Cfg::THREADS / CPR;   // rows between a thread's chunks
+  static constexpr int UA = Cfg::TM / STEP, UB = Cfg::TN / STEP;
+  static_assert(UA * STEP == Cfg::TM && UB * STEP == Cfg::TN, "DMA mapping");
 
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t offa[UA], offb[UB];  // row byte offset + chunk byte, or kOOB
-  uint32_t lima[UA], limb[UB];  // K bytes this chunk may reach before the tail
+  uint32_t offa, offb;      // byte offset of this thread's first chunk
+  uint32_t stepa, stepb;    // STEP rows, in bytes (uniform)
+  uint32_t lim;             // K bytes this thread's chunk may reach before the tail
   int wave;
 
   SKG_DEV void init(const GemmParams& g, int m0, int n0, int tid) {
     const int rows_a = g.M - m0, rows_b = g.N - n0;
     ra = make_rsrc(g.A + (size_t)m0 * g.lda_b, (uint32_t)min((int64_t)rows_a * g.lda_b, (int64_t)0x7fffffff));
     rb = make_rsrc(g.B + (size_t)n0 * g.ldb_b, (uint32_t)min((int64_t)rows_b * g.ldb_b, (int64_t)0x7fffffff));
-    const uint32_t kbytes = (uint32_t)g.K * Cfg::ESZ;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int row, chunk;
+    lds_slot<RBX>(tid, row, chunk);
+    offa = (uint32_t)row * g.lda_b + chunk * 16;
+    offb = (uint32_t)row * g.ldb_b + chunk * 16;
+    stepa = STEP * g.lda_b;
+    stepb = STEP * g.ldb_b;
+    lim = (uint32_t)g.K * Cfg::ESZ - chunk * 16;
+  }
+
+  // RBX bytes of K starting at byte kb of every row, A rows into `la`, B
+  // rows into `lb` (either may be skipped).
+  template <bool DO_A, bool DO_B>
+  SKG_DEV void issue_rows(uint32_t kb, SKG_LDS char* la, SKG_LDS char* lb) const {
+    const bool ok = kb < lim;
+    if constexpr (DO_A) {
 #pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      int row, chunk;
-      lds_slot<Cfg::RBS>(u * Cfg::THREADS + tid, row, chunk);
-      offa[u] = row < rows_a ? (uint32_t)row * g.lda_b + chunk * 16 : kOOB;
-      lima[u] = kbytes - chunk * 16;
+      for (int u = 0; u < UA; ++u)
+        dma16(ra, lds_addr(la + u * Cfg::THREADS * 16 + wave * 1024), ok ? offa + u * stepa + kb : kOOB);
     }
+    if constexpr (DO_B) {
 #pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      int row, chunk;
-      lds_slot<Cfg::RBS>(u * Cfg::THREADS + tid, row, chunk);
-      offb[u] = row < rows_b ? (uint32_t)row * g.ldb_b + chunk * 16 : kOOB;
-      limb[u] = kbytes - chunk * 16;
+      for (int u = 0; u < UB; ++u)
+        dma16(rb, lds_addr(lb + u * Cfg::THREADS * 16 + wave * 1024), ok ? offb + u * stepb + kb : kOOB);
     }
   }
+};
+
+// Sub-stage pipeline: sub-stage q holds RBS bytes of K for every row of the
+// A and B tiles.
+template <class Cfg>
+struct GemmDmaLoader : DmaRows<Cfg, Cfg::RBS> {
+  static constexpr bool kDma = true, kGrouped = false;
+  typedef DmaRows<Cfg, Cfg::RBS> Base;
+  static constexpr int LPS = Base::UA + Base::UB;  // instructions per sub-stage
 
   // Sub-stage q (K bytes [q*RBS, (q+1)*RBS) of the tile) into `stage`.
   SKG_DEV void issue(int q, SKG_LDS char* stage) const {
-    const uint32_t kb = (uint32_t)q * Cfg::RBS;
-#pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const uint32_t v = (offa[u] != kOOB && kb < lima[u]) ? offa[u] + kb : kOOB;
-      dma16(ra, lds_addr(stage + u * Cfg::THREADS * 16 + wave * 1024), v);
-    }
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const uint32_t v = (offb[u] != kOOB && kb < limb[u]) ? offb[u] + kb : kOOB;
-      dma16(rb, lds_addr(stage + Cfg::TM * Cfg::RBS + u * Cfg::THREADS * 16 + wave * 1024), v);
-    }
+    this->template issue_rows<true, true>((uint32_t)q * Cfg::RBS, stage, stage + Cfg::TM * Cfg::RBS);
+  }
+};
+
+// Grouped pipeline: group j of a segment is operand A (j even) or B (j odd)
+// of its MAC iteration j/2, RB = 128 bytes of K per row, so every
+// wave-instruction reads eight whole 128-byte lines.
+template <class Cfg>
+struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
+  static constexpr bool kDma = true, kGrouped = true;
+  static_assert(Cfg::RB == 128, "whole-line rows");
+
+  // Group j of the segment that starts at MAC iteration it0, into `slot`.
+  SKG_DEV void issue(int j, int it0, SKG_LDS char* slot) const {
+    const uint32_t kb = (uint32_t)(it0 + (j >> 1)) * Cfg::RB;
+    if ((j & 1) == 0)
+      this->template issue_rows<true, false>(kb, slot, nullptr);
+    else
+      this->template issue_rows<false, true>(kb, nullptr, slot);
   }
 };
 
@@ -233,7 +272,7 @@ struct GemmDmaLoader {
 // from out-of-range buffer offsets.
 template <class Cfg>
 struct WgradLoader {
-  static constexpr bool kDma = false;
+  static constexpr bool kDma = false, kGrouped = false;
   static_assert(Cfg::ESZ == 2, "wgrad runs on 16-bit inputs");
   static constexpr int QB = Cfg::TK / 8;             // 8-wide q blocks per K step
   static constexpr int NA = (Cfg::TM / 8) * QB;      // blocks of the A tile
@@ -346,7 +385,7 @@ struct WgradLoader {
 template <class Cfg>
 struct GemmProblem {
   typedef GemmParams Params;
-  typedef GemmDmaLoader<Cfg> Loader;
+  typedef typename std::conditional<Cfg::GROUPED, GemmGrpLoader<Cfg>, GemmDmaLoader<Cfg>>::type Loader;
 
   SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
@@ -445,6 +484,12 @@ struct Engine {
   // constant offset from the first.
   template <int RBX>
   SKG_DEV void load_frags(FragA& fa, FragB& fb, const SKG_LDS char* stage, int ks) const {
+    load_frags_ab<RBX>(fa, fb, stage, stage + Cfg::TM * RBX, ks);
+  }
+
+  template <int RBX>
+  SKG_DEV void load_frags_ab(FragA& fa, FragB& fb, const SKG_LDS char* stage,
+                             const SKG_LDS char* sb, int ks) const {
     static_assert(RBX == 128 || Cfg::MN == 32, "block offsets keep the 64-byte swizzle");
     const int lrow = lane % Cfg::MN, lk = (lane / Cfg::MN) * Cfg::Op::OPB;
     const int chunk0 = (ks * Cfg::Op::KB + lk) >> 4;
@@ -453,7 +498,6 @@ struct Engine {
     const uint32_t oa1 = lds_off<RBX>(wm * Cfg::WTM + lrow, chunk0 + h1);
     const uint32_t ob0 = lds_off<RBX>(wn * Cfg::WTN + lrow, chunk0);
     const uint32_t ob1 = lds_off<RBX>(wn * Cfg::WTN + lrow, chunk0 + h1);
-    const SKG_LDS char* sb = stage + Cfg::TM * RBX;
 #pragma unroll
     for (int f = 0; f < Cfg::FM; ++f)
       fa[f] = frag_from<Frag>(stage + oa0 + f * Cfg::MN * RBX, stage + oa1 + f * Cfg::MN * RBX);
@@ -490,7 +534,9 @@ struct Engine {
 
   // MAC iterations [k0, k1) of one tile into acc.
   SKG_DEV void mainloop(Loader& ld, int k0, int k1) {
-    if constexpr (Loader::kDma)
+    if constexpr (Loader::kGrouped)
+      mainloop_grp(ld, k0, k1);
+    else if constexpr (Loader::kDma)
       mainloop_dma(ld, k0, k1);
     else
       mainloop_regs(ld, k0, k1);
@@ -519,10 +565,15 @@ struct Engine {
       wait_vm<3 * L>();
   }
 
-  template <int CB>
+  // LAST: the segment's final sub-stage, which has nothing to wait for or
+  // prefetch.  It is a separate instantiation so that the second half of
+  // the MFMAs after the barrier is reached from one path only, and the
+  // compiler's LDS wait before it covers the fragments read before the
+  // barrier, not those of the next sub-stage read right after it.
+  template <int CB, bool LAST>
   SKG_DEV void last_kstep(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int q, int Q, int q0) {
     mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2);
-    if (q + 1 < Q) {
+    if constexpr (!LAST) {
       wait_loads(min(Cfg::NST - 2, Q - 2 - q));
       lds_barrier();
       if (q + Cfg::NST < Q) ld.issue(q0 + q + Cfg::NST, ring(q));
@@ -531,16 +582,17 @@ struct Engine {
     mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
   }
 
-  template <int FB>
+  // One sub-stage: k-steps 0 .. KSS-2 with the fragments of the next k-step
+  // read during the MFMAs of the current one, then the last k-step around
+  // the synchronisation point.  FB is the fragment buffer of k-step 0.
+  template <int FB, bool LAST>
   SKG_DEV void dma_substage(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int q, int Q, int q0) {
-    static_assert(Cfg::KSS == 1 || Cfg::KSS == 2, "k-steps per sub-stage");
-    if constexpr (Cfg::KSS == 1) {
-      last_kstep<FB>(fa, fb, ld, q, Q, q0);
-    } else {
-      load_frags<Cfg::RBS>(fa[FB ^ 1], fb[FB ^ 1], ring(q), 1);
-      mma(fa[FB], fb[FB]);
-      last_kstep<FB ^ 1>(fa, fb, ld, q, Q, q0);
+#pragma unroll
+    for (int ks = 0; ks + 1 < Cfg::KSS; ++ks) {
+      load_frags<Cfg::RBS>(fa[(FB + ks + 1) & 1], fb[(FB + ks + 1) & 1], ring(q), ks + 1);
+      mma(fa[(FB + ks) & 1], fb[(FB + ks) & 1]);
     }
+    last_kstep<(FB + Cfg::KSS - 1) & 1, LAST>(fa, fb, ld, q, Q, q0);
   }
 
   SKG_DEV void mainloop_dma(const Loader& ld, int k0, int k1) {
@@ -549,7 +601,7 @@ struct Engine {
     // segments.  The loop itself only issues loads the compiler cannot see.
     __builtin_amdgcn_s_waitcnt(0);
     zero_acc();
-    const int q0 = k0 * Cfg::SUBS, Q = (k1 - k0) * Cfg::SUBS;
+    const int q0 = k0 * Cfg::SUBS, Q = (k1 - k0) * Cfg::SUBS;  // Q >= 1
 #pragma unroll
     for (int j = 0; j < Cfg::NST; ++j)
       if (j < Q) ld.issue(q0 + j, ring(j));
@@ -558,14 +610,89 @@ struct Engine {
     FragA fa[2];
     FragB fb[2];
     load_frags<Cfg::RBS>(fa[0], fb[0], ring(0), 0);
+    // Sub-stages 0 .. Q-2, then the last one.  With one k-step per
+    // sub-stage the fragment buffers alternate, so sub-stages go in pairs.
     if constexpr (Cfg::KSS % 2 == 0) {
-      for (int q = 0; q < Q; ++q) dma_substage<0>(fa, fb, ld, q, Q, q0);
+      for (int q = 0; q < Q - 1; ++q) dma_substage<0, false>(fa, fb, ld, q, Q, q0);
+      dma_substage<0, true>(fa, fb, ld, Q - 1, Q, q0);
     } else {
-      for (int q = 0; q < Q; q += 2) {
-        dma_substage<0>(fa, fb, ld, q, Q, q0);
-        if (q + 1 < Q) dma_substage<1>(fa, fb, ld, q + 1, Q, q0);
+      int q = 0;
+      for (; q + 2 < Q; q += 2) {
+        dma_substage<0, false>(fa, fb, ld, q, Q, q0);
+        dma_substage<1, false>(fa, fb, ld, q + 1, Q, q0);
+      }
+      if (q + 2 == Q) {
+        dma_substage<0, false>(fa, fb, ld, q, Q, q0);
+        dma_substage<1, true>(fa, fb, ld, q + 1, Q, q0);
+      } else {
+        dma_substage<0, true>(fa, fb, ld, q, Q, q0);
       }
     }
+    __syncthreads();  // every wave is done with the ring before LDS is reused
+  }
+
+  // Grouped pipeline.  Group j of the segment (A or B of MAC iteration
+  // j/2) lives in ring slot j % NSLOT.  At the end of iteration i the wave
+  // waits for its own loads of iteration i+1, meets the other waves at the
+  // barrier -- after which iteration i+1 is complete in LDS and nobody reads
+  // iteration i's two slots any more -- refills those slots with groups
+  // 2i+NSLOT and 2i+NSLOT+1 and reads the first fragments of iteration i+1,
+  // all inside the last k-step's MFMAs.
+  SKG_DEV SKG_LDS char* slot(int j) const { return lds + (j % Cfg::NSLOT) * Cfg::SLOT; }
+
+  // Wait until at most n groups younger than the awaited one are in flight
+  // (younger groups alternate A, B, A, ... starting with an A group).
+  SKG_DEV static void wait_groups(int n) {
+    constexpr int A = Loader::UA, B = Loader::UB;
+    static_assert(Cfg::NSLOT <= 8 && 3 * A + 3 * B < 64, "wait table");
+    switch (n <= 0 ? 0 : n) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<A>(); break;
+      case 2: wait_vm<A + B>(); break;
+      case 3: wait_vm<2 * A + B>(); break;
+      case 4: wait_vm<2 * A + 2 * B>(); break;
+      case 5: wait_vm<3 * A + 2 * B>(); break;
+      default: wait_vm<3 * A + 3 * B>(); break;
+    }
+  }
+
+  template <bool LAST>
+  SKG_DEV void grp_iter(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G, int k0) {
+    const SKG_LDS char* sa = slot(2 * i);
+    const SKG_LDS char* sb = slot(2 * i + 1);
+#pragma unroll
+    for (int ks = 0; ks + 1 < Cfg::KSTEPS; ++ks) {
+      load_frags_ab<Cfg::RB>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
+      mma(fa[ks & 1], fb[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
+    }
+    constexpr int CB = (Cfg::KSTEPS - 1) & 1;
+    mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2);
+    if constexpr (!LAST) {
+      wait_groups(min(G, 2 * i + Cfg::NSLOT) - (2 * i + 4));
+      lds_barrier();
+      if (2 * i + Cfg::NSLOT < G) ld.issue(2 * i + Cfg::NSLOT, k0, slot(2 * i));
+      if (2 * i + Cfg::NSLOT + 1 < G) ld.issue(2 * i + Cfg::NSLOT + 1, k0, slot(2 * i + 1));
+      load_frags_ab<Cfg::RB>(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
+    }
+    mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
+  }
+
+  SKG_DEV void mainloop_grp(const Loader& ld, int k0, int k1) {
+    static_assert(Cfg::KSTEPS % 2 == 0, "k-step 0 of every iteration uses buffer 0");
+    __builtin_amdgcn_s_waitcnt(0);  // see mainloop_dma
+    zero_acc();
+    const int I = k1 - k0, G = 2 * I;  // I >= 1
+#pragma unroll
+    for (int j = 0; j < Cfg::NSLOT; ++j)
+      if (j < G) ld.issue(j, k0, slot(j));
+    wait_groups(min(Cfg::NSLOT, G) - 2);
+    lds_barrier();
+    FragA fa[2];
+    FragB fb[2];
+    load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
+    for (int i = 0; i + 1 < I; ++i) grp_iter<false>(fa, fb, ld, i, G, k0);
+    grp_iter<true>(fa, fb, ld, I - 1, G, k0);
     __syncthreads();  // every wave is done with the ring before LDS is reused
   }
 
@@ -605,6 +732,9 @@ struct Engine {
 
   // Partial tile of stream-K CTA c: fp32, tile order [row][TN].
   SKG_DEV float* partial(int c) const { return s.partials + (size_t)c * Cfg::TM * Cfg::TN; }
+  SKG_DEV __amdgpu_buffer_rsrc_t partial_rsrc(int c) const {
+    return make_rsrc(partial(c), Cfg::TM * Cfg::TN * 4);
+  }
 
   // Writes the accumulator tile out, one wave-row (WTM rows) at a time: the
   // owning waves stage it in LDS as fp32, then every thread takes a fixed
@@ -634,9 +764,41 @@ struct Engine {
 
   SKG_DEV void add_partials(Row& r, const Fix& fx, int tofs) const {
     for (int k = 0; k < fx.nfold; ++k) {
-      const f32x4* q = (const f32x4*)(partial(fx.partner(k)) + tofs);
-      r.v0 += q[0];
-      r.v1 += q[1];
+      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
+      r.v0 += load_dev16(q, tofs * 4);
+      r.v1 += load_dev16(q, tofs * 4 + 16);
+    }
+  }
+
+  // Adds the fold partners' partials into this thread's rows of the staged
+  // wave-row (full tiles).  Per partner every load of the thread is issued
+  // before the first add, so one memory round trip covers all its rows
+  // (the partials come from device scope, far from the CU).  Partners are
+  // added in the order Fix::partner gives, as add_partials does.
+  SKG_DEV void fold_staged(const Fix& fx, int pass, int col) const {
+    const int lr0 = tid / CPRO;
+    if (RSTEP > Cfg::WTM && lr0 >= Cfg::WTM) return;  // fewer rows than threads
+    constexpr int CH = NR < 8 ? NR : 8;  // rows in flight per round trip
+    static_assert(NR % CH == 0, "fold chunks");
+    for (int k = 0; k < fx.nfold; ++k) {
+      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
+#pragma unroll 1
+      for (int i0 = 0; i0 < NR; i0 += CH) {
+        f32x4 t[CH][2];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const uint32_t off = ((pass * Cfg::WTM + lr0 + (i0 + i) * RSTEP) * Cfg::TN + col) * 4;
+          t[i][0] = load_dev16(q, off);
+          t[i][1] = load_dev16(q, off + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          SKG_LDS f32x4* d =
+              (SKG_LDS f32x4*)(lds + (lr0 + (i0 + i) * RSTEP) * Cfg::EPI_PITCH32 + col * 4);
+          d[0] += t[i][0];
+          d[1] += t[i][1];
+        }
+      }
     }
   }
 
@@ -644,9 +806,9 @@ struct Engine {
   SKG_DEV void emit_full(const Row& r, const OutTile& o, const Fix& fx, float* wsp, int row, int col,
                          int tofs, float sa, const f32x4& sb0, const f32x4& sb1) const {
     if constexpr (HOW == OUT_PUBLISH) {
-      f32x4* q = (f32x4*)(partial(fx.cta) + tofs);
-      q[0] = r.v0;
-      q[1] = r.v1;
+      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
+      store_dev16(q, tofs * 4, r.v0);
+      store_dev16(q, tofs * 4 + 16, r.v1);
     } else if constexpr (HOW == OUT_WORKSPACE) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -722,8 +884,8 @@ struct Engine {
         v[4 + e] = r.v1[e];
       }
       if (fx.how == OUT_PUBLISH) {
-        float* q = partial(fx.cta) + tofs;
-        for (int e = 0; e < ncol; ++e) q[e] = v[e];
+        const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
+        for (int e = 0; e < ncol; ++e) store_dev4(q, (tofs + e) * 4, v[e]);
         continue;
       }
       if (fx.how == OUT_WORKSPACE) {
@@ -785,20 +947,25 @@ struct Engine {
         }
       }
       __syncthreads();
+      Fix fo = fx;  // what the copy itself still has to fold
+      if (full && fx.nfold > 0) {
+        fold_staged(fx, pass, col);
+        fo.nfold = 0;
+      }
       if (!full) {
         copy_ragged(o, fx, wsp, pass, col, sb0, sb1);
       } else if (fx.how == OUT_PUBLISH) {
-        copy_full<OUT_PUBLISH, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_PUBLISH, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (fx.how == OUT_WORKSPACE) {
-        copy_full<OUT_WORKSPACE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_WORKSPACE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (fx.how == OUT_ATOMIC) {
-        copy_full<OUT_ATOMIC, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_ATOMIC, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (dt == DT_F32) {
-        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (dt == DT_F16) {
-        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F16>(o, fo, wsp, pass, col, sb0, sb1);
       } else {
-        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_BF16>(o, fo, wsp, pass, col, sb0, sb1);
       }
       __syncthreads();
     }
@@ -862,6 +1029,26 @@ struct Engine {
     return fx;
   }
 
+  // Data-parallel slot s (the s-th DP tile in launch order) -> tile id.
+  // Blocks go to the 8 XCDs round robin, so consecutive slots land on
+  // different L2 caches.  Slots are first transposed so that each XCD takes
+  // one contiguous run of them, and the run is laid over the tile grid in
+  // groups of GM tile rows, column by column, so that the tiles running
+  // together on one XCD form a compact block sharing A and B panels.  A
+  // bijection on [0, dp_tiles); the DP tiles are whole rows of the tile
+  // grid plus a partial last row, which keeps its order.
+  SKG_DEV int dp_order(int s) const {
+    constexpr int XCDS = 8, GM = 4;
+    const int n8 = p.dp_tiles & ~(XCDS - 1);
+    const int u = s < n8 ? (s % XCDS) * (n8 / XCDS) + s / XCDS : s;
+    const int rows = p.dp_tiles / p.tiles_n;
+    if (u >= rows * p.tiles_n) return u;
+    const int g = u / (GM * p.tiles_n);
+    const int within = u - g * GM * p.tiles_n;
+    const int rg = min(GM, rows - g * GM);
+    return (g * GM + within % rg) * p.tiles_n + within / rg;
+  }
+
   // One bounded work loop: the stream-K range (if any) segment by segment,
   // then this block's data-parallel tiles.
   SKG_DEV void run() {
@@ -882,9 +1069,20 @@ struct Engine {
       dp_tile = b;
       dp_step = p.grid;
     }
+    // Stream-K iterations [it, split) run before the DP tiles and
+    // [split, end) after them.  dp / dp_sk: the whole range first.
+    // persistent: only a first segment that continues a tile begun by a
+    // lower CTA (it hands its partial on), then the DP tiles, then the
+    // segments this CTA owns; by then the higher CTAs it folds from have
+    // long handed their partials on, so the wait costs nothing.  Every
+    // segment a CTA waits for is a first segment of a higher CTA, so each
+    // wait still ends (the highest CTA never waits).
+    int split = end;
+    if (p.mode == MODE_PERSISTENT)
+      split = (it < end && it % p.ipt != 0) ? min(end, (it / p.ipt + 1) * p.ipt) : it;
     while (true) {
       int tile, k0, k1, cta;
-      if (it < end) {
+      if (it < split || (it < end && dp_tile >= p.dp_tiles)) {
         const int t = it / p.ipt;
         const int seg_end = min(end, (t + 1) * p.ipt);
         tile = p.dp_tiles + t;
@@ -893,7 +1091,7 @@ struct Engine {
         cta = b;
         it = seg_end;  // strictly increases
       } else if (dp_tile < p.dp_tiles) {
-        tile = dp_tile;
+        tile = dp_order(dp_tile);
         k0 = 0;
         k1 = p.ipt;
         cta = -1;
@@ -909,7 +1107,9 @@ struct Engine {
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
-  constexpr int kLds = Prob::Loader::kDma ? Cfg::LDS_DMA : Cfg::LDS;
+  constexpr int kLds = Prob::Loader::kGrouped ? Cfg::LDS_GRP
+                       : Prob::Loader::kDma   ? Cfg::LDS_DMA
+                                              : Cfg::LDS;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Engine<Cfg, Prob> e(prm, p, s, (SKG_LDS char*)lds);
   e.run();

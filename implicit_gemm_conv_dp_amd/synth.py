@@ -150,7 +150,7 @@ WORKLOADS = {
     1: GemmWorkload(1, "gemm_f16_256x256x4096_pool6_linear", 256, 256, 4096, "f16", "f16",
                     "uniform", "128x128x32", ("dp_sk",), ("linear",), 6),
     2: GemmWorkload(2, "gemm_bf16_4864x4096x4096_tree", 4864, 4096, 4096, "bf16", "bf16",
-                    "normal01", "256x256x64", ("dp_sk", "persistent"), ("tree",), 256),
+                    "normal01", "256x256x64", ("persistent", "dp_sk"), ("tree",), 256),
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
                      (1, 1), (1, 1), 1, "f16", "uniform", "128x128x64",
                      ("dp_sk", "persistent"), ("linear", "tree", "atomic", "workspace"), 256),

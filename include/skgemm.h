@@ -17,8 +17,10 @@
  * #13151 "feat(rocke): stream-K for implicit-GEMM conv wgrad", Technical
  * Details: Partitioner).  Tiles shared by several CTAs are fixed up in one of
  * four ways (same PR, Technical Details: Wgrad kernel): linear and tree are
- * deterministic hand-offs through per-(CTA, wave) flags with agent-scope
- * release/acquire; atomic adds fp32 into a zeroed fp32 output; workspace adds
+ * deterministic hand-offs through per-(CTA, wave) flags with device-scope
+ * release/acquire ordering (partials written and read at device scope, the
+ * flag stored after they complete); atomic adds fp32 into a zeroed fp32
+ * output; workspace adds
  * fp32 into zeroed scratch followed by a second-stage reduce.
  *
  * Status codes follow the single-problem ABI of the stream-K GEMM bridge
@@ -64,8 +66,11 @@ enum skg_dtype {
  *                       comparator the stream-K launch is measured against);
  *   SKG_MODE_DP_SK      grid = stream-K CTAs (block ids 0..sk_ctas-1) then
  *                       one CTA per data-parallel tile;
- *   SKG_MODE_PERSISTENT grid = the pool; each CTA runs its stream-K range,
- *                       then data-parallel tiles b, b+grid, ... */
+ *   SKG_MODE_PERSISTENT grid = the pool; each CTA runs data-parallel tiles
+ *                       b, b+grid, ... and its stream-K range: a first
+ *                       segment that only hands a partial on runs before
+ *                       the data-parallel tiles, the segments it owns after
+ *                       them (so their folds find the partials ready). */
 enum skg_mode { SKG_MODE_DP = 0, SKG_MODE_DP_SK = 1, SKG_MODE_PERSISTENT = 2 };
 
 /* Fix-up of tiles shared by several stream-K CTAs (PR #13151, same section).

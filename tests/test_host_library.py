@@ -263,16 +263,21 @@ def test_flag_ordering_in_isa():
                 continue
             n_kernels += 1
             ins = instrs(body)
-            wbl2 = [i for i, x in enumerate(ins) if x.startswith("buffer_wbl2 sc1")]
-            inv = [i for i, x in enumerate(ins) if x.startswith("buffer_inv sc1")]
-            assert wbl2 and inv, name
-            for i in wbl2:
-                # all earlier stores complete, L2 written back, then the flag store
-                assert any(x.startswith("s_waitcnt vmcnt(0)") for x in ins[max(0, i - 4):i]), name
-                nxt = [x for x in ins[i + 1:i + 4] if not x.startswith("s_")]
-                assert nxt and nxt[0].startswith("global_store_dword") and nxt[0].endswith("sc1"), name
-            for i in inv:
-                assert ins[i - 1].startswith("s_waitcnt vmcnt(0)"), name
+            # No L2-wide write-back or invalidation anywhere in the kernel.
+            assert not any(x.startswith(("buffer_wbl2", "buffer_inv")) for x in ins), name
+            # Partials go out and come back at device scope (sc1).
+            assert any(x.startswith("buffer_store_dwordx4") and x.endswith("sc1") for x in ins), name
+            assert any(x.startswith("buffer_load_dwordx4") and x.endswith("sc1") for x in ins), name
+            # The flag store (the only device-scope global store) comes right
+            # after a wait for every earlier store of the wave.
+            flags = [i for i, x in enumerate(ins)
+                     if x.startswith("global_store_dword ") and x.endswith("sc1")]
+            assert flags, name + ": no device-scope flag store"
+            for i in flags:
+                w = [j for j in range(max(0, i - 4), i) if ins[j].startswith("s_waitcnt")]
+                assert w and "vmcnt(0)" in ins[w[-1]], name
+                between = ins[w[-1] + 1:i]
+                assert not any(x.startswith(("buffer_store", "global_store")) for x in between), name
             polls = [x for x in ins if x.startswith("global_load_dword ") and x.endswith("sc1")]
-            assert polls, name + ": no agent-coherent poll"
+            assert polls, name + ": no device-scope poll"
     assert n_kernels >= 17
