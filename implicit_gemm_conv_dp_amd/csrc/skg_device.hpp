@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #define SKG_DEV __device__ __forceinline__
@@ -52,6 +54,15 @@ SKG_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voff) {
 }
 
 SKG_DEV uint32_t lds_addr(const SKG_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, int E, class F>
+SKG_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Cross-CTA hand-off (rocm-libraries PR #13151, commit adding the fence and

@@ -111,6 +111,14 @@ struct TileCfg {
   static constexpr int NSLOT = LDS_BUDGET / SLOT > 8 ? 8 : LDS_BUDGET / SLOT;
   static constexpr bool GROUPED = RB == 128 && NSLOT >= 4 && KSTEPS % 2 == 0;
   static constexpr int LDS_GRP = NSLOT * SLOT > EPI_BYTES ? NSLOT * SLOT : EPI_BYTES;
+  // Spread the refill DMAs among the MFMAs (one resident CTA per CU, 16-bit
+  // operands); otherwise issue them in one burst after the barrier, which
+  // keeps them further ahead (two CTAs per CU hide the burst) and the
+  // register footprint lower (fp8 fragments are twice as large).
+  static constexpr bool SPREAD = TM == 256 && TN == 256 && ESZ == 2;
+  // Resident CTAs per CU the register allocation must allow: tiles of up
+  // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
+  static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
   static_assert(RB == 64 || RB == 128, "LDS row layout");
   static_assert(FM >= 1 && FN >= 1 && WTM % MN == 0 && WTN % MN == 0, "wave tile");
   static_assert(KSTEPS >= 1 && RB % Op::KB == 0, "k steps");
@@ -250,7 +258,44 @@ struct GemmDmaLoader : DmaRows<Cfg, Cfg::RBS> {
 template <class Cfg>
 struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
   static constexpr bool kDma = true, kGrouped = true;
+  typedef DmaRows<Cfg, Cfg::RB> Base;
   static_assert(Cfg::RB == 128, "whole-line rows");
+
+  // Where the two groups refilled during one MAC iteration go: B of one
+  // iteration (kb_b: its first K byte) into slot_b, A of the next into
+  // slot_a.  A group that is not `live` (past the segment) reads nothing
+  // and zero-fills its slot, which nobody reads.
+  struct Refill {
+    SKG_LDS char* slot_b;
+    SKG_LDS char* slot_a;
+    uint32_t kb_b, kb_a;
+    bool live_b, live_a;
+  };
+
+  // DMA instruction N of a refill: [0, UB) for the B group, then A.
+  template <int N>
+  SKG_DEV void refill(const Refill& r) const {
+    if constexpr (N < Base::UB) {
+      const bool ok = r.live_b && r.kb_b < this->lim;
+      dma16(this->rb, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + this->wave * 1024),
+            ok ? this->offb + N * this->stepb + r.kb_b : kOOB);
+    } else {
+      constexpr int U = N - Base::UB;
+      const bool ok = r.live_a && r.kb_a < this->lim;
+      dma16(this->ra, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + this->wave * 1024),
+            ok ? this->offa + U * this->stepa + r.kb_a : kOOB);
+    }
+  }
+
+  // Group j of the segment that starts at MAC iteration it0, into `slot`;
+  // zero fill when not `live`.
+  SKG_DEV void issue_live(int j, int it0, SKG_LDS char* slot, bool live) const {
+    const uint32_t kb = live ? (uint32_t)(it0 + (j >> 1)) * Cfg::RB : 0xffffffffu;
+    if ((j & 1) == 0)
+      this->template issue_rows<true, false>(kb, slot, nullptr);
+    else
+      this->template issue_rows<false, true>(kb, nullptr, slot);
+  }
 
   // Group j of the segment that starts at MAC iteration it0, into `slot`.
   SKG_DEV void issue(int j, int it0, SKG_LDS char* slot) const {
@@ -656,8 +701,73 @@ struct Engine {
     }
   }
 
+  // The MFMAs of rows [F0, F1) of one k-step with DMA instructions
+  // [D0, D1) of a refill spread among them in program order, so that the
+  // wave issues each DMA while an MFMA runs instead of in one burst.
+  template <int F0, int F1, int D0, int D1, class Refill>
+  SKG_DEV void mma_dma(const FragA& fa, const FragB& fb, const Loader& ld, const Refill& rf) {
+    constexpr int NM = (F1 - F0) * Cfg::FN, ND = D1 - D0;
+    static_for<0, NM>([&](auto m_) {
+      constexpr int m = decltype(m_)::value;
+      constexpr int f = F0 + m / Cfg::FN, g = m % Cfg::FN;
+      Cfg::Op::run(acc[f][g], fb[g], fa[f]);  // transposed block
+      if constexpr (ND > 0) {
+        // DMA d follows MFMA (d * NM) / ND
+        static_for<0, ND>([&](auto d_) {
+          constexpr int d = decltype(d_)::value;
+          if constexpr ((d * NM) / ND == m) ld.template refill<D0 + d>(rf);
+        });
+      }
+    });
+  }
+
+  // One MAC iteration i of the grouped pipeline.  DMA: refill the two slots
+  // of iteration i-1 (freed by the barrier that started iteration i) with
+  // groups 2i-2+NSLOT (B of iteration i+1+(NSLOT-5)/2) and 2i-1+NSLOT,
+  // spread over the k-steps.  Not in iteration 0 (no slot is free yet) nor
+  // in the last (nothing left to load).
+  template <bool LAST, bool DMA>
+  SKG_DEV void grp_iter_spread(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G,
+                               int k0) {
+    static_assert(Cfg::NSLOT % 2 == 1, "the first refilled group is a B group");
+    constexpr int NDMA = DMA ? Loader::UA + Loader::UB : 0;
+    constexpr int PER = NDMA / Cfg::KSTEPS;  // DMA instructions per k-step
+    static_assert(NDMA % Cfg::KSTEPS == 0, "DMA spread");
+    typename Loader::Refill rf;
+    if constexpr (DMA) {
+      const int jb = 2 * i - 2 + Cfg::NSLOT, ja = jb + 1;
+      rf.slot_b = slot(jb);
+      rf.slot_a = slot(ja);
+      rf.kb_b = (uint32_t)(k0 + (jb >> 1)) * Cfg::RB;
+      rf.kb_a = (uint32_t)(k0 + (ja >> 1)) * Cfg::RB;
+      rf.live_b = jb < G;
+      rf.live_a = ja < G;
+    }
+    const SKG_LDS char* sa = slot(2 * i);
+    const SKG_LDS char* sb = slot(2 * i + 1);
+    static_for<0, Cfg::KSTEPS - 1>([&](auto ks_) {
+      constexpr int ks = decltype(ks_)::value;
+      load_frags_ab<Cfg::RB>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
+      mma_dma<0, Cfg::FM, ks * PER, (ks + 1) * PER>(fa[ks & 1], fb[ks & 1], ld, rf);
+      __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
+    });
+    constexpr int KL = Cfg::KSTEPS - 1, CB = KL & 1;
+    mma_dma<0, Cfg::FM / 2, KL * PER, (KL + 1) * PER>(fa[CB], fb[CB], ld, rf);
+    if constexpr (!LAST) {
+      // Groups 2i+2 and 2i+3 (iteration i+1) have landed once only the A
+      // group refilled last is younger.
+      wait_vm<Loader::UA>();
+      lds_barrier();
+      load_frags_ab<Cfg::RB>(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
+    }
+    mma_dma<Cfg::FM / 2, Cfg::FM, 0, 0>(fa[CB], fb[CB], ld, rf);
+  }
+
+  // Burst variant: at the end of iteration i the two slots it used are
+  // refilled right after the barrier with groups 2i+NSLOT and 2i+NSLOT+1.
   template <bool LAST>
-  SKG_DEV void grp_iter(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G, int k0) {
+  SKG_DEV void grp_iter_burst(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G,
+                              int k0) {
     const SKG_LDS char* sa = slot(2 * i);
     const SKG_LDS char* sb = slot(2 * i + 1);
 #pragma unroll
@@ -683,16 +793,35 @@ struct Engine {
     __builtin_amdgcn_s_waitcnt(0);  // see mainloop_dma
     zero_acc();
     const int I = k1 - k0, G = 2 * I;  // I >= 1
-#pragma unroll
-    for (int j = 0; j < Cfg::NSLOT; ++j)
-      if (j < G) ld.issue(j, k0, slot(j));
-    wait_groups(min(Cfg::NSLOT, G) - 2);
-    lds_barrier();
     FragA fa[2];
     FragB fb[2];
-    load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
-    for (int i = 0; i + 1 < I; ++i) grp_iter<false>(fa, fb, ld, i, G, k0);
-    grp_iter<true>(fa, fb, ld, I - 1, G, k0);
+    if constexpr (Cfg::SPREAD) {
+      // Prologue: all NSLOT slots; groups past the segment only zero-fill.
+      static_for<0, Cfg::NSLOT>([&](auto j_) {
+        constexpr int j = decltype(j_)::value;
+        ld.issue_live(j, k0, slot(j), j < G);
+      });
+      wait_groups(Cfg::NSLOT - 2);
+      lds_barrier();
+      load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
+      if (I == 1) {
+        grp_iter_spread<true, false>(fa, fb, ld, 0, G, k0);
+      } else {
+        grp_iter_spread<false, false>(fa, fb, ld, 0, G, k0);
+        for (int i = 1; i + 1 < I; ++i) grp_iter_spread<false, true>(fa, fb, ld, i, G, k0);
+        grp_iter_spread<true, false>(fa, fb, ld, I - 1, G, k0);
+      }
+      wait_vm<0>();  // zero-fill loads of groups past the segment
+    } else {
+#pragma unroll
+      for (int j = 0; j < Cfg::NSLOT; ++j)
+        if (j < G) ld.issue(j, k0, slot(j));
+      wait_groups(min(Cfg::NSLOT, G) - 2);
+      lds_barrier();
+      load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
+      for (int i = 0; i + 1 < I; ++i) grp_iter_burst<false>(fa, fb, ld, i, G, k0);
+      grp_iter_burst<true>(fa, fb, ld, I - 1, G, k0);
+    }
     __syncthreads();  // every wave is done with the ring before LDS is reused
   }
 
@@ -1105,7 +1234,7 @@ struct Engine {
 };
 
 template <class Cfg, class Prob>
-__global__ __launch_bounds__(Cfg::THREADS, 1) void sk_kernel(typename Prob::Params prm, KPlan p,
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_CTAS) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
   constexpr int kLds = Prob::Loader::kGrouped ? Cfg::LDS_GRP
                        : Prob::Loader::kDma   ? Cfg::LDS_DMA
