@@ -130,7 +130,7 @@ struct TileCfg {
 // i.e. column-major B) are K-contiguous; each thread moves 16-byte chunks.
 template <class Cfg>
 struct GemmLoader {
-  static constexpr bool kDma = false, kGrouped = false;
+  static constexpr bool kDma = false, kGrouped = false, kTrans = false;
   // Chunk j = tid + THREADS*u sits at row j / CPR, chunk j % CPR; THREADS is
   // a multiple of CPR, so unit u only moves the row by u * RSTEP.
   static constexpr int UA = (Cfg::TM * Cfg::CPR) / Cfg::THREADS;
@@ -242,7 +242,7 @@ struct DmaRows {
 // A and B tiles.
 template <class Cfg>
 struct GemmDmaLoader : DmaRows<Cfg, Cfg::RBS> {
-  static constexpr bool kDma = true, kGrouped = false;
+  static constexpr bool kDma = true, kGrouped = false, kTrans = false;
   typedef DmaRows<Cfg, Cfg::RBS> Base;
   static constexpr int LPS = Base::UA + Base::UB;  // instructions per sub-stage
 
@@ -257,7 +257,7 @@ struct GemmDmaLoader : DmaRows<Cfg, Cfg::RBS> {
 // wave-instruction reads eight whole 128-byte lines.
 template <class Cfg>
 struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
-  static constexpr bool kDma = true, kGrouped = true;
+  static constexpr bool kDma = true, kGrouped = true, kTrans = false;
   typedef DmaRows<Cfg, Cfg::RB> Base;
   static_assert(Cfg::RB == 128, "whole-line rows");
 
@@ -268,7 +268,7 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
   struct Refill {
     SKG_LDS char* slot_b;
     SKG_LDS char* slot_a;
-    uint32_t kb_b, kb_a;
+    int it_b, it_a;  // MAC iterations (tile-relative) of the two groups
     bool live_b, live_a;
   };
 
@@ -276,14 +276,16 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
   template <int N>
   SKG_DEV void refill(const Refill& r) const {
     if constexpr (N < Base::UB) {
-      const bool ok = r.live_b && r.kb_b < this->lim;
+      const uint32_t kb = (uint32_t)r.it_b * Cfg::RB;
+      const bool ok = r.live_b && kb < this->lim;
       dma16(this->rb, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + this->wave * 1024),
-            ok ? this->offb + N * this->stepb + r.kb_b : kOOB);
+            ok ? this->offb + N * this->stepb + kb : kOOB);
     } else {
       constexpr int U = N - Base::UB;
-      const bool ok = r.live_a && r.kb_a < this->lim;
+      const uint32_t kb = (uint32_t)r.it_a * Cfg::RB;
+      const bool ok = r.live_a && kb < this->lim;
       dma16(this->ra, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + this->wave * 1024),
-            ok ? this->offa + U * this->stepa + r.kb_a : kOOB);
+            ok ? this->offa + U * this->stepa + kb : kOOB);
     }
   }
 
@@ -317,7 +319,7 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
 // from out-of-range buffer offsets.
 template <class Cfg>
 struct WgradLoader {
-  static constexpr bool kDma = false, kGrouped = false;
+  static constexpr bool kDma = false, kGrouped = false, kTrans = false;
   static_assert(Cfg::ESZ == 2, "wgrad runs on 16-bit inputs");
   static constexpr int QB = Cfg::TK / 8;             // 8-wide q blocks per K step
   static constexpr int NA = (Cfg::TM / 8) * QB;      // blocks of the A tile
@@ -455,10 +457,154 @@ struct GemmProblem {
   SKG_DEV static int dtype_c(const Params& g) { return g.dtype_c; }
 };
 
+// Chunk swizzle of the wgrad operand tiles in LDS.  A tile holds one row
+// per reduction index q (P bytes: the tile's channels, contiguous as in
+// NHWC memory); the 16-byte chunk index is XORed with a function of the row
+// so that the transposing fragment reads -- four consecutive rows of 32
+// bytes per group of 16 lanes -- hit distinct banks (64 banks of 4 bytes).
+template <int P, int MN>
+SKG_DEV int tr_swz(int row) {
+  static_assert(P >= 256 || (P == 128) || (P == 64 && MN == 16), "wgrad tile pitch");
+  if constexpr (P >= 256)
+    return (4 * (row & 1)) ^ (8 * ((row >> 1) & 1));
+  else if constexpr (P == 128 && MN == 32)
+    return 4 * ((row >> 1) & 1);
+  else if constexpr (P == 128)
+    return (2 * ((row >> 1) & 1)) ^ (4 * ((row >> 3) & 1));
+  else
+    return 2 * ((row >> 3) & 1);
+}
+
+// wgrad operand loader for the grouped pipeline, direct to LDS without any
+// transposition: group j of a segment is the A tile (j even: rows of dY,
+// the tile's output channels of TK consecutive q) or the B tile (j odd:
+// rows of im2col(X), the tile's (r, s, c') columns) of MAC iteration j/2.
+// Every row is one contiguous run of channels in NHWC memory.  The MFMA
+// fragments, which want the reduction index contiguous per lane, are read
+// back with the gfx950 transposing LDS read.  Zero padding, rows past the
+// reduction and channels past a group come back as zero (out-of-range
+// buffer offsets).
+template <class Cfg>
+struct WgradGrpLoader {
+  static constexpr bool kDma = true, kGrouped = true, kTrans = true;
+  static_assert(Cfg::ESZ == 2, "wgrad runs on 16-bit inputs");
+  static constexpr int PA = Cfg::TM * 2, PB = Cfg::TN * 2;  // bytes per q row
+  static constexpr int CPRA = PA / 16, CPRB = PB / 16;
+  static constexpr int STEPA = Cfg::THREADS / CPRA, STEPB = Cfg::THREADS / CPRB;
+  static constexpr int UA = Cfg::TK / STEPA, UB = Cfg::TK / STEPB;  // instructions per group
+  static_assert(Cfg::THREADS % CPRA == 0 && Cfg::THREADS % CPRB == 0 && UA * STEPA == Cfg::TK &&
+                    UB * STEPB == Cfg::TK && UA >= 1 && UB >= 1,
+                "wgrad DMA mapping");
+
+  __amdgpu_buffer_rsrc_t rx, rdy;
+  uint32_t a_chan;  // byte offset of this thread's A chunk within a dY row
+  uint32_t b_chan;  // byte offset of its B chunk within an X pixel
+  int rowa, rowb;   // first tile row of its chunks
+  int tap_r, tap_s;
+  bool a_ok, b_ok;  // the chunk's channels exist
+  int wave;
+  // problem constants (uniform)
+  uint32_t k2, c2;
+  int kred, H, W, Ho, Wo, sh, sw, ph, pw;
+  FastDiv div_howo, div_wo;
+
+  SKG_DEV void init(const WgradParams& w, int group, int mrow0, int n0, int tid) {
+    rx = make_rsrc(w.X, w.x_bytes);
+    rdy = make_rsrc(w.dY, w.dy_bytes);
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    k2 = (uint32_t)w.K * 2;
+    c2 = (uint32_t)w.C * 2;
+    kred = w.kred;
+    H = w.H;
+    W = w.W;
+    Ho = w.Ho;
+    Wo = w.Wo;
+    sh = w.sh;
+    sw = w.sw;
+    ph = w.ph;
+    pw = w.pw;
+    div_howo = w.div_howo;
+    div_wo = w.div_wo;
+    rowa = tid / CPRA;
+    const int lca = (tid % CPRA) ^ tr_swz<PA, Cfg::MN>(rowa);
+    const int m = mrow0 + lca * 8;
+    a_ok = m < w.kpg;
+    a_chan = (uint32_t)(group * w.kpg + m) * 2;
+    rowb = tid / CPRB;
+    const int lcb = (tid % CPRB) ^ tr_swz<PB, Cfg::MN>(rowb);
+    const int nidx = n0 + lcb * 8;
+    b_ok = nidx < w.gemm_n;
+    const uint32_t rs = fdiv((uint32_t)nidx, w.div_cpg);
+    const int cc = nidx - (int)rs * w.cpg;
+    const uint32_t r = fdiv(rs, w.div_s);
+    tap_r = (int)r;
+    tap_s = (int)(rs - r * w.S);
+    b_chan = (uint32_t)(group * w.cpg + cc) * 2;
+  }
+
+  // dY row q of this thread's A chunk, or kOOB.
+  SKG_DEV uint32_t a_off(int q, bool live) const {
+    return (live && a_ok && q < kred) ? (uint32_t)q * k2 + a_chan : kOOB;
+  }
+  // X pixel of q shifted by this thread's filter tap, or kOOB (padding).
+  SKG_DEV uint32_t b_off(int q, bool live) const {
+    const uint32_t img = fdiv((uint32_t)q, div_howo);
+    const int rem = q - (int)img * Ho * Wo;
+    const uint32_t ho = fdiv((uint32_t)rem, div_wo);
+    const int wo = rem - (int)ho * Wo;
+    const int hi = (int)ho * sh - ph + tap_r;
+    const int wi = wo * sw - pw + tap_s;
+    const bool ok = live && b_ok && q < kred && hi >= 0 && hi < H && wi >= 0 && wi < W;
+    return ok ? (uint32_t)(((int)img * H + hi) * W + wi) * c2 + b_chan : kOOB;
+  }
+
+  template <bool IS_A>
+  SKG_DEV void issue_group(int it, SKG_LDS char* slot, bool live) const {
+    const int q0 = it * Cfg::TK;
+    if constexpr (IS_A) {
+#pragma unroll
+      for (int u = 0; u < UA; ++u)
+        dma16(rdy, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), a_off(q0 + rowa + u * STEPA, live));
+    } else {
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        dma16(rx, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), b_off(q0 + rowb + u * STEPB, live));
+    }
+  }
+
+  // Group j of the segment that starts at MAC iteration it0, into `slot`;
+  // zero fill when not `live`.
+  SKG_DEV void issue_live(int j, int it0, SKG_LDS char* slot, bool live) const {
+    if ((j & 1) == 0)
+      issue_group<true>(it0 + (j >> 1), slot, live);
+    else
+      issue_group<false>(it0 + (j >> 1), slot, live);
+  }
+  SKG_DEV void issue(int j, int it0, SKG_LDS char* slot) const { issue_live(j, it0, slot, true); }
+
+  struct Refill {
+    SKG_LDS char* slot_b;
+    SKG_LDS char* slot_a;
+    int it_b, it_a;
+    bool live_b, live_a;
+  };
+  template <int N>
+  SKG_DEV void refill(const Refill& r) const {
+    if constexpr (N < UB) {
+      dma16(rx, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + wave * 1024),
+            b_off(r.it_b * Cfg::TK + rowb + N * STEPB, r.live_b));
+    } else {
+      constexpr int U = N - UB;
+      dma16(rdy, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + wave * 1024),
+            a_off(r.it_a * Cfg::TK + rowa + U * STEPA, r.live_a));
+    }
+  }
+};
+
 template <class Cfg>
 struct WgradProblem {
   typedef WgradParams Params;
-  typedef WgradLoader<Cfg> Loader;
+  typedef typename std::conditional<Cfg::GROUPED, WgradGrpLoader<Cfg>, WgradLoader<Cfg>>::type Loader;
 
   SKG_DEV static void setup(const Params& w, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
@@ -701,6 +847,71 @@ struct Engine {
     }
   }
 
+  // Fragments of k-step ks of the grouped pipeline from the A tile at sa
+  // and the B tile at sb: K-contiguous rows (GEMM) read directly, q-row
+  // tiles (wgrad) with the transposing read.
+  SKG_DEV void grp_frags(FragA& fa, FragB& fb, const SKG_LDS char* sa, const SKG_LDS char* sb,
+                         int ks) const {
+    if constexpr (Loader::kTrans)
+      load_frags_tr(fa, fb, sa, sb, ks);
+    else
+      load_frags_ab<Cfg::RB>(fa, fb, sa, sb, ks);
+  }
+
+  // Transposing fragment reads.  ds_read_b64_tr_b16 hands lane i of each
+  // group of 16 lanes the element in column i of four consecutive rows,
+  // taking the row from lane 4s + i/4 of the group and the column offset
+  // from its address; pointing lane j of the group at row kb + j/4,
+  // columns mb + 4*(j%4) .. +3 therefore gives lane i the four consecutive
+  // reduction indices kb .. kb+3 of column mb + i.  Two such reads (rows
+  // +0..3 and +4..7) make the eight-element MFMA operand; kb is 8 * (lane /
+  // 32) for the 32x32 MFMA (16 reduction indices per k-step) and 8 * (lane
+  // / 16) for the 16x16 one (32 per k-step).  tro_a / tro_b
+  // hold, per lane and fragment, the byte offset of the first read of
+  // k-step 0; k-steps and the second read are immediate offsets.
+  uint32_t tro_a[Cfg::FM], tro_b[Cfg::FN];
+
+  template <int P>
+  SKG_DEV uint32_t tr_offset(int col0) const {
+    const int grp = lane >> 4, jj = lane & 15;
+    const int mb = Cfg::MN == 32 ? 16 * (grp & 1) : 0;
+    const int kb = Cfg::MN == 32 ? 8 * (grp >> 1) : 8 * grp;
+    const int row = kb + (jj >> 2);
+    const int col = col0 + mb + 4 * (jj & 3);
+    return (uint32_t)(row * P + (((col >> 3) ^ tr_swz<P, Cfg::MN>(row)) << 4) + (col & 7) * 2);
+  }
+
+  SKG_DEV void tr_init() {
+    if constexpr (Loader::kTrans) {
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f) tro_a[f] = tr_offset<Loader::PA>(wm * Cfg::WTM + f * Cfg::MN);
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g) tro_b[g] = tr_offset<Loader::PB>(wn * Cfg::WTN + g * Cfg::MN);
+    }
+  }
+
+  template <int P>
+  SKG_DEV static Frag tr_frag(const SKG_LDS char* base, uint32_t off, int ks) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef SKG_LDS v4i16 lds_v4i16;
+    constexpr int KE = Cfg::Op::KB / 2;  // reduction indices per k-step
+    const SKG_LDS char* p = base + off + ks * KE * P;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * P));
+    const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+    return Frag{l2[0], l2[1], h2[0], h2[1]};
+  }
+
+  SKG_DEV void load_frags_tr(FragA& fa, FragB& fb, const SKG_LDS char* sa, const SKG_LDS char* sb,
+                             int ks) const {
+    if constexpr (Loader::kTrans) {
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f) fa[f] = tr_frag<Loader::PA>(sa, tro_a[f], ks);
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g) fb[g] = tr_frag<Loader::PB>(sb, tro_b[g], ks);
+    }
+  }
+
   // The MFMAs of rows [F0, F1) of one k-step with DMA instructions
   // [D0, D1) of a refill spread among them in program order, so that the
   // wave issues each DMA while an MFMA runs instead of in one burst.
@@ -738,8 +949,8 @@ struct Engine {
       const int jb = 2 * i - 2 + Cfg::NSLOT, ja = jb + 1;
       rf.slot_b = slot(jb);
       rf.slot_a = slot(ja);
-      rf.kb_b = (uint32_t)(k0 + (jb >> 1)) * Cfg::RB;
-      rf.kb_a = (uint32_t)(k0 + (ja >> 1)) * Cfg::RB;
+      rf.it_b = k0 + (jb >> 1);
+      rf.it_a = k0 + (ja >> 1);
       rf.live_b = jb < G;
       rf.live_a = ja < G;
     }
@@ -747,7 +958,7 @@ struct Engine {
     const SKG_LDS char* sb = slot(2 * i + 1);
     static_for<0, Cfg::KSTEPS - 1>([&](auto ks_) {
       constexpr int ks = decltype(ks_)::value;
-      load_frags_ab<Cfg::RB>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
+      grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
       mma_dma<0, Cfg::FM, ks * PER, (ks + 1) * PER>(fa[ks & 1], fb[ks & 1], ld, rf);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
     });
@@ -758,7 +969,7 @@ struct Engine {
       // group refilled last is younger.
       wait_vm<Loader::UA>();
       lds_barrier();
-      load_frags_ab<Cfg::RB>(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
+      grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
     }
     mma_dma<Cfg::FM / 2, Cfg::FM, 0, 0>(fa[CB], fb[CB], ld, rf);
   }
@@ -772,7 +983,7 @@ struct Engine {
     const SKG_LDS char* sb = slot(2 * i + 1);
 #pragma unroll
     for (int ks = 0; ks + 1 < Cfg::KSTEPS; ++ks) {
-      load_frags_ab<Cfg::RB>(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
+      grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
       mma(fa[ks & 1], fb[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
     }
@@ -783,7 +994,7 @@ struct Engine {
       lds_barrier();
       if (2 * i + Cfg::NSLOT < G) ld.issue(2 * i + Cfg::NSLOT, k0, slot(2 * i));
       if (2 * i + Cfg::NSLOT + 1 < G) ld.issue(2 * i + Cfg::NSLOT + 1, k0, slot(2 * i + 1));
-      load_frags_ab<Cfg::RB>(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
+      grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
     }
     mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
   }
@@ -792,6 +1003,7 @@ struct Engine {
     static_assert(Cfg::KSTEPS % 2 == 0, "k-step 0 of every iteration uses buffer 0");
     __builtin_amdgcn_s_waitcnt(0);  // see mainloop_dma
     zero_acc();
+    tr_init();
     const int I = k1 - k0, G = 2 * I;  // I >= 1
     FragA fa[2];
     FragB fb[2];
@@ -803,7 +1015,7 @@ struct Engine {
       });
       wait_groups(Cfg::NSLOT - 2);
       lds_barrier();
-      load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
+      grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
       if (I == 1) {
         grp_iter_spread<true, false>(fa, fb, ld, 0, G, k0);
       } else {
@@ -818,7 +1030,7 @@ struct Engine {
         if (j < G) ld.issue(j, k0, slot(j));
       wait_groups(min(Cfg::NSLOT, G) - 2);
       lds_barrier();
-      load_frags_ab<Cfg::RB>(fa[0], fb[0], slot(0), slot(1), 0);
+      grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
       for (int i = 0; i + 1 < I; ++i) grp_iter_burst<false>(fa, fb, ld, i, G, k0);
       grp_iter_burst<true>(fa, fb, ld, I - 1, G, k0);
     }
