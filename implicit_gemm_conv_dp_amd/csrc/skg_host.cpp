@@ -25,7 +25,7 @@ constexpr int M_F8 = 1 << SKG_F8E4M3;
 // Must agree with the kernel instances compiled in skg_api.hip.
 const TileDesc kTiles[SKG_TILE_COUNT] = {
     /* 128x128x32  */ {128, 128, 32, 4, M_F16 | M_BF16, M_F16 | M_BF16},
-    /* 256x256x64  */ {256, 256, 64, 4, M_F16 | M_BF16, 0},
+    /* 256x256x64  */ {256, 256, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16},
     /* 256x256x128 */ {256, 256, 128, 4, M_F8, 0},
     /* 32x64x64    */ {32, 64, 64, 4, 0, M_F16 | M_BF16},
     /* 128x128x64  */ {128, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16},

@@ -16,6 +16,7 @@ WgradInst by_tile(int tile_id) {
     case SKG_TILE_32x64x64: return make<TileCfg<DT, 32, 64, 64, 2, 2, 16>>();
     case SKG_TILE_128x128x64: return make<TileCfg<DT, 128, 128, 64, 2, 2, 32>>();
     case SKG_TILE_256x128x64: return make<TileCfg<DT, 256, 128, 64, 2, 2, 32>>();
+    case SKG_TILE_256x256x64: return make<TileCfg<DT, 256, 256, 64, 2, 2, 32>>();
     default: return {nullptr, nullptr};
   }
 }

@@ -1007,7 +1007,9 @@ struct Engine {
     const int I = k1 - k0, G = 2 * I;  // I >= 1
     FragA fa[2];
     FragB fb[2];
-    if constexpr (Cfg::SPREAD) {
+    // The wgrad refills compute an im2col address per row, which does not
+    // fit between the MFMAs next to 256 accumulators: they take the burst.
+    if constexpr (Cfg::SPREAD && !Loader::kTrans) {
       // Prologue: all NSLOT slots; groups past the segment only zero-fill.
       static_for<0, Cfg::NSLOT>([&](auto j_) {
         constexpr int j = decltype(j_)::value;
@@ -1273,16 +1275,20 @@ struct Engine {
 #pragma unroll
     for (int pass = 0; pass < Cfg::WM; ++pass) {
       if (wm == pass) {
+        // One per-lane base address; every (f, g, q) is a constant offset
+        // from it (the column step of element group q is 8 or 4).
+        SKG_LDS char* st = lds + acc_row<Cfg::MN>(lane) * Cfg::EPI_PITCH32 +
+                           (wn * Cfg::WTN + acc_col<Cfg::MN>(0, lane)) * 4;
+        constexpr int QSTEP = Cfg::MN == 32 ? 8 : 4;
 #pragma unroll
         for (int f = 0; f < Cfg::FM; ++f) {
-          const int lrow = f * Cfg::MN + acc_row<Cfg::MN>(lane);
 #pragma unroll
           for (int g = 0; g < Cfg::FN; ++g)
 #pragma unroll
             for (int q = 0; q < Cfg::NACC / 4; ++q) {
               const f32x4 v = {acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
                                acc[f][g][4 * q + 3]};
-              *(SKG_LDS f32x4*)(lds + lrow * Cfg::EPI_PITCH32 + col_of(g, q) * 4) = v;
+              *(SKG_LDS f32x4*)(st + f * Cfg::MN * Cfg::EPI_PITCH32 + (g * Cfg::MN + q * QSTEP) * 4) = v;
               if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -91,7 +91,7 @@ enum skg_reduction {
  * for the operations and input types skg_tile_info reports. */
 enum skg_tile {
   SKG_TILE_128x128x32 = 0,   /* f16/bf16 GEMM and wgrad, 4 waves */
-  SKG_TILE_256x256x64 = 1,   /* f16/bf16 GEMM, 4 waves */
+  SKG_TILE_256x256x64 = 1,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_256x256x128 = 2,  /* fp8 GEMM, 4 waves */
   SKG_TILE_32x64x64 = 3,     /* f16/bf16 wgrad (small per-group M), 4 waves */
   SKG_TILE_128x128x64 = 4,   /* f16/bf16 GEMM and wgrad, 4 waves */

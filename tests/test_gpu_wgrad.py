@@ -29,7 +29,7 @@ SHAPES = {
     "grouped": (2, 12, 12, 64, 32, 3, 3, (2, 2), (1, 1), 4),
     "wide": (1, 17, 15, 144, 40, 3, 2, (1, 2), (1, 0), 1),
 }
-TILES = ["128x128x32", "32x64x64", "128x128x64", "256x128x64"]
+TILES = ["128x128x32", "32x64x64", "128x128x64", "256x128x64", "256x256x64"]
 
 
 def run(x, dy, shape, fmt, tile, mode, red, ctas, ws=None):

@@ -182,7 +182,7 @@ def test_wgrad_validation_rejects():
     assert "groups" in bad(groups=3)
     assert "multiples of 8" in bad(c=12)
     assert "dtype" in bad(dtype="e4m3")
-    assert "instance" in bad(tile="256x256x64")
+    assert "instance" in bad(tile="256x256x128")
     assert "empty" in bad(h=1, pad=(0, 0))
     assert "stride" in bad(stride=(0, 1))
     assert "ctas" in bad(ctas=0)
