@@ -111,11 +111,10 @@ struct TileCfg {
   static constexpr int NSLOT = LDS_BUDGET / SLOT > 8 ? 8 : LDS_BUDGET / SLOT;
   static constexpr bool GROUPED = RB == 128 && NSLOT >= 4 && KSTEPS % 2 == 0;
   static constexpr int LDS_GRP = NSLOT * SLOT > EPI_BYTES ? NSLOT * SLOT : EPI_BYTES;
-  // Spread the refill DMAs among the MFMAs (one resident CTA per CU, 16-bit
-  // operands); otherwise issue them in one burst after the barrier, which
-  // keeps them further ahead (two CTAs per CU hide the burst) and the
-  // register footprint lower (fp8 fragments are twice as large).
-  static constexpr bool SPREAD = TM == 256 && TN == 256 && ESZ == 2;
+  // Spread the refill DMAs among the MFMAs (256x256 tiles: one resident
+  // CTA per CU); otherwise issue them in one burst after the barrier, which
+  // keeps them further ahead (two CTAs per CU hide the burst).
+  static constexpr bool SPREAD = TM == 256 && TN == 256;
   // Resident CTAs per CU the register allocation must allow: tiles of up
   // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
   static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
@@ -960,6 +959,13 @@ struct Engine {
       constexpr int ks = decltype(ks_)::value;
       grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
       mma_dma<0, Cfg::FM, ks * PER, (ks + 1) * PER>(fa[ks & 1], fb[ks & 1], ld, rf);
+      // Alternate MFMAs and the next k-step's LDS reads from the start of
+      // the k-step, so the reads have the rest of it to land.
+      static_for<0, 8>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      });
+      __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM * Cfg::FN - 8, 0);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
     });
     constexpr int KL = Cfg::KSTEPS - 1, CB = KL & 1;

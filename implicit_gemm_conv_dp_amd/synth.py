@@ -152,7 +152,7 @@ WORKLOADS = {
     2: GemmWorkload(2, "gemm_bf16_4864x4096x4096_tree", 4864, 4096, 4096, "bf16", "bf16",
                     "normal01", "256x256x64", ("persistent", "dp_sk"), ("tree",), 256),
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
-                     (1, 1), (1, 1), 1, "f16", "uniform", "128x128x64",
+                     (1, 1), (1, 1), 1, "f16", "uniform", "256x128x64",
                      ("dp_sk", "persistent"), ("linear", "tree", "atomic", "workspace"), 256),
     4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
                      (2, 2), (1, 1), 32, "bf16", "uniform", "32x64x64", ("dp_sk",), ("linear",),
