@@ -1424,15 +1424,22 @@ struct Engine {
     }
     // Stream-K iterations [it, split) run before the DP tiles and
     // [split, end) after them.  dp / dp_sk: the whole range first.
-    // persistent: only a first segment that continues a tile begun by a
-    // lower CTA (it hands its partial on), then the DP tiles, then the
-    // segments this CTA owns; by then the higher CTAs it folds from have
-    // long handed their partials on, so the wait costs nothing.  Every
-    // segment a CTA waits for is a first segment of a higher CTA, so each
-    // wait still ends (the highest CTA never waits).
+    // persistent: first only a first segment that hands its partial on
+    // without folding anything (a tile begun by a lower CTA, and in a tree
+    // an odd position), then the DP tiles, then the segments that fold --
+    // by then the partials they fold were handed on long before, so the
+    // waits cost nothing.  A CTA only waits for first segments of higher
+    // CTAs (pure hand-offs, which never wait, or folds that wait in turn on
+    // still higher CTAs), so every wait ends.
     int split = end;
-    if (p.mode == MODE_PERSISTENT)
-      split = (it < end && it % p.ipt != 0) ? min(end, (it / p.ipt + 1) * p.ipt) : it;
+    if (p.mode == MODE_PERSISTENT) {
+      split = it;
+      if (it < end && it % p.ipt != 0) {
+        const int t = it / p.ipt, seg_end = min(end, (t + 1) * p.ipt);
+        const Fix fx = fixup(p.dp_tiles + t, it - t * p.ipt, seg_end - t * p.ipt, b);
+        if (fx.nfold == 0) split = seg_end;
+      }
+    }
     while (true) {
       int tile, k0, k1, cta;
       if (it < split || (it < end && dp_tile >= p.dp_tiles)) {
