@@ -140,9 +140,18 @@ def cpu_baseline(wl, inp, target_s):
             break
         grow = min(8.0, max(2.0, target_s / max(t, 1e-3)))
         units = min(full, int(units * grow))
+    # The whole workload takes less than the target: repeat it.
+    reps = 1
+    while t * (reps + 1) / reps < target_s / 2 and units >= full and reps < 64:
+        t_more, _ = run(units)
+        t += t_more
+        reps += 1
+    flops *= reps
     threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
     what = ("rows [0, %d) of the %d-row output" % (units, full)) if wl.op == "gemm" else \
         ("images [0, %d) of %d" % (units, full))
+    if reps > 1:
+        what += ", %d runs" % reps
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "%s, fp64 oracle (numpy float64 matmul), %.1f s" % (what, t),
             "seconds": t}
