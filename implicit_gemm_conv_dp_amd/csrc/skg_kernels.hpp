@@ -288,24 +288,16 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
     }
   }
 
-  // Group j of the segment that starts at MAC iteration it0, into `slot`;
+  // Group j (A when even, B when odd) of MAC iteration `it` into `slot`;
   // zero fill when not `live`.
-  SKG_DEV void issue_live(int j, int it0, SKG_LDS char* slot, bool live) const {
-    const uint32_t kb = live ? (uint32_t)(it0 + (j >> 1)) * Cfg::RB : 0xffffffffu;
+  SKG_DEV void issue_live(int j, int it, SKG_LDS char* slot, bool live) const {
+    const uint32_t kb = live ? (uint32_t)it * Cfg::RB : 0xffffffffu;
     if ((j & 1) == 0)
       this->template issue_rows<true, false>(kb, slot, nullptr);
     else
       this->template issue_rows<false, true>(kb, nullptr, slot);
   }
-
-  // Group j of the segment that starts at MAC iteration it0, into `slot`.
-  SKG_DEV void issue(int j, int it0, SKG_LDS char* slot) const {
-    const uint32_t kb = (uint32_t)(it0 + (j >> 1)) * Cfg::RB;
-    if ((j & 1) == 0)
-      this->template issue_rows<true, false>(kb, slot, nullptr);
-    else
-      this->template issue_rows<false, true>(kb, nullptr, slot);
-  }
+  SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
 };
 
 // ---------------------------------------------------------------------------
@@ -571,15 +563,15 @@ struct WgradGrpLoader {
     }
   }
 
-  // Group j of the segment that starts at MAC iteration it0, into `slot`;
+  // Group j (A when even, B when odd) of MAC iteration `it` into `slot`;
   // zero fill when not `live`.
-  SKG_DEV void issue_live(int j, int it0, SKG_LDS char* slot, bool live) const {
+  SKG_DEV void issue_live(int j, int it, SKG_LDS char* slot, bool live) const {
     if ((j & 1) == 0)
-      issue_group<true>(it0 + (j >> 1), slot, live);
+      issue_group<true>(it, slot, live);
     else
-      issue_group<false>(it0 + (j >> 1), slot, live);
+      issue_group<false>(it, slot, live);
   }
-  SKG_DEV void issue(int j, int it0, SKG_LDS char* slot) const { issue_live(j, it0, slot, true); }
+  SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
 
   struct Refill {
     SKG_LDS char* slot_b;
@@ -830,6 +822,21 @@ struct Engine {
   // all inside the last k-step's MFMAs.
   SKG_DEV SKG_LDS char* slot(int j) const { return lds + (j % Cfg::NSLOT) * Cfg::SLOT; }
 
+  // Order of the MAC iterations of a wgrad segment [k0, k0+L): local step
+  // i runs iteration k0 + (i + rot) % L, rot = -k0 mod L, i.e. every
+  // segment starts at the iteration whose index is a multiple of its
+  // length.  Stream-K segments of different tiles (other groups, other
+  // filter taps) that cover the same reduction indices then tend to read
+  // the same dY and X rows at the same time, which lets them share L2
+  // lines.  A data-parallel tile (k0 = 0) keeps its natural order; GEMM
+  // segments keep theirs.
+  int gk0, gL, grot;
+  SKG_DEV int iter(int i) const {
+    if constexpr (!Loader::kTrans) return gk0 + i;  // GEMM: natural order
+    const int x = i + grot;
+    return gk0 + (x >= gL ? x - gL : x);
+  }
+
   // Wait until at most n groups younger than the awaited one are in flight
   // (younger groups alternate A, B, A, ... starting with an A group).
   SKG_DEV static void wait_groups(int n) {
@@ -948,8 +955,8 @@ struct Engine {
       const int jb = 2 * i - 2 + Cfg::NSLOT, ja = jb + 1;
       rf.slot_b = slot(jb);
       rf.slot_a = slot(ja);
-      rf.it_b = k0 + (jb >> 1);
-      rf.it_a = k0 + (ja >> 1);
+      rf.it_b = iter(jb >> 1);
+      rf.it_a = iter(ja >> 1);
       rf.live_b = jb < G;
       rf.live_a = ja < G;
     }
@@ -998,8 +1005,9 @@ struct Engine {
     if constexpr (!LAST) {
       wait_groups(min(G, 2 * i + Cfg::NSLOT) - (2 * i + 4));
       lds_barrier();
-      if (2 * i + Cfg::NSLOT < G) ld.issue(2 * i + Cfg::NSLOT, k0, slot(2 * i));
-      if (2 * i + Cfg::NSLOT + 1 < G) ld.issue(2 * i + Cfg::NSLOT + 1, k0, slot(2 * i + 1));
+      if (2 * i + Cfg::NSLOT < G) ld.issue(2 * i + Cfg::NSLOT, iter((2 * i + Cfg::NSLOT) >> 1), slot(2 * i));
+      if (2 * i + Cfg::NSLOT + 1 < G)
+        ld.issue(2 * i + Cfg::NSLOT + 1, iter((2 * i + Cfg::NSLOT + 1) >> 1), slot(2 * i + 1));
       grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
     }
     mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
@@ -1011,6 +1019,9 @@ struct Engine {
     zero_acc();
     tr_init();
     const int I = k1 - k0, G = 2 * I;  // I >= 1
+    gk0 = k0;
+    gL = I;
+    grot = (I - k0 % I) % I;
     FragA fa[2];
     FragB fb[2];
     // The wgrad refills compute an im2col address per row, which does not
@@ -1019,7 +1030,7 @@ struct Engine {
       // Prologue: all NSLOT slots; groups past the segment only zero-fill.
       static_for<0, Cfg::NSLOT>([&](auto j_) {
         constexpr int j = decltype(j_)::value;
-        ld.issue_live(j, k0, slot(j), j < G);
+        ld.issue_live(j, iter(j >> 1), slot(j), j < G);
       });
       wait_groups(Cfg::NSLOT - 2);
       lds_barrier();
@@ -1035,7 +1046,7 @@ struct Engine {
     } else {
 #pragma unroll
       for (int j = 0; j < Cfg::NSLOT; ++j)
-        if (j < G) ld.issue(j, k0, slot(j));
+        if (j < G) ld.issue(j, iter(j >> 1), slot(j));
       wait_groups(min(Cfg::NSLOT, G) - 2);
       lds_barrier();
       grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
@@ -1405,21 +1416,23 @@ struct Engine {
   // One bounded work loop: the stream-K range (if any) segment by segment,
   // then this block's data-parallel tiles.
   SKG_DEV void run() {
-    const int b = blockIdx.x;
+    const int blk = blockIdx.x;
+    const bool sk_block = p.mode != MODE_DP && blk < p.sk_ctas;
+    const int b = blk;  // stream-K CTA index (block order)
     int it = 0, end = 0;
-    if (p.mode != MODE_DP && b < p.sk_ctas) {
+    if (sk_block) {
       it = b * p.ipc + min(b, p.extra);
       end = it + p.ipc + (b < p.extra ? 1 : 0);
     }
     int dp_tile, dp_step;
     if (p.mode == MODE_DP) {
-      dp_tile = b;
+      dp_tile = blk;
       dp_step = p.dp_tiles;  // one tile
     } else if (p.mode == MODE_DP_SK) {
-      dp_tile = b >= p.sk_ctas ? b - p.sk_ctas : p.dp_tiles;
+      dp_tile = blk >= p.sk_ctas ? blk - p.sk_ctas : p.dp_tiles;
       dp_step = p.dp_tiles;
     } else {
-      dp_tile = b;
+      dp_tile = blk;
       dp_step = p.grid;
     }
     // Stream-K iterations [it, split) run before the DP tiles and
