@@ -157,6 +157,10 @@ def cpu_baseline(wl, inp, target_s):
             "seconds": t}
 
 
+def names(enum):
+    return {v: k for k, v in enum.items()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,7 +280,10 @@ def main():
         "config": {"workload": wl.name, "tile": tile, "mode": mode, "reduction": red,
                    "ctas": ctas, "plan": {k: plan[k] for k in (
                        "tiles", "iters_per_tile", "dp_tiles", "sk_tiles", "sk_ctas",
-                       "iters_per_sk_cta", "extra_iters", "grid", "max_contrib", "tree_rounds")}},
+                       "iters_per_sk_cta", "extra_iters", "grid", "max_contrib", "tree_rounds")},
+                   "resolved": {"mode": names(skg.MODES)[plan["mode"]],
+                                "reduction": names(skg.REDUCTIONS)[plan["reduction"]],
+                                "ctas": plan["pool"], "slices": plan["slices"]}},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

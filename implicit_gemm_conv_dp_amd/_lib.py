@@ -12,16 +12,17 @@ LIB_PATH = os.path.join(_HERE, "libskgemm.so")
 
 SKG_OK, SKG_ERR_HIP, SKG_ERR_UNSUPPORTED = 0, -1, -2
 F16, BF16, F8E4M3, F32 = 0, 1, 2, 3
-MODE_DP, MODE_DP_SK, MODE_PERSISTENT = 0, 1, 2
-RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE = 0, 1, 2, 3
+MODE_DP, MODE_DP_SK, MODE_PERSISTENT, MODE_SPLITK, MODE_AUTO = 0, 1, 2, 3, 4
+RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO = 0, 1, 2, 3, 4
 OP_GEMM, OP_WGRAD = 0, 1
 TILE_128x128x32, TILE_256x256x64, TILE_256x256x128, TILE_32x64x64, TILE_128x128x64, \
     TILE_256x128x64 = range(6)
 TILE_COUNT = 6
 
-MODES = {"dp": MODE_DP, "dp_sk": MODE_DP_SK, "persistent": MODE_PERSISTENT}
+MODES = {"dp": MODE_DP, "dp_sk": MODE_DP_SK, "persistent": MODE_PERSISTENT,
+         "splitk": MODE_SPLITK, "auto": MODE_AUTO}
 REDUCTIONS = {"linear": RED_LINEAR, "tree": RED_TREE, "atomic": RED_ATOMIC,
-              "workspace": RED_WORKSPACE}
+              "workspace": RED_WORKSPACE, "auto": RED_AUTO}
 DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32}
 TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
          "256x256x128": TILE_256x256x128, "32x64x64": TILE_32x64x64,
@@ -59,7 +60,8 @@ class skg_plan_t(ctypes.Structure):
                 ("tiles_m", "tiles_n", "tiles", "iters_per_tile", "pool", "dp_tiles", "sk_tiles",
                  "sk_ctas", "sk_iters", "iters_per_sk_cta", "extra_iters", "grid", "max_contrib",
                  "linear_partners", "tree_rounds", "flags_bytes", "partials_bytes",
-                 "workspace_bytes")]
+                 "workspace_bytes")] + \
+               [(n, ctypes.c_int32) for n in ("requested_mode", "slices")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

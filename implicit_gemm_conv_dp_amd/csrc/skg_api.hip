@@ -185,7 +185,7 @@ int skg_plan_gemm(const skg_gemm_args_t* a, skg_plan_t* out) {
       rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
       if (rc) return rc;
     }
-    return make_plan(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+    return plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
   } catch (...) {
     return hip_failure("exception in skg_plan_gemm");
   }
@@ -203,7 +203,7 @@ int skg_plan_wgrad(const skg_wgrad_args_t* a, skg_plan_t* out) {
       rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
       if (rc) return rc;
     }
-    return make_plan(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+    return plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
   } catch (...) {
     return hip_failure("exception in skg_plan_wgrad");
   }
@@ -226,7 +226,7 @@ int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stre
     rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
     if (rc) return rc;
     skg_plan_t pl;
-    rc = make_plan(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    rc = plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
     if (rc) return rc;
     rc = check_run(pl, ws, ws_bytes, cus, per_cu);
     if (rc) return rc;
@@ -275,7 +275,7 @@ int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* st
     rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
     if (rc) return rc;
     skg_plan_t pl;
-    rc = make_plan(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    rc = plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
     if (rc) return rc;
     rc = check_run(pl, ws, ws_bytes, cus, per_cu);
     if (rc) return rc;

@@ -66,17 +66,95 @@ int elem_bytes(int dtype) {
   }
 }
 
-static int check_launch_knobs(int mode, int reduction, int ctas) {
-  if (mode < SKG_MODE_DP || mode > SKG_MODE_PERSISTENT) return unsupported("unknown launch mode");
+// Automatic launch choice and the split-K comparator (PR #13151, commit
+// making stream-K the "auto" default and its review follow-up): stream-K
+// for tiles that leave a ragged wave of the pool over a long reduction
+// when that partition has stream-K CTAs, split-K otherwise; "auto"
+// reduction = workspace.  Split-K runs as dp_sk with a pool of tiles x
+// slices; default slices fill the pool but stay at least kLongReduction
+// iterations long (a slice's fp32 partial tile round trip costs about as
+// many bytes as that many iterations' operand tiles).  Same steps as the
+// oracle's resolve_launch.
+constexpr int64_t kLongReduction = 8;
+
+static int resolve_launch(const GemmShape& g, int& mode, int& reduction, int& ctas, int num_cus,
+                          int resident_per_cu, int& slices) {
+  slices = 1;
+  if (reduction == SKG_RED_AUTO) reduction = SKG_RED_WORKSPACE;
   if (reduction < SKG_RED_LINEAR || reduction > SKG_RED_WORKSPACE)
     return unsupported("unknown stream-K reduction");
+  if (ctas == 0 || ctas < -1) return unsupported("streamk ctas must be -1 or positive");
+  if (g.tiles_m <= 0 || g.tiles_n <= 0 || g.iters_per_tile <= 0) return unsupported("empty problem");
+  const int64_t T = g.tiles_m * g.tiles_n, ipt = g.iters_per_tile;
+  auto pool = [&](int64_t* P) {
+    if (ctas > 0) {
+      *P = ctas;
+      return SKG_OK;
+    }
+    int32_t d = 0;
+    const int rc = skg_default_pool(reduction, num_cus, resident_per_cu, &d);
+    *P = d;
+    return rc;
+  };
+  int64_t S = 1;
+  if (mode == SKG_MODE_AUTO) {
+    int64_t P = 0;
+    int rc = pool(&P);
+    if (rc) return rc;
+    if (T % P != 0 && T < 2 * P && ipt >= kLongReduction && (T - (T / P) * P) * ipt >= P) {
+      mode = SKG_MODE_DP_SK;
+      ctas = (int)P;
+      return SKG_OK;
+    }
+    S = std::min<int64_t>(P / T, ipt / kLongReduction);  // split-K filling the same pool
+  } else if (mode == SKG_MODE_SPLITK) {
+    if (ctas == -1) {
+      int64_t P = 0;
+      int rc = pool(&P);
+      if (rc) return rc;
+      S = std::min<int64_t>(P / T, ipt / kLongReduction);
+    } else {
+      S = ctas;
+    }
+  }
+  if (mode == SKG_MODE_AUTO || mode == SKG_MODE_SPLITK) {
+    if (S > ipt) S = ipt;
+    if (S < 1) S = 1;
+    if (T * S > INT32_MAX) return unsupported("too many split-K CTAs");
+    slices = (int)S;
+    mode = S == 1 ? SKG_MODE_DP : SKG_MODE_DP_SK;
+    ctas = (int)(T * S);
+  }
+  return SKG_OK;
+}
+
+int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, int ctas,
+                int num_cus, int resident_per_cu, skg_plan_t* out) {
+  const int requested = mode;
+  int slices = 1;
+  int rc = resolve_launch(g, mode, reduction, ctas, num_cus, resident_per_cu, slices);
+  if (rc) return rc;
+  rc = make_plan(g, t, mode, reduction, ctas, num_cus, resident_per_cu, out);
+  if (rc) return rc;
+  out->requested_mode = requested;
+  out->slices = slices;
+  return SKG_OK;
+}
+
+// `requested`: the caller's knobs (AUTO / SPLITK allowed); otherwise the
+// resolved launch the planner plans.
+static int check_launch_knobs(int mode, int reduction, int ctas, bool requested) {
+  const int max_mode = requested ? SKG_MODE_AUTO : SKG_MODE_PERSISTENT;
+  const int max_red = requested ? SKG_RED_AUTO : SKG_RED_WORKSPACE;
+  if (mode < SKG_MODE_DP || mode > max_mode) return unsupported("unknown launch mode");
+  if (reduction < SKG_RED_LINEAR || reduction > max_red) return unsupported("unknown stream-K reduction");
   if (ctas == 0 || ctas < -1) return unsupported("streamk ctas must be -1 or positive");
   return SKG_OK;
 }
 
 int make_plan(const GemmShape& g, const TileDesc& t, int mode, int reduction, int ctas,
               int num_cus, int resident_per_cu, skg_plan_t* out) {
-  int rc = check_launch_knobs(mode, reduction, ctas);
+  int rc = check_launch_knobs(mode, reduction, ctas, false);
   if (rc) return rc;
   if (g.tiles_m <= 0 || g.tiles_n <= 0 || g.iters_per_tile <= 0) return unsupported("empty problem");
   skg_plan_t p;
@@ -192,7 +270,7 @@ int validate_gemm(const skg_gemm_args_t* a) {
   if (a->dtype_c != SKG_F16 && a->dtype_c != SKG_BF16 && a->dtype_c != SKG_F32)
     return unsupported("unsupported C dtype");
   if (!(t->gemm_mask & (1 << a->dtype_ab))) return unsupported("tile has no GEMM instance for this A/B dtype");
-  int rc = check_launch_knobs(a->mode, a->reduction, a->ctas);
+  int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);
   if (rc) return rc;
   if (a->reduction == SKG_RED_ATOMIC && a->dtype_c != SKG_F32)
     return unsupported("atomic reduction needs an fp32 output");
@@ -214,7 +292,7 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
   if (!t) return unsupported("unknown tile id");
   if (a->dtype != SKG_F16 && a->dtype != SKG_BF16) return unsupported("unsupported wgrad dtype");
   if (!(t->wgrad_mask & (1 << a->dtype))) return unsupported("tile has no wgrad instance for this dtype");
-  int rc = check_launch_knobs(a->mode, a->reduction, a->ctas);
+  int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);
   if (rc) return rc;
   if (a->n <= 0 || a->h <= 0 || a->w <= 0 || a->c <= 0 || a->k <= 0 || a->r <= 0 || a->s <= 0)
     return unsupported("sizes must be positive");

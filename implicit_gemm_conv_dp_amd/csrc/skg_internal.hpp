@@ -37,6 +37,9 @@ struct GemmShape {
 // resident_per_cu are only read when ctas == -1.
 int make_plan(const GemmShape& g, const TileDesc& t, int mode, int reduction,
               int ctas, int num_cus, int resident_per_cu, skg_plan_t* out);
+// make_plan after resolving SKG_MODE_AUTO / SKG_MODE_SPLITK / SKG_RED_AUTO.
+int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction,
+                int ctas, int num_cus, int resident_per_cu, skg_plan_t* out);
 
 // Argument checks that need no device (a0 of the hot path).
 int validate_gemm(const skg_gemm_args_t* a);

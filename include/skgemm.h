@@ -71,7 +71,27 @@ enum skg_dtype {
  *                       segment that only hands a partial on runs before
  *                       the data-parallel tiles, the segments it owns after
  *                       them (so their folds find the partials ready). */
-enum skg_mode { SKG_MODE_DP = 0, SKG_MODE_DP_SK = 1, SKG_MODE_PERSISTENT = 2 };
+enum skg_mode {
+  SKG_MODE_DP = 0,
+  SKG_MODE_DP_SK = 1,
+  SKG_MODE_PERSISTENT = 2,
+  /* SKG_MODE_SPLITK  comparator: every tile is cut into `ctas` equal K
+   *                  slices (clamped to [1, iterations per tile]; ctas =
+   *                  -1: as many as fill the default pool while every slice
+   *                  keeps >= 8 MAC iterations), one CTA per slice; runs as
+   *                  dp_sk with a pool of tiles x slices.  1 slice is plain
+   *                  data-parallel. */
+  SKG_MODE_SPLITK = 3,
+  /* SKG_MODE_AUTO    the choice of the "auto" default of PR #13151 (commit
+   *                  making stream-K the auto default, and its review
+   *                  follow-up): dp_sk when the tiles leave a ragged wave
+   *                  of the pool (tiles mod pool != 0, tiles < 2 x pool)
+   *                  over a long reduction (>= 8 MAC iterations per tile)
+   *                  and that partition has stream-K CTAs; split-K with
+   *                  the default slice count otherwise.  skg_plan_* report
+   *                  the launch it resolved to. */
+  SKG_MODE_AUTO = 4
+};
 
 /* Fix-up of tiles shared by several stream-K CTAs (PR #13151, same section).
  *   LINEAR     deterministic: the owner folds the contributors in CTA order;
@@ -84,7 +104,9 @@ enum skg_reduction {
   SKG_RED_LINEAR = 0,
   SKG_RED_TREE = 1,
   SKG_RED_ATOMIC = 2,
-  SKG_RED_WORKSPACE = 3
+  SKG_RED_WORKSPACE = 3,
+  SKG_RED_AUTO = 4  /* resolves to WORKSPACE: it never waits, so it takes the
+                       occupancy-sized pool (same commit as SKG_MODE_AUTO) */
 };
 
 /* Compiled tile instances.  TM x TN x TK in elements; each instance exists
@@ -132,7 +154,8 @@ typedef struct skg_gemm_args {
   int32_t tile_id;         /* enum skg_tile */
   int32_t mode;            /* enum skg_mode */
   int32_t reduction;       /* enum skg_reduction */
-  int32_t ctas;            /* stream-K pool; -1 = default pool; 0 or < -1 rejected */
+  int32_t ctas;            /* stream-K pool (split-K: slices per tile); -1 = default;
+                              0 or < -1 rejected */
 } skg_gemm_args_t;
 
 /* wgrad problem (PR #13151, Motivation and Technical Details).  X is the
@@ -172,6 +195,8 @@ typedef struct skg_plan {
   int64_t flags_bytes;       /* 4 * sk_ctas * n_waves rounded up to 256 (linear/tree) */
   int64_t partials_bytes;    /* sk_ctas * TM * TN * 4 (linear/tree) */
   int64_t workspace_bytes;   /* bytes the caller must pass as ws */
+  int32_t requested_mode;    /* the mode asked for; `mode` is what runs */
+  int32_t slices;            /* split-K slices per tile (1 unless split-K) */
 } skg_plan_t;
 
 /* Reason for the last non-zero status on this thread ("" if none).  The

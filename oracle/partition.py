@@ -253,3 +253,72 @@ def check_plan(p):
     if p.sk_ctas and p.max_contrib > ceil_div(ipt, p.iters_per_sk_cta) + 1:
         bad.append("contributor bound exceeded")
     return bad
+
+
+# ---------------------------------------------------------------------------
+# Automatic launch choice and the split-K comparator (rocm-libraries PR
+# #13151: the commit that made stream-K the "auto" default -- stream-K where
+# a candidate has few output tiles over a long reduction, the grid-per-tile
+# split-K kernel everywhere else, and "auto" for the reduction resolving to
+# the workspace fix-up because it never waits and so gets the
+# occupancy-sized pool -- and the review follow-up that builds the partition
+# the launch will really use and keeps split-K when it has no stream-K
+# CTAs).  The pages print no thresholds ("coarse on purpose"); readings:
+#
+# * few tiles: the tiles leave a ragged data-parallel wave (T mod P != 0)
+#   and are fewer than two full waves (T < 2P), so that wave is a large
+#   part of the run;
+# * long reduction: at least LONG_REDUCTION MAC iterations per tile;
+# * split-K cuts every tile into S equal K slices; the default S fills the
+#   pool (pool // tiles) but keeps every slice at least LONG_REDUCTION
+#   iterations long, since a slice's fp32 partial tile costs a write and a
+#   read of about as many bytes as that many iterations' operand tiles; an
+#   explicit S is clamped to [1, iters_per_tile] only; S = 1 is plain
+#   data-parallel.  It runs on the stream-K engine as dp_sk with a pool of
+#   tiles * S CTAs, whose partition has dp_tiles = 0 and gives every CTA
+#   one slice (ranges straddle two tiles' slices when S does not divide
+#   iters_per_tile).
+
+LONG_REDUCTION = 8
+
+
+def resolve_launch(tiles, iters_per_tile, mode, reduction, ctas, num_cus=None,
+                   resident_per_cu=None):
+    """Resolve ``mode in {dp, dp_sk, persistent, splitk, auto}`` and
+    ``reduction in {linear, tree, atomic, workspace, auto}`` to the launch
+    the planner plans.  Returns ``(mode, reduction, ctas, slices)`` with mode
+    one of dp / dp_sk / persistent; ``slices`` is the split-K slice count
+    (1 when not split-K)."""
+    if reduction == "auto":
+        reduction = "workspace"
+    if reduction not in REDUCTIONS:
+        raise ValueError("unknown reduction")
+    if ctas == 0 or ctas < -1:
+        raise ValueError("streamk ctas must be -1 or positive")
+    T, ipt = tiles, iters_per_tile
+
+    def pool():
+        if ctas > 0:
+            return ctas
+        if num_cus is None or resident_per_cu is None:
+            raise ValueError("default pool needs the device's CU count")
+        return default_pool(reduction, num_cus, resident_per_cu)
+
+    if mode == "auto":
+        P = pool()
+        if T % P != 0 and T < 2 * P and ipt >= LONG_REDUCTION:
+            # The stream-K partition at this pool has stream-K CTAs unless
+            # the remainder tiles hold fewer iterations than the pool.
+            if (T - (T // P) * P) * ipt >= P:
+                return "dp_sk", reduction, P, 1
+        S = min(P // T, ipt // LONG_REDUCTION)  # split-K filling the same pool
+    elif mode == "splitk":
+        S = min(pool() // T, ipt // LONG_REDUCTION) if ctas == -1 else ctas
+    if mode in ("auto", "splitk"):
+        S = max(1, min(S, ipt))
+        if S == 1:
+            return "dp", reduction, T, 1
+        return "dp_sk", reduction, T * S, S
+    if mode not in MODES:
+        raise ValueError("unknown mode")
+    return mode, reduction, ctas, 1

@@ -183,3 +183,51 @@ def test_workload_full_size(index):
             else:
                 err = sampled_check(Y, wl, inp)
                 assert err <= TOL[wl.dtype_ab], "%s %s %s: %.3e" % (wl.name, mode, red, err)
+
+
+SEL_TILE_DT = [("128x128x32", "f16"), ("256x256x64", "bf16"), ("256x256x128", "e4m3")]
+
+
+@pytest.mark.parametrize("tile,fmt", SEL_TILE_DT)
+def test_split_k_and_auto_integer_exact(tile, fmt):
+    # 3 x 2 tiles of 25 MAC iterations: split-K slices that divide the
+    # reduction and ones that straddle, every fix-up; "auto" on explicit and
+    # default pools (stream-K here: a ragged wave over a long reduction).
+    M, N, K = shape_for(tile, True)
+    A = synth.integer_codes(fmt, M * K, 41, 0.15)
+    B = synth.integer_codes(fmt, N * K, 42, 0.15)
+    sa, sb = synth.pow2_scales(M, 43), synth.pow2_scales(N, 44)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
+    fmt_c = "f32"
+    cases = [("splitk", "workspace", 5, 5), ("splitk", "tree", 3, 3), ("splitk", "linear", 2, 2),
+             ("splitk", "atomic", 25, 25), ("splitk", "workspace", 40, 25),
+             ("splitk", "tree", 1, 1), ("auto", "auto", 7, 1), ("auto", "tree", 64, 1),
+             ("auto", "auto", -1, None)]
+    for mode, red, ctas, slices in cases:
+        Y, plan = run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa, sb)
+        label = "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas)
+        assert np.array_equal(Y, R), label + ": not bit-exact (max diff %g)" % np.nanmax(np.abs(Y - R))
+        assert plan["requested_mode"] == skg.MODES[mode], label
+        if slices is not None:
+            assert plan["slices"] == slices, (label, plan["slices"])
+        if mode == "auto" and ctas != -1:
+            assert plan["mode"] == skg.MODES["dp_sk"] and plan["sk_ctas"] > 0, label
+
+
+@pytest.mark.parametrize("tile,fmt", SEL_TILE_DT)
+def test_auto_splits_one_short_tile(tile, fmt):
+    # One tile whose iterations are fewer than the pool: the stream-K
+    # partition would have no stream-K CTAs, so "auto" runs split-K with
+    # slices of at least eight iterations (40 iterations over a 64-CTA pool:
+    # 5 slices).
+    tm, tn, tk = map(int, tile.split("x"))
+    M, N, K = tm - 3, tn - 8, 40 * tk
+    g = synth.rng(51)
+    dist = "normal" if fmt == "e4m3" else "uniform"
+    A = synth.to_codes(synth.draw(dist, M * K, 52), fmt)
+    B = synth.to_codes(synth.draw(dist, N * K, 53), fmt)
+    R = oracle_gemm(fmt, A, B, M, N, K)
+    Y, plan = run(A, B, M, N, K, fmt, "bf16", tile, "auto", "auto", 64)
+    assert plan["slices"] == 5 and plan["sk_ctas"] == 5 and plan["dp_tiles"] == 0
+    assert plan["reduction"] == skg.REDUCTIONS["workspace"]
+    assert_close(Y, R, fmt, "%s auto one short tile" % tile)

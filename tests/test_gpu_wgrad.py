@@ -97,3 +97,36 @@ def test_workload_full_size(index):
         for red in wl.reductions:
             Y, plan = run(inp["x"], inp["dy"], shape, wl.dtype, wl.tile, mode, red, wl.ctas)
             assert_close(Y, R, wl.dtype, "%s %s %s" % (wl.name, mode, red))
+
+
+@pytest.mark.parametrize("tile", ["32x64x64", "128x128x64", "256x256x64"])
+@pytest.mark.parametrize("name", ["dense", "grouped"])
+def test_split_k_and_auto_integer_exact(name, tile):
+    shape = SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 61)
+    for mode, red, ctas in [("splitk", "workspace", 2), ("splitk", "tree", 3),
+                            ("splitk", "linear", 7), ("splitk", "atomic", 4),
+                            ("auto", "auto", 5), ("auto", "linear", 9), ("auto", "auto", -1),
+                            ("splitk", "auto", -1)]:
+        Y, plan = run(x, dy, shape, "bf16", tile, mode, red, ctas)
+        assert np.array_equal(Y, R), "%s %s %s %s ctas=%d not bit-exact" % (name, tile, mode, red,
+                                                                             ctas)
+        assert plan["requested_mode"] == skg.MODES[mode]
+
+
+@pytest.mark.parametrize("mode", ["auto", "splitk"])
+def test_workload_auto_and_split_k_full_size(mode):
+    # The dense wgrad workload on the default pool: "auto" resolves to
+    # stream-K with the workspace fix-up, split-K to equal K slices.
+    wl = synth.WORKLOADS[3]
+    inp = wl.inputs()
+    shape = (wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s, wl.stride, wl.pad, wl.groups)
+    R = oracle_wgrad(wl.dtype, inp["x"], inp["dy"], wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s,
+                     wl.stride[0], wl.stride[1], wl.pad[0], wl.pad[1], wl.groups).reshape(wl.k, -1)
+    Y, plan = run(inp["x"], inp["dy"], shape, wl.dtype, wl.tile, mode, "auto", -1)
+    if mode == "auto":
+        assert plan["mode"] == skg.MODES["dp_sk"] and plan["sk_ctas"] > 0 and plan["slices"] == 1
+    else:
+        assert plan["slices"] > 1 and plan["dp_tiles"] == 0
+    assert plan["reduction"] == skg.REDUCTIONS["workspace"]
+    assert_close(Y, R, wl.dtype, "%s %s" % (wl.name, mode))
