@@ -1103,6 +1103,8 @@ struct Engine {
   //   OUT_ATOMIC:    fp32 atomic add of (v * sa[row]) * sb[col] into C;
   //   OUT_WORKSPACE: fp32 atomic add of v into the tile's scratch wsp;
   //   OUT_PUBLISH:   stores v as this CTA's partial.
+  // (Full tiles take the two atomic forms through atomic_full, one column
+  // per lane.)
   // A wave reads and writes partials only in the rows its threads own (the
   // same rows in every CTA), so one flag per (CTA, wave) orders each
   // hand-off: the producer's wave w releases its flag after its last partial
@@ -1142,7 +1144,7 @@ struct Engine {
     static_assert(NR % CH == 0, "fold chunks");
     for (int k = 0; k < fx.nfold; ++k) {
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
-#pragma unroll 1
+#pragma unroll 2
       for (int i0 = 0; i0 < NR; i0 += CH) {
         f32x4 t[CH][2];
 #pragma unroll
@@ -1169,23 +1171,11 @@ struct Engine {
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
       store_dev16(q, tofs * 4, r.v0);
       store_dev16(q, tofs * 4 + 16, r.v1);
-    } else if constexpr (HOW == OUT_WORKSPACE) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        unsafeAtomicAdd(wsp + tofs + e, r.v0[e]);
-        unsafeAtomicAdd(wsp + tofs + 4 + e, r.v1[e]);
-      }
     } else {
+      static_assert(HOW == OUT_STORE, "atomic fix-ups copy out through atomic_full");
       const f32x4 w0 = (r.v0 * sa) * sb0, w1 = (r.v1 * sa) * sb1;
       const size_t idx = (size_t)row * o.ld + col;
-      if constexpr (HOW == OUT_ATOMIC) {
-        float* dst = (float*)o.base + idx;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          unsafeAtomicAdd(dst + e, w0[e]);
-          unsafeAtomicAdd(dst + 4 + e, w1[e]);
-        }
-      } else if constexpr (DTC == DT_F32) {
+      if constexpr (DTC == DT_F32) {
         f32x4* dst = (f32x4*)((float*)o.base + idx);
         dst[0] = w0;
         dst[1] = w1;
@@ -1221,6 +1211,34 @@ struct Engine {
       add_partials(r, fx, tofs);
       const float sa = (HOW == OUT_STORE || HOW == OUT_ATOMIC) && o.sa ? o.sa[row] : 1.f;
       emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sa, sb0, sb1);
+    }
+  }
+
+  // Atomic copy-out of one pass of a full tile (atomic and workspace
+  // fix-ups, partners already folded): consecutive lanes take consecutive
+  // columns, so each wave-instruction adds into one contiguous 256-byte run
+  // of the row instead of 4-byte pieces 32 bytes apart.
+  template <int HOW>
+  SKG_DEV void atomic_full(const OutTile& o, float* wsp, int pass) const {
+    static_assert(Cfg::THREADS % Cfg::TN == 0 || Cfg::TN % Cfg::THREADS == 0, "atomic mapping");
+    constexpr int TPR = Cfg::TN < Cfg::THREADS ? Cfg::TN : Cfg::THREADS;  // threads per row
+    constexpr int RPS = Cfg::THREADS / TPR;                                 // rows per step
+    const int c0 = tid % TPR, lr0 = tid / TPR;
+#pragma unroll
+    for (int cc = 0; cc < Cfg::TN; cc += TPR) {
+      const int c = c0 + cc;
+      const float sb = HOW == OUT_ATOMIC && o.sb ? o.sb[c] : 1.f;
+#pragma unroll 2
+      for (int lr = lr0; lr < Cfg::WTM; lr += RPS) {
+        const int row = pass * Cfg::WTM + lr;
+        const float v = *(const SKG_LDS float*)(lds + lr * Cfg::EPI_PITCH32 + c * 4);
+        if constexpr (HOW == OUT_WORKSPACE) {
+          unsafeAtomicAdd(wsp + row * Cfg::TN + c, v);
+        } else {
+          const float sa = o.sa ? o.sa[row] : 1.f;
+          unsafeAtomicAdd((float*)o.base + (size_t)row * o.ld + c, (v * sa) * sb);
+        }
+      }
     }
   }
 
@@ -1321,9 +1339,9 @@ struct Engine {
       } else if (fx.how == OUT_PUBLISH) {
         copy_full<OUT_PUBLISH, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (fx.how == OUT_WORKSPACE) {
-        copy_full<OUT_WORKSPACE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
+        atomic_full<OUT_WORKSPACE>(o, wsp, pass);
       } else if (fx.how == OUT_ATOMIC) {
-        copy_full<OUT_ATOMIC, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
+        atomic_full<OUT_ATOMIC>(o, wsp, pass);
       } else if (dt == DT_F32) {
         copy_full<OUT_STORE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (dt == DT_F16) {
