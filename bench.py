@@ -14,6 +14,7 @@ the CPU oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -24,7 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # Dense MFMA peaks of MI355X (TFLOP/s) and its HBM3E bandwidth (GB/s).
-MFMA_PEAK = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
+MFMA_PEAK = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
 HBM_PEAK_GBS = 8000.0
 METRIC = "TFLOP/s and % of MFMA peak, stream-K GEMM and conv wgrad on 1 MI355X"
 
@@ -39,6 +40,10 @@ def parse():
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--ctas", type=int, default=None)
     ap.add_argument("--tile", default=None)
+    ap.add_argument("--dtype", default=None, choices=["e4m3", "e5m2"],
+                    help="fp8 operand format of the fp8 GEMM workload (default e4m3)")
+    ap.add_argument("--scale-mode", default=None, choices=["rowcol", "tensor"],
+                    help="scales of the fp8 GEMM workload (default rowcol)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample (0 disables it)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -97,7 +102,7 @@ def alg_bytes(wl):
     if wl.op == "gemm":
         eab = 1 if wl.dtype_ab == "e4m3" else 2
         ec = 4 if wl.dtype_c == "f32" else 2
-        extra = 4 * (wl.M + wl.N) if wl.scales else 0
+        extra = (4 * (wl.M + wl.N) if wl.scale_mode == "rowcol" else 8) if wl.scales else 0
         return eab * (wl.M * wl.K + wl.N * wl.K) + ec * wl.M * wl.N + extra
     ho, wo = wl.out_hw
     return 2 * (wl.n * wl.h * wl.w * wl.c + wl.n * ho * wo * wl.k) + \
@@ -116,8 +121,9 @@ def cpu_baseline(wl, inp, target_s):
         if wl.op == "gemm":
             rows = frac_units
             oracle_gemm(wl.dtype_ab, inp["A"][:rows * wl.K], inp["B"], rows, wl.N, wl.K,
-                        scale_a=None if "scale_a" not in inp else inp["scale_a"][:rows],
-                        scale_b=inp.get("scale_b"))
+                        scale_a=None if "scale_a" not in inp else
+                        (inp["scale_a"][:rows] if wl.scale_mode == "rowcol" else inp["scale_a"]),
+                        scale_b=inp.get("scale_b"), scale_mode=wl.scale_mode)
             flops = 2.0 * rows * wl.N * wl.K
         else:
             imgs = frac_units
@@ -179,6 +185,12 @@ def main():
     from implicit_gemm_conv_dp_amd import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.dtype or args.scale_mode:
+        if wl.op != "gemm" or not wl.scales:
+            sys.exit("--dtype / --scale-mode apply to the fp8 GEMM workload only")
+        dt, sm = args.dtype or wl.dtype_ab, args.scale_mode or wl.scale_mode
+        wl = dataclasses.replace(wl, dtype_ab=dt, scale_mode=sm, name="gemm_%s_%dx%dx%d_%s_scales" % (
+            dt, wl.M, wl.N, wl.K, "rowcol" if sm == "rowcol" else "per_tensor"))
     mode = args.mode or wl.modes[0]
     red = args.reduction or wl.reductions[0]
     ctas = args.ctas if args.ctas is not None else wl.ctas
@@ -199,7 +211,7 @@ def main():
         out = torch.empty(wl.M * wl.N, dtype=torch.float32 if wl.dtype_c == "f32" else torch.int16,
                           device=dev)
         kw = dict(M=wl.M, N=wl.N, K=wl.K, dtype_ab=wl.dtype_ab, dtype_c=wl.dtype_c, tile=tile,
-                  mode=mode, reduction=red, ctas=ctas)
+                  mode=mode, reduction=red, ctas=ctas, scale_mode=wl.scale_mode)
         plan = skg.plan_gemm(**kw)
         ws = skg.workspace_for(plan, dev)
 

@@ -17,10 +17,10 @@ element type is ``dtype_ab`` / ``dtype_c``.  ``wgrad`` takes NHWC ``x`` and
 from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
                    skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
-                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES)
+                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES)
 
 __all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
-           "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES",
+           "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES", "SCALE_MODES",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
            "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events"]
 
@@ -39,7 +39,8 @@ def _ptr(t):
 
 
 def gemm_args(A=None, B=None, C=None, *, M, N, K, dtype_ab, dtype_c, lda=None, ldb=None,
-              ldc=None, scale_a=None, scale_b=None, tile, mode, reduction, ctas):
+              ldc=None, scale_a=None, scale_b=None, scale_mode="rowcol", tile, mode, reduction,
+              ctas):
     a = _lib.skg_gemm_args_t()
     a.M, a.N, a.K = M, N, K
     a.dtype_ab = _enum(DTYPES, dtype_ab, "dtype")
@@ -53,6 +54,7 @@ def gemm_args(A=None, B=None, C=None, *, M, N, K, dtype_ab, dtype_c, lda=None, l
     a.mode = _enum(MODES, mode, "mode")
     a.reduction = _enum(REDUCTIONS, reduction, "reduction")
     a.ctas = ctas
+    a.scale_mode = _enum(SCALE_MODES, scale_mode, "scale mode")
     return a
 
 

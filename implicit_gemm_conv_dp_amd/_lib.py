@@ -11,7 +11,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libskgemm.so")
 
 SKG_OK, SKG_ERR_HIP, SKG_ERR_UNSUPPORTED = 0, -1, -2
-F16, BF16, F8E4M3, F32 = 0, 1, 2, 3
+F16, BF16, F8E4M3, F32, F8E5M2 = 0, 1, 2, 3, 4
+SCALE_ROWCOL, SCALE_TENSOR = 0, 1
 MODE_DP, MODE_DP_SK, MODE_PERSISTENT, MODE_SPLITK, MODE_AUTO = 0, 1, 2, 3, 4
 RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO = 0, 1, 2, 3, 4
 OP_GEMM, OP_WGRAD = 0, 1
@@ -23,7 +24,8 @@ MODES = {"dp": MODE_DP, "dp_sk": MODE_DP_SK, "persistent": MODE_PERSISTENT,
          "splitk": MODE_SPLITK, "auto": MODE_AUTO}
 REDUCTIONS = {"linear": RED_LINEAR, "tree": RED_TREE, "atomic": RED_ATOMIC,
               "workspace": RED_WORKSPACE, "auto": RED_AUTO}
-DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32}
+DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32, "e5m2": F8E5M2}
+SCALE_MODES = {"rowcol": SCALE_ROWCOL, "tensor": SCALE_TENSOR}
 TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
          "256x256x128": TILE_256x256x128, "32x64x64": TILE_32x64x64,
          "128x128x64": TILE_128x128x64, "256x128x64": TILE_256x128x64}
@@ -43,7 +45,8 @@ class skg_gemm_args_t(ctypes.Structure):
                 ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
                 ("scale_a", ctypes.c_void_p), ("scale_b", ctypes.c_void_p),
                 ("tile_id", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("reduction", ctypes.c_int32), ("ctas", ctypes.c_int32)]
+                ("reduction", ctypes.c_int32), ("ctas", ctypes.c_int32),
+                ("scale_mode", ctypes.c_int32)]
 
 
 class skg_wgrad_args_t(ctypes.Structure):

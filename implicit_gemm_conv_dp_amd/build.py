@@ -28,7 +28,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
-SOURCES = ["skg_host.cpp", "skg_api.hip", "skg_inst_gemm.hip", "skg_inst_wgrad.hip"]
+SOURCES = ["skg_host.cpp", "skg_api.hip", "skg_inst_gemm.hip", "skg_inst_gemm_f16.hip",
+           "skg_inst_gemm_bf16.hip", "skg_inst_gemm_f8.hip", "skg_inst_wgrad.hip"]
 
 
 def _compile(src):

@@ -21,7 +21,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-enum { DT_F16 = 0, DT_BF16 = 1, DT_F8 = 2, DT_F32 = 3 };
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F8 = 2, DT_F32 = 3, DT_BF8 = 4 };
 enum { MODE_DP = 0, MODE_DP_SK = 1, MODE_PERSISTENT = 2 };
 enum { RED_LINEAR = 0, RED_TREE = 1, RED_ATOMIC = 2, RED_WORKSPACE = 3 };
 
@@ -176,29 +176,38 @@ struct Mfma<DT_BF16, 16> {
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
-// fp8 (OCP E4M3 on gfx950): the f8f6f4 family with K = 64 (32x32) or 128
-// (16x16) per instruction; format code 0 selects E4M3 for both operands.
-// Zero scale operands select the unscaled instruction (no block scales, and
-// it keeps its accumulator in AGPRs); the row and column scales are applied
-// in the epilogue instead.
-template <>
-struct Mfma<DT_F8, 32> {
+// fp8 (OCP E4M3, DT_F8) and bf8 (OCP E5M2, DT_BF8) on gfx950: the f8f6f4
+// family with K = 64 (32x32) or 128 (16x16) per instruction; format code 0
+// selects E4M3, 1 selects E5M2, the same for both operands.  Zero scale
+// operands select the unscaled instruction (no block scales, and it keeps its
+// accumulator in AGPRs); the row and column scales are applied in the
+// epilogue instead.
+template <int FMT>
+struct MfmaF8x32 {
   static constexpr int OPB = 32, KB = 64, NACC = 16;
   typedef f32x16 acc_t;
   typedef i32x8 frag_t;
   SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
-    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
   }
 };
-template <>
-struct Mfma<DT_F8, 16> {
+template <int FMT>
+struct MfmaF8x16 {
   static constexpr int OPB = 32, KB = 128, NACC = 4;
   typedef f32x4 acc_t;
   typedef i32x8 frag_t;
   SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
-    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
   }
 };
+template <>
+struct Mfma<DT_F8, 32> : MfmaF8x32<0> {};
+template <>
+struct Mfma<DT_F8, 16> : MfmaF8x16<0> {};
+template <>
+struct Mfma<DT_BF8, 32> : MfmaF8x32<1> {};
+template <>
+struct Mfma<DT_BF8, 16> : MfmaF8x16<1> {};
 
 // One operand fragment from two 16-byte LDS reads (OPB = 32) or one.
 template <class FragT>

@@ -20,7 +20,7 @@ thread_local std::string g_last_error;
 
 constexpr int M_F16 = 1 << SKG_F16;
 constexpr int M_BF16 = 1 << SKG_BF16;
-constexpr int M_F8 = 1 << SKG_F8E4M3;
+constexpr int M_F8 = 1 << SKG_F8E4M3 | 1 << SKG_F8E5M2;
 
 // Must agree with the kernel instances compiled in skg_api.hip.
 const TileDesc kTiles[SKG_TILE_COUNT] = {
@@ -58,6 +58,7 @@ int elem_bytes(int dtype) {
     case SKG_BF16:
       return 2;
     case SKG_F8E4M3:
+    case SKG_F8E5M2:
       return 1;
     case SKG_F32:
       return 4;
@@ -265,8 +266,11 @@ int validate_gemm(const skg_gemm_args_t* a) {
   if (!a) return unsupported("null arguments");
   const TileDesc* t = tile_desc(a->tile_id);
   if (!t) return unsupported("unknown tile id");
-  if (a->dtype_ab != SKG_F16 && a->dtype_ab != SKG_BF16 && a->dtype_ab != SKG_F8E4M3)
+  if (a->dtype_ab != SKG_F16 && a->dtype_ab != SKG_BF16 && a->dtype_ab != SKG_F8E4M3 &&
+      a->dtype_ab != SKG_F8E5M2)
     return unsupported("unsupported A/B dtype");
+  if (a->scale_mode != SKG_SCALE_ROWCOL && a->scale_mode != SKG_SCALE_TENSOR)
+    return unsupported("unknown scale mode");
   if (a->dtype_c != SKG_F16 && a->dtype_c != SKG_BF16 && a->dtype_c != SKG_F32)
     return unsupported("unsupported C dtype");
   if (!(t->gemm_mask & (1 << a->dtype_ab))) return unsupported("tile has no GEMM instance for this A/B dtype");

@@ -39,7 +39,9 @@ struct Scratch {
 };
 
 // Where an output tile lands: a row-major window with valid extent
-// rows x cols, optional per-row / per-column scales.
+// rows x cols, optional per-row / per-column scales (the problem's
+// kScaleInc is 1), or one scale for every row and one for every column
+// (kScaleInc is 0: per-tensor).
 struct OutTile {
   char* base;
   const float* sa;
@@ -74,7 +76,7 @@ struct WgradParams {
 template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64>
 struct TileCfg {
   static constexpr int DT = DT_, TM = TM_, TN = TN_, TK = TK_, WM = WM_, WN = WN_, MN = MN_;
-  static constexpr int ESZ = DT == DT_F8 ? 1 : 2;
+  static constexpr int ESZ = DT == DT_F8 || DT == DT_BF8 ? 1 : 2;
   static constexpr int RB = TK * ESZ;  // LDS row bytes (K contiguous)
   static constexpr int CPR = RB / 16;  // 16-byte chunks per row
   static constexpr int NW = WM * WN, THREADS = 64 * NW;
@@ -420,9 +422,12 @@ struct WgradLoader {
 
 // ---------------------------------------------------------------------------
 // Problem policies: tile coordinates, loader set-up and the output window.
-template <class Cfg>
+// TENSOR: one scale for all of A and one for all of B instead of per-row /
+// per-column scales.
+template <class Cfg, bool TENSOR = false>
 struct GemmProblem {
   typedef GemmParams Params;
+  static constexpr int kScaleInc = TENSOR ? 0 : 1;
   typedef typename std::conditional<Cfg::GROUPED, GemmGrpLoader<Cfg>, GemmDmaLoader<Cfg>>::type Loader;
 
   SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
@@ -438,8 +443,8 @@ struct GemmProblem {
     const int esz = g.dtype_c == DT_F32 ? 4 : 2;
     OutTile o;
     o.base = g.C + ((size_t)m0 * g.ldc + n0) * esz;
-    o.sa = g.sa ? g.sa + m0 : nullptr;
-    o.sb = g.sb ? g.sb + n0 : nullptr;
+    o.sa = g.sa ? g.sa + m0 * kScaleInc : nullptr;
+    o.sb = g.sb ? g.sb + n0 * kScaleInc : nullptr;
     o.ld = g.ldc;
     o.rows = g.M - m0;
     o.cols = g.N - n0;
@@ -594,6 +599,7 @@ struct WgradGrpLoader {
 
 template <class Cfg>
 struct WgradProblem {
+  static constexpr int kScaleInc = 1;  // no scales
   typedef WgradParams Params;
   typedef typename std::conditional<Cfg::GROUPED, WgradGrpLoader<Cfg>, WgradLoader<Cfg>>::type Loader;
 
@@ -626,7 +632,14 @@ struct WgradProblem {
 };
 
 // ---------------------------------------------------------------------------
-template <class Cfg, class Prob>
+// Fix-up families: each kernel instance carries the code of one, so the
+// epilogue of the other does not take part in its register allocation.
+//   FIX_HANDOFF: linear and tree (partials handed on through flags);
+//   FIX_ATOMIC:  atomic and workspace (fp32 atomics, nothing waits).
+// Data-parallel-only launches use FIX_HANDOFF.
+enum { FIX_HANDOFF = 0, FIX_ATOMIC = 1 };
+
+template <class Cfg, class Prob, int FIX>
 struct Engine {
   typedef typename Cfg::acc_t acc_t;
   typedef typename Prob::Params Params;
@@ -1144,7 +1157,7 @@ struct Engine {
     static_assert(NR % CH == 0, "fold chunks");
     for (int k = 0; k < fx.nfold; ++k) {
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
-#pragma unroll 2
+#pragma unroll 1
       for (int i0 = 0; i0 < NR; i0 += CH) {
         f32x4 t[CH][2];
 #pragma unroll
@@ -1208,8 +1221,8 @@ struct Engine {
       const int lr = lr0 + i * RSTEP, row = pass * Cfg::WTM + lr;
       Row r = staged(lr, col);
       const int tofs = row * Cfg::TN + col;
-      add_partials(r, fx, tofs);
-      const float sa = (HOW == OUT_STORE || HOW == OUT_ATOMIC) && o.sa ? o.sa[row] : 1.f;
+      if constexpr (FIX == FIX_HANDOFF) add_partials(r, fx, tofs);
+      const float sa = HOW == OUT_STORE && o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
       emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sa, sb0, sb1);
     }
   }
@@ -1227,15 +1240,15 @@ struct Engine {
 #pragma unroll
     for (int cc = 0; cc < Cfg::TN; cc += TPR) {
       const int c = c0 + cc;
-      const float sb = HOW == OUT_ATOMIC && o.sb ? o.sb[c] : 1.f;
-#pragma unroll 2
+      const float sb = HOW == OUT_ATOMIC && o.sb ? o.sb[c * Prob::kScaleInc] : 1.f;
+#pragma unroll 1
       for (int lr = lr0; lr < Cfg::WTM; lr += RPS) {
         const int row = pass * Cfg::WTM + lr;
         const float v = *(const SKG_LDS float*)(lds + lr * Cfg::EPI_PITCH32 + c * 4);
         if constexpr (HOW == OUT_WORKSPACE) {
           unsafeAtomicAdd(wsp + row * Cfg::TN + c, v);
         } else {
-          const float sa = o.sa ? o.sa[row] : 1.f;
+          const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
           unsafeAtomicAdd((float*)o.base + (size_t)row * o.ld + c, (v * sa) * sb);
         }
       }
@@ -1254,27 +1267,30 @@ struct Engine {
       if (row >= o.rows) break;
       Row r = staged(lr, col);
       const int tofs = row * Cfg::TN + col;
-      add_partials(r, fx, tofs);
+      if constexpr (FIX == FIX_HANDOFF) add_partials(r, fx, tofs);
       float v[VC];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] = r.v0[e];
         v[4 + e] = r.v1[e];
       }
-      if (fx.how == OUT_PUBLISH) {
-        const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
-        for (int e = 0; e < ncol; ++e) store_dev4(q, (tofs + e) * 4, v[e]);
-        continue;
+      if constexpr (FIX == FIX_HANDOFF) {
+        if (fx.how == OUT_PUBLISH) {
+          const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
+          for (int e = 0; e < ncol; ++e) store_dev4(q, (tofs + e) * 4, v[e]);
+          continue;
+        }
+      } else {
+        if (fx.how == OUT_WORKSPACE) {
+          for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
+          continue;
+        }
       }
-      if (fx.how == OUT_WORKSPACE) {
-        for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
-        continue;
-      }
-      const float sa = o.sa ? o.sa[row] : 1.f;
+      const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
       const size_t idx = (size_t)row * o.ld + col;
       for (int e = 0; e < ncol; ++e) {
         const float w = (v[e] * sa) * (e < 4 ? sb0[e] : sb1[e - 4]);
-        if (fx.how == OUT_ATOMIC)
+        if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC)
           unsafeAtomicAdd((float*)o.base + idx + e, w);
         else if (dt == DT_F32)
           ((float*)o.base)[idx + e] = w;
@@ -1294,7 +1310,11 @@ struct Engine {
     const bool full = o.rows >= Cfg::TM && o.cols >= Cfg::TN;  // CTA-uniform
     const bool scaled = fx.how == OUT_STORE || fx.how == OUT_ATOMIC;
     f32x4 sb0 = {1.f, 1.f, 1.f, 1.f}, sb1 = sb0;
-    if (scaled && o.sb) {
+    if (Prob::kScaleInc == 0 && scaled && o.sb) {
+      const float t = o.sb[0];
+      sb0 = f32x4{t, t, t, t};
+      sb1 = sb0;
+    } else if (scaled && o.sb) {
       if (col + VC <= o.cols) {
         sb0 = *(const f32x4*)(o.sb + col);
         sb1 = *(const f32x4*)(o.sb + col + 4);
@@ -1305,7 +1325,8 @@ struct Engine {
         }
       }
     }
-    for (int k = 0; k < fx.nfold; ++k) flag_wait(s.flags + fx.partner(k) * Cfg::NW + wave);
+    if constexpr (FIX == FIX_HANDOFF)
+      for (int k = 0; k < fx.nfold; ++k) flag_wait(s.flags + fx.partner(k) * Cfg::NW + wave);
     const int dt = Prob::dtype_c(prm);
 #pragma unroll
     for (int pass = 0; pass < Cfg::WM; ++pass) {
@@ -1330,17 +1351,19 @@ struct Engine {
       }
       __syncthreads();
       Fix fo = fx;  // what the copy itself still has to fold
-      if (full && fx.nfold > 0) {
-        fold_staged(fx, pass, col);
-        fo.nfold = 0;
+      if constexpr (FIX == FIX_HANDOFF) {
+        if (full && fx.nfold > 0) {
+          fold_staged(fx, pass, col);
+          fo.nfold = 0;
+        }
       }
       if (!full) {
         copy_ragged(o, fx, wsp, pass, col, sb0, sb1);
-      } else if (fx.how == OUT_PUBLISH) {
+      } else if (FIX == FIX_HANDOFF && fx.how == OUT_PUBLISH) {
         copy_full<OUT_PUBLISH, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
-      } else if (fx.how == OUT_WORKSPACE) {
+      } else if (FIX == FIX_ATOMIC && fx.how == OUT_WORKSPACE) {
         atomic_full<OUT_WORKSPACE>(o, wsp, pass);
-      } else if (fx.how == OUT_ATOMIC) {
+      } else if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC) {
         atomic_full<OUT_ATOMIC>(o, wsp, pass);
       } else if (dt == DT_F32) {
         copy_full<OUT_STORE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
@@ -1351,7 +1374,8 @@ struct Engine {
       }
       __syncthreads();
     }
-    if (fx.how == OUT_PUBLISH) flag_publish(s.flags + fx.cta * Cfg::NW + wave);
+    if constexpr (FIX == FIX_HANDOFF)
+      if (fx.how == OUT_PUBLISH) flag_publish(s.flags + fx.cta * Cfg::NW + wave);
   }
 
   SKG_DEV int cta_of(int it) const {
@@ -1380,15 +1404,16 @@ struct Engine {
     Fix fx = {OUT_STORE, 0, cta, false};
     if (cta < 0) return fx;  // data-parallel tile: sole writer
     const bool started = k0 == 0, ended = k1 == p.ipt;
-    if (p.reduction == RED_WORKSPACE) {
-      fx.how = OUT_WORKSPACE;
+    if constexpr (FIX == FIX_ATOMIC) {
+      // workspace: every stream-K segment adds into the tile's scratch (the
+      // second stage writes C); atomic: a whole tile is stored directly.
+      if (p.reduction == RED_WORKSPACE)
+        fx.how = OUT_WORKSPACE;
+      else if (!(started && ended))
+        fx.how = OUT_ATOMIC;
       return fx;
     }
     if (started && ended) return fx;  // a whole tile inside one range
-    if (p.reduction == RED_ATOMIC) {
-      fx.how = OUT_ATOMIC;
-      return fx;
-    }
     const int sk_tile = tile - p.dp_tiles;
     const int first = cta_of(sk_tile * p.ipt);
     const int last = cta_of(sk_tile * p.ipt + p.ipt - 1);
@@ -1495,14 +1520,14 @@ struct Engine {
   }
 };
 
-template <class Cfg, class Prob>
+template <class Cfg, class Prob, int FIX>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_CTAS) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
   constexpr int kLds = Prob::Loader::kGrouped ? Cfg::LDS_GRP
                        : Prob::Loader::kDma   ? Cfg::LDS_DMA
                                               : Cfg::LDS;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
-  Engine<Cfg, Prob> e(prm, p, s, (SKG_LDS char*)lds);
+  Engine<Cfg, Prob, FIX> e(prm, p, s, (SKG_LDS char*)lds);
   e.run();
 }
 
@@ -1522,8 +1547,8 @@ __global__ __launch_bounds__(256) void stage2_kernel(typename Prob::Params prm, 
     const int row = idx / Cfg::TN, col = idx % Cfg::TN;
     if (row >= o.rows || col >= o.cols) continue;
     float v = w[idx];
-    if (o.sa) v *= o.sa[row];
-    if (o.sb) v *= o.sb[col];
+    if (o.sa) v *= o.sa[row * Prob::kScaleInc];
+    if (o.sb) v *= o.sb[col * Prob::kScaleInc];
     const size_t oi = (size_t)row * o.ld + col;
     if (dt == DT_F32)
       ((float*)o.base)[oi] = v;

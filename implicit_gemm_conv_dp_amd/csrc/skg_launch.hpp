@@ -20,17 +20,29 @@ struct WgradInst {
 };
 
 // {nullptr, nullptr} when the (tile, dtype) pair has no compiled instance.
-GemmInst gemm_instance(int tile_id, int dtype);
+// tensor_scales selects the per-tensor scale instances.
+GemmInst gemm_instance(int tile_id, int dtype, bool tensor_scales);
+GemmInst gemm_instance_f16(int tile_id, bool tensor_scales);
+GemmInst gemm_instance_bf16(int tile_id, bool tensor_scales);
+GemmInst gemm_instance_f8(int tile_id, int dtype, bool tensor_scales);
 WgradInst wgrad_instance(int tile_id, int dtype);
 
-// Launches the stream-K kernel (bracketed by ev0 / ev1 when they are set)
-// and, for the workspace reduction, the second stage.
+// Launches the stream-K kernel of the plan's fix-up family (bracketed by ev0
+// / ev1 when they are set) and, for the workspace reduction, the second
+// stage.
 template <class Cfg, class Prob>
 hipError_t launch_instance(const typename Prob::Params& prm, const KPlan& p, const Scratch& s,
                            hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((sk_kernel<Cfg, Prob>), dim3(p.grid), dim3(Cfg::THREADS), 0, st, prm, p, s);
+  // A plan without stream-K CTAs runs no fix-up: it takes the hand-off
+  // family, the instance every data-parallel-only launch uses.
+  if ((p.reduction == RED_ATOMIC || p.reduction == RED_WORKSPACE) && p.sk_ctas > 0)
+    hipLaunchKernelGGL((sk_kernel<Cfg, Prob, FIX_ATOMIC>), dim3(p.grid), dim3(Cfg::THREADS), 0, st,
+                       prm, p, s);
+  else
+    hipLaunchKernelGGL((sk_kernel<Cfg, Prob, FIX_HANDOFF>), dim3(p.grid), dim3(Cfg::THREADS), 0, st,
+                       prm, p, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
@@ -44,7 +56,15 @@ hipError_t launch_instance(const typename Prob::Params& prm, const KPlan& p, con
 
 template <class Cfg, class Prob>
 hipError_t occupancy_instance(int* out) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, sk_kernel<Cfg, Prob>, Cfg::THREADS, 0);
+  // Both families are built with the same launch bounds and LDS; the
+  // smaller of the two residencies is reported.
+  int h = 0, a = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&h, sk_kernel<Cfg, Prob, FIX_HANDOFF>,
+                                                              Cfg::THREADS, 0);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, sk_kernel<Cfg, Prob, FIX_ATOMIC>, Cfg::THREADS, 0);
+  *out = h < a ? h : a;
+  return e;
 }
 
 }  // namespace skg

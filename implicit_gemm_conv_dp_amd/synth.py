@@ -2,8 +2,8 @@
 
 This module holds none of the engine's arithmetic: it draws numbers with
 numpy's PCG64 generator and stores them in the operand formats through
-torch's CPU casts (float32 -> float16 / bfloat16 / float8_e4m3fn, round to
-nearest even).  Both the HIP path and the CPU oracle read the same stored
+torch's CPU casts (float32 -> float16 / bfloat16 / float8_e4m3fn /
+float8_e5m2, round to nearest even).  Both the HIP path and the CPU oracle read the same stored
 codes.
 
 Seeds: workload ``i`` (1..5) uses base seed ``1000 + i``; its operand streams
@@ -17,8 +17,9 @@ import numpy as np
 import torch
 
 TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
-            "f32": torch.float32}
-CODE_DT = {"f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "f32": np.uint32}
+            "e5m2": torch.float8_e5m2, "f32": torch.float32}
+CODE_DT = {"f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
+           "f32": np.uint32}
 
 
 def rng(seed):
@@ -43,7 +44,7 @@ def draw(dist, n, seed):
 def to_codes(values, fmt):
     """Store float values in ``fmt`` via torch's CPU cast; returns the codes."""
     t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).to(TORCH_DT[fmt])
-    view = torch.uint8 if fmt == "e4m3" else (torch.int16 if fmt != "f32" else torch.int32)
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[np.dtype(CODE_DT[fmt]).itemsize]
     return t.view(view).numpy().view(CODE_DT[fmt])
 
 
@@ -77,6 +78,7 @@ class GemmWorkload:
     ctas: int
     scales: bool = False
     op: str = "gemm"
+    scale_mode: str = "rowcol"   # or "tensor": one scale per operand
 
     @property
     def seed(self):
@@ -94,8 +96,9 @@ class GemmWorkload:
             "B": to_codes(draw(self.dist, self.N * self.K, s + 1), self.dtype_ab),
         }
         if self.scales:
-            out["scale_a"] = draw("scale", self.M, s + 2).astype(np.float32)
-            out["scale_b"] = draw("scale", self.N, s + 3).astype(np.float32)
+            per = self.scale_mode == "rowcol"
+            out["scale_a"] = draw("scale", self.M if per else 1, s + 2).astype(np.float32)
+            out["scale_b"] = draw("scale", self.N if per else 1, s + 3).astype(np.float32)
         return out
 
 
@@ -153,7 +156,7 @@ WORKLOADS = {
                     "normal01", "256x256x64", ("persistent", "dp_sk"), ("tree",), 256),
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
                      (1, 1), (1, 1), 1, "f16", "uniform", "256x128x64",
-                     ("dp_sk", "persistent"), ("linear", "tree", "atomic", "workspace"), 256),
+                     ("dp_sk", "persistent"), ("workspace", "linear", "tree", "atomic"), 256),
     4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
                      (2, 2), (1, 1), 32, "bf16", "uniform", "32x64x64", ("dp_sk",), ("linear",),
                      256),

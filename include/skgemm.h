@@ -58,7 +58,25 @@ enum skg_dtype {
   SKG_F16 = 0,     /* IEEE binary16 */
   SKG_BF16 = 1,    /* bfloat16 */
   SKG_F8E4M3 = 2,  /* OCP fp8 E4M3 (bias 7, max 448, no inf), the gfx950 fp8 */
-  SKG_F32 = 3      /* IEEE binary32 (outputs only) */
+  SKG_F32 = 3,     /* IEEE binary32 (outputs only) */
+  SKG_F8E5M2 = 4   /* OCP bf8 E5M2 (bias 15, max 57344, inf and NaN: the upper
+                      byte of an IEEE binary16), the gfx950 bf8 ("gemm_rowcolquant
+                      dispatcher bridge" PR: fp8/bf8 rcr scope; OCP encoding on
+                      gfx950 per its round-3 fixes) */
+};
+
+/* How scale_a / scale_b apply.  Row/column scaling is the "gemm_rowcolquant
+ * dispatcher bridge" PR's own; per-tensor scaling is its sibling
+ * "tensor_quant" (same PR, final description: one scalar scale for all of A
+ * and one for all of B).
+ *   SKG_SCALE_ROWCOL  scale_a holds M floats (one per row of A), scale_b N
+ *                     floats (one per column of B);
+ *   SKG_SCALE_TENSOR  scale_a and scale_b each hold one float for the whole
+ *                     operand.
+ * Either pointer may be NULL (scale 1) in both modes. */
+enum skg_scale_mode {
+  SKG_SCALE_ROWCOL = 0,
+  SKG_SCALE_TENSOR = 1
 };
 
 /* Launch modes (PR #13151, Technical Details: Wgrad kernel, launch modes).
@@ -133,7 +151,8 @@ typedef struct skg_tile_info {
 /* GEMM problem.  A is M x K row-major with leading dimension lda (elements),
  * B is K x N column-major (column n is K contiguous elements at B + n*ldb),
  * C is M x N row-major with leading dimension ldc.  scale_a (M floats) and
- * scale_b (N floats) are optional (NULL means 1.0); the epilogue computes
+ * scale_b (N floats; one float each with SKG_SCALE_TENSOR) are optional
+ * (NULL means 1.0); the epilogue computes
  * C[m][n] = round_to_nearest_even((acc * scale_a[m]) * scale_b[n]) in fp32
  * ("gemm_rowcolquant dispatcher bridge" PR, final description: scales applied
  * in the epilogue, fp32 accumulator narrowed only there).
@@ -141,7 +160,7 @@ typedef struct skg_tile_info {
  * multiple of 16 bytes of input type. */
 typedef struct skg_gemm_args {
   int64_t M, N, K;
-  int32_t dtype_ab;        /* SKG_F16, SKG_BF16 or SKG_F8E4M3 */
+  int32_t dtype_ab;        /* SKG_F16, SKG_BF16, SKG_F8E4M3 or SKG_F8E5M2 */
   int32_t dtype_c;         /* SKG_F16, SKG_BF16 or SKG_F32 */
   const void* A;
   int64_t lda;
@@ -156,6 +175,7 @@ typedef struct skg_gemm_args {
   int32_t reduction;       /* enum skg_reduction */
   int32_t ctas;            /* stream-K pool (split-K: slices per tile); -1 = default;
                               0 or < -1 rejected */
+  int32_t scale_mode;      /* enum skg_scale_mode */
 } skg_gemm_args_t;
 
 /* wgrad problem (PR #13151, Motivation and Technical Details).  X is the

@@ -12,10 +12,13 @@ stored mantissa bits:
                with mantissa 111; the largest finite value is 448.  This is the
                fp8 encoding gfx950 uses (the "gemm_rowcolquant dispatcher
                bridge" PR, round-3 fixes: OCP on gfx950, FNUZ on gfx942).
+* ``e5m2``  -- OCP 8-bit floating point, E5M2 variant ("bf8" on that PR):
+               E=5, B=15, M=2, infinities and NaNs as in IEEE-754; its codes
+               are the upper bytes of binary16 codes.
 
 Decoding is exact in float64.  Encoding rounds to nearest, ties to even.
-Values beyond the largest finite number become +/-inf for f16 / bf16 (IEEE
-overflow under round-to-nearest) and saturate to +/-448 for e4m3 (our reading:
+Values beyond the largest finite number become +/-inf for f16 / bf16 / e5m2
+(IEEE overflow under round-to-nearest) and saturate to +/-448 for e4m3 (our reading:
 the pages only name the OCP encoding; saturation is the conventional
 "satfinite" conversion and never triggers on the workloads, whose fp8 data is
 quantised N(0,1)).
@@ -28,6 +31,7 @@ FORMATS = {
     "f16": (5, 15, 10, True, 2),
     "bf16": (8, 127, 7, True, 2),
     "e4m3": (4, 7, 3, False, 1),
+    "e5m2": (5, 15, 2, True, 1),
 }
 
 

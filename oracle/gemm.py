@@ -10,7 +10,10 @@ description, scope section; and the stream-K GEMM bridge commit
 
 in the "rcr" layout: A row-major (element (m, k) at ``A[m*lda + k]``), B
 column-major (element (k, n) at ``B[n*ldb + k]``), C row-major.  The scales
-are float32 vectors of length M and N; an absent scale is 1.  Everything is
+are float32 vectors of length M and N (``scale_mode="rowcol"``), or one
+float each for the whole of A and of B (``scale_mode="tensor"``, the
+per-tensor sibling "tensor_quant" named in that PR's final description:
+sA[m] = sA, sB[n] = sB); an absent scale is 1.  Everything is
 evaluated in float64 on the decoded input codes, so the result is the exact
 product sum up to float64 rounding.  The matrix product itself is numpy's
 float64 matmul (a library primitive); there is no blocking or reordering here.
@@ -36,9 +39,30 @@ def operand_matrix(fmt, codes, rows, cols, ld):
     return decode(fmt, padded.reshape(rows, ld)[:, :cols])
 
 
+def scale_vectors(scale_a, scale_b, M, N, scale_mode):
+    """Per-row and per-column float64 scale vectors (None stays None)."""
+    if scale_mode not in ("rowcol", "tensor"):
+        raise ValueError("unknown scale mode")
+    out = []
+    for s, n in ((scale_a, M), (scale_b, N)):
+        if s is None:
+            out.append(None)
+            continue
+        s = np.asarray(s, dtype=np.float64).reshape(-1)
+        if scale_mode == "tensor":
+            if s.size != 1:
+                raise ValueError("a per-tensor scale is one value")
+            s = np.full(n, s[0])
+        elif s.size != n:
+            raise ValueError("scale length")
+        out.append(s)
+    return out
+
+
 def gemm(fmt, a_codes, b_codes, M, N, K, lda=None, ldb=None,
-         scale_a=None, scale_b=None):
+         scale_a=None, scale_b=None, scale_mode="rowcol"):
     """float64 ``R`` (M x N) for rcr operands holding ``fmt`` codes."""
+    scale_a, scale_b = scale_vectors(scale_a, scale_b, M, N, scale_mode)
     lda = K if lda is None else lda
     ldb = K if ldb is None else ldb
     a = operand_matrix(fmt, a_codes, M, K, lda)          # a[m][k]
@@ -52,16 +76,22 @@ def gemm(fmt, a_codes, b_codes, M, N, K, lda=None, ldb=None,
 
 
 def gemm_entry(fmt, a_codes, b_codes, m, n, K, lda=None, ldb=None,
-               scale_a=None, scale_b=None):
+               scale_a=None, scale_b=None, scale_mode="rowcol"):
     """One output element R[m][n], computed on its own (for sampled checks of
     outputs too large to form whole)."""
+    if scale_mode == "tensor":
+        m_s = n_s = 0
+    elif scale_mode == "rowcol":
+        m_s, n_s = m, n
+    else:
+        raise ValueError("unknown scale mode")
     lda = K if lda is None else lda
     ldb = K if ldb is None else ldb
     a_row = decode(fmt, np.asarray(a_codes).reshape(-1)[m * lda: m * lda + K])
     b_col = decode(fmt, np.asarray(b_codes).reshape(-1)[n * ldb: n * ldb + K])
     v = float(np.dot(a_row, b_col))
     if scale_a is not None:
-        v *= float(np.asarray(scale_a).reshape(-1)[m])
+        v *= float(np.asarray(scale_a).reshape(-1)[m_s])
     if scale_b is not None:
-        v *= float(np.asarray(scale_b).reshape(-1)[n])
+        v *= float(np.asarray(scale_b).reshape(-1)[n_s])
     return v

@@ -8,9 +8,10 @@ import torch
 
 from oracle import codecs
 
-VIEW = {"f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8, "f32": torch.int32}
-NPV = {"f16": np.int16, "bf16": np.int16, "e4m3": np.uint8, "f32": np.int32}
-TOL = {"f16": 5e-3, "bf16": 5e-3, "e4m3": 2e-2}
+VIEW = {"f16": torch.int16, "bf16": torch.int16, "e4m3": torch.uint8, "e5m2": torch.uint8,
+        "f32": torch.int32}
+NPV = {"f16": np.int16, "bf16": np.int16, "e4m3": np.uint8, "e5m2": np.uint8, "f32": np.int32}
+TOL = {"f16": 5e-3, "bf16": 5e-3, "e4m3": 2e-2, "e5m2": 2e-2}
 
 
 def to_dev(codes, fmt):

@@ -28,16 +28,19 @@ MODES = ["dp", "dp_sk", "persistent"]
 REDS = ["linear", "tree", "atomic", "workspace"]
 TILE_DT = [("128x128x32", "f16"), ("128x128x32", "bf16"), ("256x256x64", "bf16"),
            ("256x256x64", "f16"), ("128x128x64", "bf16"), ("256x128x64", "f16"),
-           ("256x256x128", "e4m3")]
+           ("256x256x128", "e4m3"), ("256x256x128", "e5m2")]
+FP8 = ("e4m3", "e5m2")
 
 
-def run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa=None, sb=None, ws=None, C=None):
+def run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa=None, sb=None, ws=None, C=None,
+        scale_mode="rowcol"):
     dA, dB = to_dev(A, fmt), to_dev(B, fmt)
     dC = C if C is not None else out_buffer(fmt_c, M * N)
     dsa = to_dev_f32(sa) if sa is not None else None
     dsb = to_dev_f32(sb) if sb is not None else None
     plan = skg.gemm(dA, dB, dC, dsa, dsb, workspace=ws, M=M, N=N, K=K, dtype_ab=fmt,
-                    dtype_c=fmt_c, tile=tile, mode=mode, reduction=red, ctas=ctas)
+                    dtype_c=fmt_c, tile=tile, mode=mode, reduction=red, ctas=ctas,
+                    scale_mode=scale_mode)
     torch.cuda.synchronize()
     return decode_out(dC, fmt_c).reshape(M, N), plan
 
@@ -53,7 +56,7 @@ def shape_for(tile, k_tail=False):
 def test_random_all_modes_and_fixups(tile, fmt):
     M, N, K = shape_for(tile)
     g = synth.rng(11)
-    dist = "normal" if fmt == "e4m3" else "uniform"
+    dist = "normal" if fmt in FP8 else "uniform"
     A = synth.to_codes(synth.draw(dist, M * K, 1), fmt)
     B = synth.to_codes(synth.draw(dist, N * K, 2), fmt)
     sa = synth.draw("scale", M, 3).astype(np.float32)
@@ -65,7 +68,7 @@ def test_random_all_modes_and_fixups(tile, fmt):
                 continue
             for ctas in (4, 7, 13):
                 fmt_c = "f32" if red == "atomic" else ("bf16" if int(g.integers(2)) else "f16")
-                if fmt_c == "f16" and fmt == "e4m3":
+                if fmt_c == "f16" and fmt in FP8:
                     fmt_c = "bf16"
                 Y, plan = run(A, B, M, N, K, fmt, fmt_c, tile, mode, red, ctas, sa, sb)
                 assert_close(Y, R, fmt, "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas))
@@ -223,7 +226,7 @@ def test_auto_splits_one_short_tile(tile, fmt):
     tm, tn, tk = map(int, tile.split("x"))
     M, N, K = tm - 3, tn - 8, 40 * tk
     g = synth.rng(51)
-    dist = "normal" if fmt == "e4m3" else "uniform"
+    dist = "normal" if fmt in FP8 else "uniform"
     A = synth.to_codes(synth.draw(dist, M * K, 52), fmt)
     B = synth.to_codes(synth.draw(dist, N * K, 53), fmt)
     R = oracle_gemm(fmt, A, B, M, N, K)
@@ -231,3 +234,52 @@ def test_auto_splits_one_short_tile(tile, fmt):
     assert plan["slices"] == 5 and plan["sk_ctas"] == 5 and plan["dp_tiles"] == 0
     assert plan["reduction"] == skg.REDUCTIONS["workspace"]
     assert_close(Y, R, fmt, "%s auto one short tile" % tile)
+
+
+@pytest.mark.parametrize("tile,fmt", [("256x256x128", "e4m3"), ("256x256x128", "e5m2"),
+                                      ("256x256x64", "bf16"), ("128x128x32", "f16")])
+def test_per_tensor_scales(tile, fmt):
+    # One scale for all of A and one for all of B: bit-exact on integer data
+    # with power-of-two scales, every launch mode and fix-up; random data
+    # within the tolerance.
+    M, N, K = shape_for(tile, True)
+    A = synth.integer_codes(fmt, M * K, 71, 0.15)
+    B = synth.integer_codes(fmt, N * K, 72, 0.15)
+    sa, sb = np.array([0.5], np.float32), np.array([4.0], np.float32)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb, scale_mode="tensor")
+    for mode, red, ctas in [("dp", "linear", 1), ("dp_sk", "linear", 5), ("dp_sk", "tree", 13),
+                            ("persistent", "workspace", 7), ("persistent", "atomic", 4),
+                            ("splitk", "tree", 3)]:
+        Y, plan = run(A, B, M, N, K, fmt, "f32", tile, mode, red, ctas, sa, sb,
+                      scale_mode="tensor")
+        assert np.array_equal(Y, R), "%s %s %s %s per-tensor not bit-exact" % (tile, fmt, mode, red)
+    A = synth.to_codes(synth.draw("normal", M * K, 73), fmt)
+    B = synth.to_codes(synth.draw("normal", N * K, 74), fmt)
+    sa, sb = np.array([1.37], np.float32), np.array([0.61], np.float32)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb, scale_mode="tensor")
+    Y, plan = run(A, B, M, N, K, fmt, "bf16", tile, "dp_sk", "tree", 7, sa, sb,
+                  scale_mode="tensor")
+    assert_close(Y, R, fmt, "%s %s per-tensor random" % (tile, fmt))
+    # one scale pointer only: the other operand is unscaled
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_b=sb, scale_mode="tensor")
+    Y, plan = run(A, B, M, N, K, fmt, "bf16", tile, "dp_sk", "linear", 7, None, sb,
+                  scale_mode="tensor")
+    assert_close(Y, R, fmt, "%s %s per-tensor B only" % (tile, fmt))
+
+
+def test_e5m2_workload_shape_sampled():
+    # The fp8 workload's shape and launch with E5M2 operands and per-tensor
+    # scales, checked on sampled outputs.
+    wl = synth.WORKLOADS[5]
+    M = N = K = 8192
+    A = synth.to_codes(synth.draw("normal", M * K, 81), "e5m2")
+    B = synth.to_codes(synth.draw("normal", N * K, 82), "e5m2")
+    sa, sb = np.array([1.25], np.float32), np.array([0.75], np.float32)
+    Y, plan = run(A, B, M, N, K, "e5m2", "bf16", wl.tile, wl.modes[0], wl.reductions[0], wl.ctas,
+                  sa, sb, scale_mode="tensor")
+    assert not np.isnan(Y).any(), "unwritten outputs"
+    g = synth.rng(98)
+    ms, ns = g.integers(0, M, 800), g.integers(0, N, 800)
+    ref = np.array([gemm_entry("e5m2", A, B, int(m), int(c), K, scale_a=sa, scale_b=sb,
+                               scale_mode="tensor") for m, c in zip(ms, ns)])
+    assert rel_err(Y[ms, ns], ref) <= TOL["e5m2"]

@@ -76,6 +76,7 @@ def same_plan(c, o):
 
 
 GEMM_TILE_DT = [("128x128x32", "f16"), ("256x256x64", "bf16"), ("256x256x128", "e4m3"),
+                ("256x256x128", "e5m2"),
                 ("128x128x64", "bf16"), ("256x128x64", "f16")]
 
 
@@ -163,6 +164,8 @@ def test_gemm_validation_rejects():
     assert "tile" in bad(tile=17)
     assert "instance" in bad(tile="256x256x128")
     assert "instance" in bad(dtype_ab="e4m3")
+    assert "instance" in bad(dtype_ab="e5m2")
+    assert "scale mode" in bad(scale_mode=2)
     assert "dtype" in bad(dtype_c="e4m3")
     assert "positive" in bad(M=0)
     assert "16 bytes" in bad(K=100)
@@ -256,7 +259,7 @@ def test_flag_ordering_in_isa():
     with tempfile.TemporaryDirectory() as tmp:
         objs = code_objects(tmp)
     assert objs, "no gfx950 code object in the library"
-    n_kernels = 0
+    n_kernels = n_atomic = 0
     for dis in objs:
         for name, body in kernels(dis).items():
             if "sk_kernel" not in name:
@@ -265,6 +268,16 @@ def test_flag_ordering_in_isa():
             ins = instrs(body)
             # No L2-wide write-back or invalidation anywhere in the kernel.
             assert not any(x.startswith(("buffer_wbl2", "buffer_inv")) for x in ins), name
+            # The last template argument is the fix-up family: 1 = atomic /
+            # workspace, which hands nothing on and waits for nothing.
+            fam = re.search(r"ELi([01])EEEvNT", name)
+            assert fam, name
+            if fam.group(1) == "1":
+                n_atomic += 1
+                assert not any(x.endswith("sc1") and x.startswith(("global_store", "global_load"))
+                               for x in ins), name + ": flags in an atomic-family kernel"
+                assert any(x.startswith("global_atomic_add_f32") for x in ins), name
+                continue
             # Partials go out and come back at device scope (sc1).
             assert any(x.startswith("buffer_store_dwordx4") and x.endswith("sc1") for x in ins), name
             assert any(x.startswith("buffer_load_dwordx4") and x.endswith("sc1") for x in ins), name
@@ -280,4 +293,4 @@ def test_flag_ordering_in_isa():
                 assert not any(x.startswith(("buffer_store", "global_store")) for x in between), name
             polls = [x for x in ins if x.startswith("global_load_dword ") and x.endswith("sc1")]
             assert polls, name + ": no device-scope poll"
-    assert n_kernels >= 17
+    assert n_kernels >= 40 and n_atomic == n_kernels // 2

@@ -1,9 +1,10 @@
 """Pins of the oracle's number formats (CPU only).
 
 Each format is checked against something other than the oracle itself:
-library casts (numpy's float16, torch's bfloat16 / float8_e4m3fn), the OCP
-specification's closed forms (tests/golden/e4m3_ocp_codes.txt) and the
-round-to-nearest-even rule on every midpoint.
+library casts (numpy's float16, torch's bfloat16 / float8_e4m3fn /
+float8_e5m2), the OCP specification's closed forms
+(tests/golden/e4m3_ocp_codes.txt; E5M2 codes are the upper bytes of binary16
+codes) and the round-to-nearest-even rule on every midpoint.
 """
 
 import os
@@ -41,6 +42,16 @@ def test_e4m3_decode_matches_torch_on_every_code():
     assert same(codecs.decode("e4m3", ALL8), t.double().numpy())
 
 
+def test_e5m2_is_the_upper_byte_of_binary16():
+    # OCP E5M2 shares binary16's sign, exponent and bias; its two mantissa
+    # bits are binary16's top two, so code c decodes as the binary16 c << 8.
+    ref = (ALL8.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    assert same(codecs.decode("e5m2", ALL8), ref)
+    t = torch.from_numpy(ALL8.copy()).view(torch.float8_e5m2)
+    assert same(codecs.decode("e5m2", ALL8), t.double().numpy())
+    assert codecs.max_finite("e5m2") == 57344.0
+
+
 def test_e4m3_spec_table(golden_dir):
     with open(os.path.join(golden_dir, "e4m3_ocp_codes.txt")) as f:
         rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
@@ -55,7 +66,8 @@ def test_e4m3_spec_table(golden_dir):
     assert codecs.max_finite("bf16") == float(torch.finfo(torch.bfloat16).max)
 
 
-@pytest.mark.parametrize("fmt,codes", [("f16", ALL16), ("bf16", ALL16), ("e4m3", ALL8)])
+@pytest.mark.parametrize("fmt,codes", [("f16", ALL16), ("bf16", ALL16), ("e4m3", ALL8),
+                                       ("e5m2", ALL8)])
 def test_encode_inverts_decode(fmt, codes):
     vals = codecs.decode(fmt, codes)
     finite = ~np.isnan(vals)
@@ -63,7 +75,8 @@ def test_encode_inverts_decode(fmt, codes):
     assert np.array_equal(back, codes[finite])
 
 
-@pytest.mark.parametrize("fmt,codes", [("f16", ALL16), ("bf16", ALL16), ("e4m3", ALL8)])
+@pytest.mark.parametrize("fmt,codes", [("f16", ALL16), ("bf16", ALL16), ("e4m3", ALL8),
+                                       ("e5m2", ALL8)])
 def test_encode_rounds_midpoints_to_even(fmt, codes):
     ebits, bias, mbits, has_inf, _ = codecs.FORMATS[fmt]
     sign_bit = 1 << (ebits + mbits)
@@ -83,7 +96,8 @@ def test_encode_rounds_midpoints_to_even(fmt, codes):
 
 
 @pytest.mark.parametrize("fmt,tdt", [("f16", torch.float16), ("bf16", torch.bfloat16),
-                                     ("e4m3", torch.float8_e4m3fn)])
+                                     ("e4m3", torch.float8_e4m3fn),
+                                     ("e5m2", torch.float8_e5m2)])
 def test_encode_matches_torch_cast_on_random_floats(fmt, tdt):
     rng = np.random.default_rng(7)
     x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 1, 30, 300)])
@@ -91,7 +105,7 @@ def test_encode_matches_torch_cast_on_random_floats(fmt, tdt):
     if fmt == "e4m3":
         x = x[np.abs(x) < 440]
     ref = torch.from_numpy(x).to(tdt)
-    ref_codes = ref.view(torch.uint8 if fmt == "e4m3" else torch.int16).numpy()
+    ref_codes = ref.view(torch.uint8 if fmt in ("e4m3", "e5m2") else torch.int16).numpy()
     got = codecs.encode(fmt, x.astype(np.float64))
     assert np.array_equal(got.view(ref_codes.dtype), ref_codes)
 
@@ -102,3 +116,9 @@ def test_overflow_rules():
     # e4m3 saturates (reading R21): beyond 448 stays 448, never NaN.
     assert codecs.decode("e4m3", codecs.encode("e4m3", [470.0, 1e6, -1e6])).tolist() == [448.0, 448.0, -448.0]
     assert codecs.decode("e4m3", codecs.encode("e4m3", [464.0]))[0] == 448.0
+    # e5m2 overflows to inf like binary16 (IEEE rounding: at and beyond the
+    # midpoint 61440 between 57344 and the next binade).
+    assert np.isinf(codecs.decode("e5m2", codecs.encode("e5m2", [61440.0]))[0])
+    assert codecs.decode("e5m2", codecs.encode("e5m2", [61439.0]))[0] == 57344.0
+    t = torch.tensor([61440.0, 61439.0]).to(torch.float8_e5m2).double().numpy()
+    assert np.isinf(t[0]) and t[1] == 57344.0

@@ -20,7 +20,7 @@ def rand_codes(fmt, shape, rng, lo=-3, hi=3):
     return codecs.encode(fmt, vals)
 
 
-@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3", "e5m2"])
 def test_identity_b_gives_scaled_a(fmt):
     rng = np.random.default_rng(1)
     M, K = 7, 12
@@ -40,7 +40,7 @@ def test_all_ones_gives_k():
     assert np.array_equal(gemm("f16", one, oneb, M, N, K), np.full((M, N), float(K)))
 
 
-@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "e4m3", "e5m2"])
 def test_matches_triple_loop_with_leading_dimensions(fmt):
     rng = np.random.default_rng(2)
     M, N, K, lda, ldb = 5, 4, 6, 9, 8
@@ -72,3 +72,27 @@ def test_nonsymmetric_hand_example():
 def test_rejects_short_buffers():
     with pytest.raises(ValueError):
         gemm("f16", np.zeros(5, np.uint16), np.zeros(6, np.uint16), 2, 2, 3)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_per_tensor_scales_by_triple_loop(fmt):
+    # One scale for all of A and one for all of B (per-tensor quantisation):
+    # an independent loop, and the per-element form.
+    rng = np.random.default_rng(3)
+    M, N, K = 4, 5, 7
+    a = rand_codes(fmt, (M * K,), rng)
+    b = rand_codes(fmt, (N * K,), rng)
+    sa, sb = np.float32(1.75), np.float32(0.375)
+    r = gemm(fmt, a, b, M, N, K, scale_a=[sa], scale_b=[sb], scale_mode="tensor")
+    av = [float(v) for v in codecs.decode(fmt, a)]
+    bv = [float(v) for v in codecs.decode(fmt, b)]
+    for m in range(M):
+        for n in range(N):
+            acc = sum(av[m * K + k] * bv[n * K + k] for k in range(K))
+            assert r[m, n] == pytest.approx(acc * float(sa) * float(sb), rel=1e-14, abs=1e-14)
+            e = gemm_entry(fmt, a, b, m, n, K, scale_a=[sa], scale_b=[sb], scale_mode="tensor")
+            assert e == pytest.approx(r[m, n], rel=1e-14, abs=1e-14)
+    with pytest.raises(ValueError):
+        gemm(fmt, a, b, M, N, K, scale_a=[sa, sa], scale_mode="tensor")
+    with pytest.raises(ValueError):
+        gemm(fmt, a, b, M, N, K, scale_mode="block")
