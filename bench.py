@@ -100,7 +100,7 @@ def measured_traffic(path, name, tile, mode, red, ctas):
 def alg_bytes(wl):
     """Each input read once plus the output written once."""
     if wl.op == "gemm":
-        eab = 1 if wl.dtype_ab == "e4m3" else 2
+        eab = 1 if wl.dtype_ab in ("e4m3", "e5m2") else 2
         ec = 4 if wl.dtype_c == "f32" else 2
         extra = (4 * (wl.M + wl.N) if wl.scale_mode == "rowcol" else 8) if wl.scales else 0
         return eab * (wl.M * wl.K + wl.N * wl.K) + ec * wl.M * wl.N + extra
@@ -135,20 +135,20 @@ def cpu_baseline(wl, inp, target_s):
         return time.perf_counter() - t0, flops
 
     # One small warm-up run, then grow the sample (at most 8x per step, by
-    # the measured rate) until it takes half the target time or covers the
-    # whole workload.
+    # the measured rate) until it takes the target time or covers the whole
+    # workload.
     full = wl.M if wl.op == "gemm" else wl.n
     units = max(1, full // 64)
     run(units)
     while True:
         t, flops = run(units)
-        if t >= target_s / 2 or units >= full:
+        if t >= target_s or units >= full:
             break
         grow = min(8.0, max(2.0, target_s / max(t, 1e-3)))
         units = min(full, int(units * grow))
     # The whole workload takes less than the target: repeat it.
     reps = 1
-    while t * (reps + 1) / reps < target_s / 2 and units >= full and reps < 64:
+    while t < target_s and units >= full and reps < 256:
         t_more, _ = run(units)
         t += t_more
         reps += 1
