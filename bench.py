@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--ctas", type=int, default=None)
     ap.add_argument("--tile", default=None)
+    ap.add_argument("--sk-order", default="auto", choices=["auto", "block", "xcd"],
+                    help="stream-K CTA order (auto: xcd for wgrad, block for GEMM)")
     ap.add_argument("--dtype", default=None, choices=["e4m3", "e5m2"],
                     help="fp8 operand format of the fp8 GEMM workload (default e4m3)")
     ap.add_argument("--scale-mode", default=None, choices=["rowcol", "tensor"],
@@ -211,7 +213,8 @@ def main():
         out = torch.empty(wl.M * wl.N, dtype=torch.float32 if wl.dtype_c == "f32" else torch.int16,
                           device=dev)
         kw = dict(M=wl.M, N=wl.N, K=wl.K, dtype_ab=wl.dtype_ab, dtype_c=wl.dtype_c, tile=tile,
-                  mode=mode, reduction=red, ctas=ctas, scale_mode=wl.scale_mode)
+                  mode=mode, reduction=red, ctas=ctas, scale_mode=wl.scale_mode,
+                  sk_order=args.sk_order)
         plan = skg.plan_gemm(**kw)
         ws = skg.workspace_for(plan, dev)
 
@@ -223,7 +226,7 @@ def main():
         out = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device=dev)
         kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
                   pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile=tile, mode=mode,
-                  reduction=red, ctas=ctas)
+                  reduction=red, ctas=ctas, sk_order=args.sk_order)
         plan = skg.plan_wgrad(**kw)
         ws = skg.workspace_for(plan, dev)
 
@@ -295,7 +298,8 @@ def main():
                        "iters_per_sk_cta", "extra_iters", "grid", "max_contrib", "tree_rounds")},
                    "resolved": {"mode": names(skg.MODES)[plan["mode"]],
                                 "reduction": names(skg.REDUCTIONS)[plan["reduction"]],
-                                "ctas": plan["pool"], "slices": plan["slices"]}},
+                                "ctas": plan["pool"], "slices": plan["slices"],
+                                "sk_order": names(skg.SK_ORDERS)[plan["sk_order"]]}},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -17,10 +17,11 @@ element type is ``dtype_ab`` / ``dtype_c``.  ``wgrad`` takes NHWC ``x`` and
 from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
                    skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
-                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES)
+                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
 
 __all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
            "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES", "SCALE_MODES",
+           "SK_ORDERS",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
            "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events"]
 
@@ -40,7 +41,7 @@ def _ptr(t):
 
 def gemm_args(A=None, B=None, C=None, *, M, N, K, dtype_ab, dtype_c, lda=None, ldb=None,
               ldc=None, scale_a=None, scale_b=None, scale_mode="rowcol", tile, mode, reduction,
-              ctas):
+              ctas, sk_order="auto"):
     a = _lib.skg_gemm_args_t()
     a.M, a.N, a.K = M, N, K
     a.dtype_ab = _enum(DTYPES, dtype_ab, "dtype")
@@ -55,11 +56,12 @@ def gemm_args(A=None, B=None, C=None, *, M, N, K, dtype_ab, dtype_c, lda=None, l
     a.reduction = _enum(REDUCTIONS, reduction, "reduction")
     a.ctas = ctas
     a.scale_mode = _enum(SCALE_MODES, scale_mode, "scale mode")
+    a.sk_order = _enum(SK_ORDERS, sk_order, "stream-K order")
     return a
 
 
 def wgrad_args(x=None, dy=None, dw=None, *, n, h, w, c, k, r, s, stride=(1, 1), pad=(0, 0),
-               groups=1, dtype, tile, mode, reduction, ctas):
+               groups=1, dtype, tile, mode, reduction, ctas, sk_order="auto"):
     a = _lib.skg_wgrad_args_t()
     a.n, a.h, a.w, a.c, a.k, a.r, a.s = n, h, w, c, k, r, s
     a.stride_h, a.stride_w = stride
@@ -71,6 +73,7 @@ def wgrad_args(x=None, dy=None, dw=None, *, n, h, w, c, k, r, s, stride=(1, 1), 
     a.mode = _enum(MODES, mode, "mode")
     a.reduction = _enum(REDUCTIONS, reduction, "reduction")
     a.ctas = ctas
+    a.sk_order = _enum(SK_ORDERS, sk_order, "stream-K order")
     return a
 
 

@@ -26,6 +26,8 @@ REDUCTIONS = {"linear": RED_LINEAR, "tree": RED_TREE, "atomic": RED_ATOMIC,
               "workspace": RED_WORKSPACE, "auto": RED_AUTO}
 DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32, "e5m2": F8E5M2}
 SCALE_MODES = {"rowcol": SCALE_ROWCOL, "tensor": SCALE_TENSOR}
+SK_ORDER_AUTO, SK_ORDER_BLOCK, SK_ORDER_XCD = 0, 1, 2
+SK_ORDERS = {"auto": SK_ORDER_AUTO, "block": SK_ORDER_BLOCK, "xcd": SK_ORDER_XCD}
 TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
          "256x256x128": TILE_256x256x128, "32x64x64": TILE_32x64x64,
          "128x128x64": TILE_128x128x64, "256x128x64": TILE_256x128x64}
@@ -46,7 +48,7 @@ class skg_gemm_args_t(ctypes.Structure):
                 ("scale_a", ctypes.c_void_p), ("scale_b", ctypes.c_void_p),
                 ("tile_id", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("reduction", ctypes.c_int32), ("ctas", ctypes.c_int32),
-                ("scale_mode", ctypes.c_int32)]
+                ("scale_mode", ctypes.c_int32), ("sk_order", ctypes.c_int32)]
 
 
 class skg_wgrad_args_t(ctypes.Structure):
@@ -54,7 +56,7 @@ class skg_wgrad_args_t(ctypes.Structure):
                 ("n", "h", "w", "c", "k", "r", "s", "stride_h", "stride_w", "pad_h", "pad_w",
                  "groups", "dtype")] + \
                [("x", ctypes.c_void_p), ("dy", ctypes.c_void_p), ("dw", ctypes.c_void_p)] + \
-               [(n, ctypes.c_int32) for n in ("tile_id", "mode", "reduction", "ctas")]
+               [(n, ctypes.c_int32) for n in ("tile_id", "mode", "reduction", "ctas", "sk_order")]
 
 
 class skg_plan_t(ctypes.Structure):
@@ -64,7 +66,7 @@ class skg_plan_t(ctypes.Structure):
                  "sk_ctas", "sk_iters", "iters_per_sk_cta", "extra_iters", "grid", "max_contrib",
                  "linear_partners", "tree_rounds", "flags_bytes", "partials_bytes",
                  "workspace_bytes")] + \
-               [(n, ctypes.c_int32) for n in ("requested_mode", "slices")]
+               [(n, ctypes.c_int32) for n in ("requested_mode", "slices", "sk_order")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -93,6 +93,7 @@ KPlan to_kplan(const skg_plan_t& pl) {
   k.grid = (int)pl.grid;
   k.mode = pl.mode;
   k.reduction = pl.reduction;
+  k.sk_order = pl.sk_order == SKG_SK_ORDER_XCD ? SK_ORDER_XCD : SK_ORDER_BLOCK;
   return k;
 }
 
@@ -185,7 +186,8 @@ int skg_plan_gemm(const skg_gemm_args_t* a, skg_plan_t* out) {
       rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
       if (rc) return rc;
     }
-    return plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+    return plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
+                       resolve_sk_order(a->sk_order, false), cus, per_cu, out);
   } catch (...) {
     return hip_failure("exception in skg_plan_gemm");
   }
@@ -203,7 +205,8 @@ int skg_plan_wgrad(const skg_wgrad_args_t* a, skg_plan_t* out) {
       rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
       if (rc) return rc;
     }
-    return plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, out);
+    return plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
+                       resolve_sk_order(a->sk_order, true), cus, per_cu, out);
   } catch (...) {
     return hip_failure("exception in skg_plan_wgrad");
   }
@@ -226,7 +229,8 @@ int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stre
     rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);
     if (rc) return rc;
     skg_plan_t pl;
-    rc = plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    rc = plan_launch(gemm_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
+                     resolve_sk_order(a->sk_order, false), cus, per_cu, &pl);
     if (rc) return rc;
     rc = check_run(pl, ws, ws_bytes, cus, per_cu);
     if (rc) return rc;
@@ -275,7 +279,8 @@ int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* st
     rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
     if (rc) return rc;
     skg_plan_t pl;
-    rc = plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas, cus, per_cu, &pl);
+    rc = plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
+                     resolve_sk_order(a->sk_order, true), cus, per_cu, &pl);
     if (rc) return rc;
     rc = check_run(pl, ws, ws_bytes, cus, per_cu);
     if (rc) return rc;

@@ -129,8 +129,13 @@ static int resolve_launch(const GemmShape& g, int& mode, int& reduction, int& ct
   return SKG_OK;
 }
 
+int resolve_sk_order(int requested, bool wgrad) {
+  if (requested != SKG_SK_ORDER_AUTO) return requested;
+  return wgrad ? SKG_SK_ORDER_XCD : SKG_SK_ORDER_BLOCK;
+}
+
 int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, int ctas,
-                int num_cus, int resident_per_cu, skg_plan_t* out) {
+                int sk_order, int num_cus, int resident_per_cu, skg_plan_t* out) {
   const int requested = mode;
   int slices = 1;
   int rc = resolve_launch(g, mode, reduction, ctas, num_cus, resident_per_cu, slices);
@@ -139,6 +144,7 @@ int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, 
   if (rc) return rc;
   out->requested_mode = requested;
   out->slices = slices;
+  out->sk_order = sk_order;
   return SKG_OK;
 }
 
@@ -271,6 +277,8 @@ int validate_gemm(const skg_gemm_args_t* a) {
     return unsupported("unsupported A/B dtype");
   if (a->scale_mode != SKG_SCALE_ROWCOL && a->scale_mode != SKG_SCALE_TENSOR)
     return unsupported("unknown scale mode");
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+    return unsupported("unknown stream-K CTA order");
   if (a->dtype_c != SKG_F16 && a->dtype_c != SKG_BF16 && a->dtype_c != SKG_F32)
     return unsupported("unsupported C dtype");
   if (!(t->gemm_mask & (1 << a->dtype_ab))) return unsupported("tile has no GEMM instance for this A/B dtype");
@@ -295,6 +303,8 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
   const TileDesc* t = tile_desc(a->tile_id);
   if (!t) return unsupported("unknown tile id");
   if (a->dtype != SKG_F16 && a->dtype != SKG_BF16) return unsupported("unsupported wgrad dtype");
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+    return unsupported("unknown stream-K CTA order");
   if (!(t->wgrad_mask & (1 << a->dtype))) return unsupported("tile has no wgrad instance for this dtype");
   int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);
   if (rc) return rc;

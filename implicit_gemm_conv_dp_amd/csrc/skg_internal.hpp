@@ -37,9 +37,12 @@ struct GemmShape {
 // resident_per_cu are only read when ctas == -1.
 int make_plan(const GemmShape& g, const TileDesc& t, int mode, int reduction,
               int ctas, int num_cus, int resident_per_cu, skg_plan_t* out);
-// make_plan after resolving SKG_MODE_AUTO / SKG_MODE_SPLITK / SKG_RED_AUTO.
+// make_plan after resolving SKG_MODE_AUTO / SKG_MODE_SPLITK / SKG_RED_AUTO;
+// sk_order is already resolved (resolve_sk_order) and copied into the plan.
 int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction,
-                int ctas, int num_cus, int resident_per_cu, skg_plan_t* out);
+                int ctas, int sk_order, int num_cus, int resident_per_cu, skg_plan_t* out);
+// SKG_SK_ORDER_AUTO -> XCD for wgrad, BLOCK for GEMM; others unchanged.
+int resolve_sk_order(int requested, bool wgrad);
 
 // Argument checks that need no device (a0 of the hot path).
 int validate_gemm(const skg_gemm_args_t* a);

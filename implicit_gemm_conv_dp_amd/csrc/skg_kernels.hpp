@@ -25,10 +25,13 @@ namespace skg {
 
 // ---------------------------------------------------------------------------
 // Plan as the kernels see it (32-bit; the host checks the ranges).
+enum { SK_ORDER_BLOCK = 0, SK_ORDER_XCD = 1 };
+
 struct KPlan {
   int tiles_m, tiles_n, ipt;
   int dp_tiles, sk_tiles, sk_ctas, ipc, extra;
   int grid, mode, reduction;
+  int sk_order;  // SK_ORDER_BLOCK or SK_ORDER_XCD
 };
 
 // The caller's workspace, carved up on the host.
@@ -1461,7 +1464,15 @@ struct Engine {
   SKG_DEV void run() {
     const int blk = blockIdx.x;
     const bool sk_block = p.mode != MODE_DP && blk < p.sk_ctas;
-    const int b = blk;  // stream-K CTA index (block order)
+    // Stream-K CTA index.  XCD order: blocks are dealt to the 8 XCDs round
+    // robin (block blk to XCD blk % 8), so give XCD x the contiguous run of
+    // CTAs [x*q + min(x, r), ...) of its q or q + 1 blocks: CTAs that share
+    // a tile, and neighbouring tiles, then share one L2.
+    int b = blk;
+    if (sk_block && p.sk_order == SK_ORDER_XCD) {
+      const int q = p.sk_ctas >> 3, r = p.sk_ctas & 7, x = blk & 7;
+      b = x * q + min(x, r) + (blk >> 3);
+    }
     int it = 0, end = 0;
     if (sk_block) {
       it = b * p.ipc + min(b, p.extra);

@@ -127,6 +127,28 @@ enum skg_reduction {
                        occupancy-sized pool (same commit as SKG_MODE_AUTO) */
 };
 
+/* Which stream-K CTA each block runs (the dispatch order of the partition's
+ * CTAs; the partition itself is the same).  Workgroups go to the 8 XCDs of
+ * gfx950 round robin, block i to XCD i mod 8, and each XCD has its own L2.
+ *   SKG_SK_ORDER_AUTO   XCD for wgrad, BLOCK for GEMM (measured: wgrad's
+ *                       neighbouring stream-K CTAs read the same operand
+ *                       lines, GEMM's do not);
+ *   SKG_SK_ORDER_BLOCK  block b runs stream-K CTA b;
+ *   SKG_SK_ORDER_XCD    the stream-K CTAs are dealt to the XCDs in contiguous
+ *                       runs: block b runs CTA x*q + min(x, r) + b/8 with
+ *                       x = b mod 8, q = sk_ctas / 8, r = sk_ctas mod 8, so
+ *                       that CTAs sharing a tile, and neighbouring tiles,
+ *                       share one L2.
+ * The chiplet swizzle the pages reject with stream-K (PR #13151,
+ * Constraints) remaps tiles; this remaps only whole stream-K ranges.
+ * Waits still target higher CTA ids and all stream-K CTAs are co-resident,
+ * so every wait ends in either order. */
+enum skg_sk_order {
+  SKG_SK_ORDER_AUTO = 0,
+  SKG_SK_ORDER_BLOCK = 1,
+  SKG_SK_ORDER_XCD = 2
+};
+
 /* Compiled tile instances.  TM x TN x TK in elements; each instance exists
  * for the operations and input types skg_tile_info reports. */
 enum skg_tile {
@@ -176,6 +198,7 @@ typedef struct skg_gemm_args {
   int32_t ctas;            /* stream-K pool (split-K: slices per tile); -1 = default;
                               0 or < -1 rejected */
   int32_t scale_mode;      /* enum skg_scale_mode */
+  int32_t sk_order;        /* enum skg_sk_order */
 } skg_gemm_args_t;
 
 /* wgrad problem (PR #13151, Motivation and Technical Details).  X is the
@@ -193,6 +216,7 @@ typedef struct skg_wgrad_args {
   const void* dy;
   float* dw;
   int32_t tile_id, mode, reduction, ctas;
+  int32_t sk_order;        /* enum skg_sk_order */
 } skg_wgrad_args_t;
 
 /* Resolved launch plan, returned by value so that no derived quantity is
@@ -217,6 +241,7 @@ typedef struct skg_plan {
   int64_t workspace_bytes;   /* bytes the caller must pass as ws */
   int32_t requested_mode;    /* the mode asked for; `mode` is what runs */
   int32_t slices;            /* split-K slices per tile (1 unless split-K) */
+  int32_t sk_order;          /* SKG_SK_ORDER_BLOCK or SKG_SK_ORDER_XCD */
 } skg_plan_t;
 
 /* Reason for the last non-zero status on this thread ("" if none).  The

@@ -283,3 +283,29 @@ def test_e5m2_workload_shape_sampled():
     ref = np.array([gemm_entry("e5m2", A, B, int(m), int(c), K, scale_a=sa, scale_b=sb,
                                scale_mode="tensor") for m, c in zip(ms, ns)])
     assert rel_err(Y[ms, ns], ref) <= TOL["e5m2"]
+
+
+@pytest.mark.parametrize("tile,fmt", [("128x128x32", "f16"), ("256x256x64", "bf16"),
+                                      ("256x256x128", "e4m3")])
+def test_xcd_sk_order_integer_exact(tile, fmt):
+    # Stream-K CTAs dealt to the XCDs in contiguous runs (not the GEMM
+    # default): same results bit for bit, every mode and fix-up, pools that
+    # are and are not multiples of 8.
+    M, N, K = shape_for(tile, True)
+    A = synth.integer_codes(fmt, M * K, 91, 0.15)
+    B = synth.integer_codes(fmt, N * K, 92, 0.15)
+    sa, sb = synth.pow2_scales(M, 93), synth.pow2_scales(N, 94)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
+    for mode in ("dp_sk", "persistent"):
+        for red in REDS:
+            for ctas in (8, 13, 16):
+                dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+                dC = out_buffer("f32", M * N)
+                plan = skg.gemm(dA, dB, dC, to_dev_f32(sa), to_dev_f32(sb), M=M, N=N, K=K,
+                                dtype_ab=fmt, dtype_c="f32", tile=tile, mode=mode, reduction=red,
+                                ctas=ctas, sk_order="xcd")
+                torch.cuda.synchronize()
+                assert plan["sk_order"] == skg.SK_ORDERS["xcd"]
+                Y = decode_out(dC, "f32").reshape(M, N)
+                assert np.array_equal(Y, R), "%s %s %s %s ctas=%d xcd order" % (tile, fmt, mode,
+                                                                                red, ctas)

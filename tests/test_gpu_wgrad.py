@@ -32,13 +32,13 @@ SHAPES = {
 TILES = ["128x128x32", "32x64x64", "128x128x64", "256x128x64", "256x256x64"]
 
 
-def run(x, dy, shape, fmt, tile, mode, red, ctas, ws=None):
+def run(x, dy, shape, fmt, tile, mode, red, ctas, ws=None, sk_order="auto"):
     n, h, w, c, k, r, s, st, pd, g = shape
     dx, ddy = to_dev(x, fmt), to_dev(dy, fmt)
     dw = out_buffer("f32", k * r * s * (c // g))
     plan = skg.wgrad(dx, ddy, dw.view(torch.float32), workspace=ws,
                      n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st, pad=pd, groups=g, dtype=fmt,
-                     tile=tile, mode=mode, reduction=red, ctas=ctas)
+                     tile=tile, mode=mode, reduction=red, ctas=ctas, sk_order=sk_order)
     torch.cuda.synchronize()
     return decode_out(dw, "f32").reshape(k, -1), plan
 
@@ -130,3 +130,17 @@ def test_workload_auto_and_split_k_full_size(mode):
         assert plan["slices"] > 1 and plan["dp_tiles"] == 0
     assert plan["reduction"] == skg.REDUCTIONS["workspace"]
     assert_close(Y, R, wl.dtype, "%s %s" % (wl.name, mode))
+
+
+@pytest.mark.parametrize("tile", ["32x64x64", "256x128x64"])
+@pytest.mark.parametrize("name", ["grouped", "wide"])
+def test_block_sk_order_integer_exact(name, tile):
+    # Stream-K CTAs in block order (not the wgrad default): bit-exact too.
+    shape = SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 95)
+    for mode in ("dp_sk", "persistent"):
+        for red in REDS:
+            for ctas in (7, 16):
+                Y, plan = run(x, dy, shape, "bf16", tile, mode, red, ctas, sk_order="block")
+                assert plan["sk_order"] == skg.SK_ORDERS["block"]
+                assert np.array_equal(Y, R), "%s %s %s %s block order" % (name, tile, mode, red)

@@ -294,3 +294,32 @@ def test_flag_ordering_in_isa():
             polls = [x for x in ins if x.startswith("global_load_dword ") and x.endswith("sc1")]
             assert polls, name + ": no device-scope poll"
     assert n_kernels >= 40 and n_atomic == n_kernels // 2
+
+
+def test_sk_order_resolution_and_rejection():
+    g = dict(M=600, N=400, K=4096, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
+             mode="dp_sk", reduction="tree", ctas=13)
+    assert skg.plan_gemm(**g)["sk_order"] == _lib.SK_ORDER_BLOCK
+    assert skg.plan_gemm(sk_order="xcd", **g)["sk_order"] == _lib.SK_ORDER_XCD
+    w = dict(n=2, h=9, w=9, c=16, k=24, r=3, s=3, stride=(1, 1), pad=(1, 1), groups=1,
+             dtype="bf16", tile="128x128x64", mode="dp_sk", reduction="linear", ctas=8)
+    assert skg.plan_wgrad(**w)["sk_order"] == _lib.SK_ORDER_XCD
+    assert skg.plan_wgrad(sk_order="block", **w)["sk_order"] == _lib.SK_ORDER_BLOCK
+    # the order changes no field of the partition
+    a, b = skg.plan_gemm(**g), skg.plan_gemm(sk_order="xcd", **g)
+    assert all(a[f] == b[f] for f in FIELDS)
+    assert "order" in rejected(skg.plan_gemm, sk_order=3, **g)
+    assert "order" in rejected(skg.plan_wgrad, sk_order=-1, **w)
+
+
+def test_xcd_order_is_a_permutation_into_contiguous_runs():
+    # The block -> stream-K CTA map documented for SKG_SK_ORDER_XCD: every
+    # CTA runs exactly once, and the CTAs of one XCD (blocks b with the same
+    # b mod 8) form one contiguous run, in block order.
+    for S in list(range(1, 70)) + [255, 256, 257, 480, 1216]:
+        q, r = S // 8, S % 8
+        m = [(b % 8) * q + min(b % 8, r) + b // 8 for b in range(S)]
+        assert sorted(m) == list(range(S)), S
+        for x in range(8):
+            run = [m[b] for b in range(x, S, 8)]
+            assert run == list(range(run[0], run[0] + len(run))) if run else True, (S, x)
