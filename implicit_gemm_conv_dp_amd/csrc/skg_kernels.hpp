@@ -120,6 +120,9 @@ struct TileCfg {
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
   static constexpr bool SPREAD = TM == 256 && TN == 256;
+  // Rolling A fragments in the spread pipeline (fewer live fragment
+  // registers; see Engine::grp_iter_roll).
+  static constexpr bool ROLL = SPREAD;
   // Resident CTAs per CU the register allocation must allow: tiles of up
   // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
   static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
@@ -1003,6 +1006,100 @@ struct Engine {
     mma_dma<Cfg::FM / 2, Cfg::FM, 0, 0>(fa[CB], fb[CB], ld, rf);
   }
 
+  // One A (IS_A) or B fragment `idx` of k-step ks from a grouped GEMM slot.
+  template <bool IS_A>
+  SKG_DEV Frag one_frag(const SKG_LDS char* st, int idx, int ks) const {
+    const int lrow = lane % Cfg::MN, lk = (lane / Cfg::MN) * Cfg::Op::OPB;
+    const int chunk0 = (ks * Cfg::Op::KB + lk) >> 4;
+    const int r0 = (IS_A ? wm * Cfg::WTM : wn * Cfg::WTN) + lrow;
+    const uint32_t o0 = lds_off<Cfg::RB>(r0, chunk0), o1 = lds_off<Cfg::RB>(r0, chunk0 + Cfg::OPC - 1);
+    return frag_from<Frag>(st + o0 + idx * Cfg::MN * Cfg::RB, st + o1 + idx * Cfg::MN * Cfg::RB);
+  }
+
+  // Rolling-fragment variant of grp_iter_spread.  The MFMAs of a k-step run
+  // row by row (one A fragment each); a row's A fragment is dead once its
+  // row is issued, so the next k-step's A fragment of that row is read into
+  // the same registers during the following row.  Only B is double
+  // buffered: FM + 2 FN fragments are live instead of 2 (FM + FN).
+  // Reads per row region (ks, f):
+  //   f == 0:           A(ks, FM-1), which the previous region freed;
+  //   ks < KL, f >= 1:  A(ks+1, f-1);  ks < KL, any f:  B(ks+1) spread;
+  //   ks == KL:         the next iteration's k-step 0, after the barrier
+  //                     that sits before row H = FM/2: A(0, 0..H-1) at row
+  //                     H, A(0, f-1) at row f > H, B(0) spread over H..FM-1.
+  // The refill DMAs of k-step ks are spread over its rows (over the rows
+  // before the barrier in the last k-step), as in grp_iter_spread.
+  template <bool LAST, bool DMA>
+  SKG_DEV void grp_iter_roll(FragA& fa, FragB (&fb)[2], const Loader& ld, int i, int G) {
+    static_assert(Cfg::NSLOT % 2 == 1, "the first refilled group is a B group");
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, H = FM / 2, KL = Cfg::KSTEPS - 1;
+    constexpr int NDMA = DMA ? Loader::UA + Loader::UB : 0;
+    constexpr int PER = NDMA / Cfg::KSTEPS;  // DMA instructions per k-step
+    static_assert(NDMA % Cfg::KSTEPS == 0 && PER % FM == 0 && FN % FM == 0 && FN % H == 0,
+                  "rolling schedule");
+    typename Loader::Refill rf;
+    if constexpr (DMA) {
+      const int jb = 2 * i - 2 + Cfg::NSLOT, ja = jb + 1;
+      rf.slot_b = slot(jb);
+      rf.slot_a = slot(ja);
+      rf.it_b = iter(jb >> 1);
+      rf.it_a = iter(ja >> 1);
+      rf.live_b = jb < G;
+      rf.live_a = ja < G;
+    }
+    const SKG_LDS char* sa = slot(2 * i);
+    const SKG_LDS char* sb = slot(2 * i + 1);
+    const SKG_LDS char* na = slot(2 * i + 2);
+    const SKG_LDS char* nb = slot(2 * i + 3);
+    static_for<0, Cfg::KSTEPS>([&](auto ks_) {
+      constexpr int ks = decltype(ks_)::value, CB = ks & 1, NB = CB ^ 1;
+      static_for<0, FM>([&](auto f_) {
+        constexpr int f = decltype(f_)::value;
+        constexpr bool last_step = ks == KL;
+        constexpr int RD = !last_step ? PER / FM : (f < H ? PER / H : 0);
+        constexpr int D0 = ks * PER + (!last_step ? f * (PER / FM) : (f < H ? f * (PER / H) : 0));
+        if constexpr (last_step && f == H && !LAST) {
+          // Groups 2i+2 and 2i+3 (iteration i+1) have landed once only the
+          // A group refilled last is younger.
+          wait_vm<Loader::UA>();
+          lds_barrier();
+        }
+        mma_dma<f, f + 1, D0, D0 + RD>(fa, fb[CB], ld, rf);
+        if constexpr (f == 0) {
+          fa[FM - 1] = one_frag<true>(sa, FM - 1, ks);
+        }
+        if constexpr (!last_step) {
+          if constexpr (f >= 1) {
+            fa[f - 1] = one_frag<true>(sa, f - 1, ks + 1);
+            }
+          static_for<f * (FN / FM), (f + 1) * (FN / FM)>([&](auto g_) {
+            constexpr int g = decltype(g_)::value;
+            fb[NB][g] = one_frag<false>(sb, g, ks + 1);
+          });
+        } else if constexpr (!LAST && f >= H) {
+          if constexpr (f == H) {
+            static_for<0, H>([&](auto r_) {
+              constexpr int r = decltype(r_)::value;
+              fa[r] = one_frag<true>(na, r, 0);
+            });
+          } else {
+            fa[f - 1] = one_frag<true>(na, f - 1, 0);
+            }
+          static_for<(f - H) * (FN / H), (f - H + 1) * (FN / H)>([&](auto g_) {
+            constexpr int g = decltype(g_)::value;
+            fb[NB][g] = one_frag<false>(nb, g, 0);
+          });
+        }
+        // Alternate the row's MFMAs with its LDS reads.
+        static_for<0, FN>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, Cfg::OPC, 0);  // one fragment's reads
+        });
+        __builtin_amdgcn_sched_barrier(0);  // one row per scheduling region
+      });
+    });
+  }
+
   // Burst variant: at the end of iteration i the two slots it used are
   // refilled right after the barrier with groups 2i+NSLOT and 2i+NSLOT+1.
   template <bool LAST>
@@ -1042,7 +1139,33 @@ struct Engine {
     FragB fb[2];
     // The wgrad refills compute an im2col address per row, which does not
     // fit between the MFMAs next to 256 accumulators: they take the burst.
-    if constexpr (Cfg::SPREAD && !Loader::kTrans) {
+    if constexpr (Cfg::SPREAD && !Loader::kTrans && Cfg::ROLL) {
+      // Prologue as below; k-step 0's A fragments but the last (which the
+      // first row region reads) and its B fragments.
+      static_for<0, Cfg::NSLOT>([&](auto j_) {
+        constexpr int j = decltype(j_)::value;
+        ld.issue_live(j, iter(j >> 1), slot(j), j < G);
+      });
+      wait_groups(Cfg::NSLOT - 2);
+      lds_barrier();
+      FragA ra;
+      static_for<0, Cfg::FM - 1>([&](auto r_) {
+        constexpr int r = decltype(r_)::value;
+        ra[r] = one_frag<true>(slot(0), r, 0);
+      });
+      static_for<0, Cfg::FN>([&](auto g_) {
+        constexpr int g = decltype(g_)::value;
+        fb[0][g] = one_frag<false>(slot(1), g, 0);
+      });
+      if (I == 1) {
+        grp_iter_roll<true, false>(ra, fb, ld, 0, G);
+      } else {
+        grp_iter_roll<false, false>(ra, fb, ld, 0, G);
+        for (int i = 1; i + 1 < I; ++i) grp_iter_roll<false, true>(ra, fb, ld, i, G);
+        grp_iter_roll<true, false>(ra, fb, ld, I - 1, G);
+      }
+      wait_vm<0>();  // zero-fill loads of groups past the segment
+    } else if constexpr (Cfg::SPREAD && !Loader::kTrans) {
       // Prologue: all NSLOT slots; groups past the segment only zero-fill.
       static_for<0, Cfg::NSLOT>([&](auto j_) {
         constexpr int j = decltype(j_)::value;
@@ -1106,26 +1229,77 @@ struct Engine {
     SKG_DEV int partner(int k) const { return tree ? cta + (1 << k) : cta + 1 + k; }
   };
 
-  // Partial tile of stream-K CTA c: fp32, tile order [row][TN].
+  // Partial tile of stream-K CTA c: TM x TN fp32 in register order.  Wave
+  // w's accumulators fill bytes [w * WBYTES, (w + 1) * WBYTES); float4 j of
+  // lane l (the order of acc[f][g][4q .. 4q+3], j = (f * FN + g) * NACC/4 + q)
+  // lies at (j * 64 + l) * 16.  Producer and consumer of a (CTA, wave) flag
+  // hold the same fragments, so a wave folds its partner's wave straight into
+  // its registers, and every wave-instruction moves 1 KiB contiguous.
+  static constexpr int PSLOTS = Cfg::FM * Cfg::FN * Cfg::NACC / 4;  // float4 per lane
+  static constexpr uint32_t WBYTES = PSLOTS * 64 * 16;
+  static_assert(WBYTES * Cfg::NW == Cfg::TM * Cfg::TN * 4, "register-order partial");
   SKG_DEV float* partial(int c) const { return s.partials + (size_t)c * Cfg::TM * Cfg::TN; }
   SKG_DEV __amdgpu_buffer_rsrc_t partial_rsrc(int c) const {
     return make_rsrc(partial(c), Cfg::TM * Cfg::TN * 4);
   }
+  // Byte offset of this lane's float4 0 in its wave's block; float4 j adds
+  // the wave-uniform j * 1024.
+  SKG_DEV uint32_t part_base() const { return wave * WBYTES + (uint32_t)lane * 16; }
+
+  // OUT_PUBLISH: this wave's accumulators go out as the CTA's partial, then
+  // the wave's flag is set once its stores have completed.
+  SKG_DEV void publish_regs(int cta) const {
+    const __amdgpu_buffer_rsrc_t q = partial_rsrc(cta);
+    const uint32_t base = part_base();
+    static_for<0, PSLOTS>([&](auto j_) {
+      constexpr int j = decltype(j_)::value;
+      constexpr int f = j / (Cfg::FN * (Cfg::NACC / 4)), g = (j / (Cfg::NACC / 4)) % Cfg::FN;
+      constexpr int e = 4 * (j % (Cfg::NACC / 4));
+      store_dev16_s(q, base, j * 1024, f32x4{acc[f][g][e], acc[f][g][e + 1], acc[f][g][e + 2], acc[f][g][e + 3]});
+    });
+    flag_publish(s.flags + cta * Cfg::NW + wave);
+  }
+
+  // Adds the fold partners' partials into the accumulators, partner by
+  // partner in the order Fix::partner gives.  Each wave waits only for the
+  // flag of its own wave in the partner CTA.  The loads of a batch are all
+  // issued before its first add, so one memory round trip covers FB float4
+  // per lane.
+  SKG_DEV void fold_regs(const Fix& fx) {
+    constexpr int FB = PSLOTS < 32 ? PSLOTS : 32;
+    static_assert(PSLOTS % FB == 0, "fold batches");
+    for (int k = 0; k < fx.nfold; ++k) {
+      const int c = fx.partner(k);
+      flag_wait(s.flags + c * Cfg::NW + wave);
+      const __amdgpu_buffer_rsrc_t q = partial_rsrc(c);
+      const uint32_t base = part_base();
+      static_for<0, PSLOTS / FB>([&](auto b_) {
+        constexpr int b = decltype(b_)::value;
+        f32x4 t[FB];
+        static_for<0, FB>([&](auto i_) {
+          constexpr int i = decltype(i_)::value;
+          t[i] = load_dev16_s(q, base, (b * FB + i) * 1024);
+        });
+        static_for<0, FB>([&](auto i_) {
+          constexpr int i = decltype(i_)::value, j = b * FB + i;
+          constexpr int f = j / (Cfg::FN * (Cfg::NACC / 4)), g = (j / (Cfg::NACC / 4)) % Cfg::FN;
+          constexpr int e = 4 * (j % (Cfg::NACC / 4));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[f][g][e + u] = add_in_agpr(acc[f][g][e + u], t[i][u]);
+        });
+      });
+    }
+  }
 
   // Writes the accumulator tile out, one wave-row (WTM rows) at a time: the
   // owning waves stage it in LDS as fp32, then every thread takes a fixed
-  // 8-column chunk of the staged rows, adds the partners' partials and
+  // 8-column chunk of the staged rows and
   //   OUT_STORE:     C = cvt((v * sa[row]) * sb[col]), round to nearest even;
   //   OUT_ATOMIC:    fp32 atomic add of (v * sa[row]) * sb[col] into C;
   //   OUT_WORKSPACE: fp32 atomic add of v into the tile's scratch wsp;
-  //   OUT_PUBLISH:   stores v as this CTA's partial.
   // (Full tiles take the two atomic forms through atomic_full, one column
-  // per lane.)
-  // A wave reads and writes partials only in the rows its threads own (the
-  // same rows in every CTA), so one flag per (CTA, wave) orders each
-  // hand-off: the producer's wave w releases its flag after its last partial
-  // store; the consumer's wave w acquires that flag before its first partial
-  // load.
+  // per lane.)  Partials never pass through here: publish_regs and fold_regs
+  // move them between registers and memory before the copy-out.
   static constexpr int VC = 8;                      // columns per thread chunk
   static constexpr int CPRO = Cfg::TN / VC;         // chunks per row
   static constexpr int RSTEP = Cfg::THREADS / CPRO; // rows between a thread's rows
@@ -1140,54 +1314,10 @@ struct Engine {
     return Row{*(const SKG_LDS f32x4*)p, *(const SKG_LDS f32x4*)(p + 16)};
   }
 
-  SKG_DEV void add_partials(Row& r, const Fix& fx, int tofs) const {
-    for (int k = 0; k < fx.nfold; ++k) {
-      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
-      r.v0 += load_dev16(q, tofs * 4);
-      r.v1 += load_dev16(q, tofs * 4 + 16);
-    }
-  }
-
-  // Adds the fold partners' partials into this thread's rows of the staged
-  // wave-row (full tiles).  Per partner every load of the thread is issued
-  // before the first add, so one memory round trip covers all its rows
-  // (the partials come from device scope, far from the CU).  Partners are
-  // added in the order Fix::partner gives, as add_partials does.
-  SKG_DEV void fold_staged(const Fix& fx, int pass, int col) const {
-    const int lr0 = tid / CPRO;
-    if (RSTEP > Cfg::WTM && lr0 >= Cfg::WTM) return;  // fewer rows than threads
-    constexpr int CH = NR < 8 ? NR : 8;  // rows in flight per round trip
-    static_assert(NR % CH == 0, "fold chunks");
-    for (int k = 0; k < fx.nfold; ++k) {
-      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.partner(k));
-#pragma unroll 1
-      for (int i0 = 0; i0 < NR; i0 += CH) {
-        f32x4 t[CH][2];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const uint32_t off = ((pass * Cfg::WTM + lr0 + (i0 + i) * RSTEP) * Cfg::TN + col) * 4;
-          t[i][0] = load_dev16(q, off);
-          t[i][1] = load_dev16(q, off + 16);
-        }
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          SKG_LDS f32x4* d =
-              (SKG_LDS f32x4*)(lds + (lr0 + (i0 + i) * RSTEP) * Cfg::EPI_PITCH32 + col * 4);
-          d[0] += t[i][0];
-          d[1] += t[i][1];
-        }
-      }
-    }
-  }
-
   template <int HOW, int DTC>
   SKG_DEV void emit_full(const Row& r, const OutTile& o, const Fix& fx, float* wsp, int row, int col,
                          int tofs, float sa, const f32x4& sb0, const f32x4& sb1) const {
-    if constexpr (HOW == OUT_PUBLISH) {
-      const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
-      store_dev16(q, tofs * 4, r.v0);
-      store_dev16(q, tofs * 4 + 16, r.v1);
-    } else {
+    {
       static_assert(HOW == OUT_STORE, "atomic fix-ups copy out through atomic_full");
       const f32x4 w0 = (r.v0 * sa) * sb0, w1 = (r.v1 * sa) * sb1;
       const size_t idx = (size_t)row * o.ld + col;
@@ -1224,8 +1354,7 @@ struct Engine {
       const int lr = lr0 + i * RSTEP, row = pass * Cfg::WTM + lr;
       Row r = staged(lr, col);
       const int tofs = row * Cfg::TN + col;
-      if constexpr (FIX == FIX_HANDOFF) add_partials(r, fx, tofs);
-      const float sa = HOW == OUT_STORE && o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
+      const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
       emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sa, sb0, sb1);
     }
   }
@@ -1270,24 +1399,15 @@ struct Engine {
       if (row >= o.rows) break;
       Row r = staged(lr, col);
       const int tofs = row * Cfg::TN + col;
-      if constexpr (FIX == FIX_HANDOFF) add_partials(r, fx, tofs);
       float v[VC];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[e] = r.v0[e];
         v[4 + e] = r.v1[e];
       }
-      if constexpr (FIX == FIX_HANDOFF) {
-        if (fx.how == OUT_PUBLISH) {
-          const __amdgpu_buffer_rsrc_t q = partial_rsrc(fx.cta);
-          for (int e = 0; e < ncol; ++e) store_dev4(q, (tofs + e) * 4, v[e]);
-          continue;
-        }
-      } else {
-        if (fx.how == OUT_WORKSPACE) {
-          for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
-          continue;
-        }
+      if (FIX == FIX_ATOMIC && fx.how == OUT_WORKSPACE) {
+        for (int e = 0; e < ncol; ++e) unsafeAtomicAdd(wsp + tofs + e, v[e]);
+        continue;
       }
       const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
       const size_t idx = (size_t)row * o.ld + col;
@@ -1328,8 +1448,6 @@ struct Engine {
         }
       }
     }
-    if constexpr (FIX == FIX_HANDOFF)
-      for (int k = 0; k < fx.nfold; ++k) flag_wait(s.flags + fx.partner(k) * Cfg::NW + wave);
     const int dt = Prob::dtype_c(prm);
 #pragma unroll
     for (int pass = 0; pass < Cfg::WM; ++pass) {
@@ -1353,32 +1471,21 @@ struct Engine {
         }
       }
       __syncthreads();
-      Fix fo = fx;  // what the copy itself still has to fold
-      if constexpr (FIX == FIX_HANDOFF) {
-        if (full && fx.nfold > 0) {
-          fold_staged(fx, pass, col);
-          fo.nfold = 0;
-        }
-      }
       if (!full) {
         copy_ragged(o, fx, wsp, pass, col, sb0, sb1);
-      } else if (FIX == FIX_HANDOFF && fx.how == OUT_PUBLISH) {
-        copy_full<OUT_PUBLISH, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
       } else if (FIX == FIX_ATOMIC && fx.how == OUT_WORKSPACE) {
         atomic_full<OUT_WORKSPACE>(o, wsp, pass);
       } else if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC) {
         atomic_full<OUT_ATOMIC>(o, wsp, pass);
       } else if (dt == DT_F32) {
-        copy_full<OUT_STORE, DT_F32>(o, fo, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
       } else if (dt == DT_F16) {
-        copy_full<OUT_STORE, DT_F16>(o, fo, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1);
       } else {
-        copy_full<OUT_STORE, DT_BF16>(o, fo, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1);
       }
       __syncthreads();
     }
-    if constexpr (FIX == FIX_HANDOFF)
-      if (fx.how == OUT_PUBLISH) flag_publish(s.flags + fx.cta * Cfg::NW + wave);
   }
 
   SKG_DEV int cta_of(int it) const {
@@ -1394,6 +1501,13 @@ struct Engine {
     Prob::setup(prm, p, tile, ld, o, tid);
     mainloop(ld, k0, k1);
     const Fix fx = fixup(tile, k0, k1, cta);
+    if constexpr (FIX == FIX_HANDOFF) {
+      if (fx.nfold > 0) fold_regs(fx);
+      if (fx.how == OUT_PUBLISH) {
+        publish_regs(fx.cta);
+        return;
+      }
+    }
     write_out(o, fx, fx.how == OUT_WORKSPACE ? s.ws + (size_t)(tile - p.dp_tiles) * Cfg::TM * Cfg::TN
                                              : nullptr);
   }
