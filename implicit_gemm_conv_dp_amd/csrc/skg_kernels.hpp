@@ -1322,9 +1322,10 @@ struct Engine {
       const f32x4 w0 = (r.v0 * sa) * sb0, w1 = (r.v1 * sa) * sb1;
       const size_t idx = (size_t)row * o.ld + col;
       if constexpr (DTC == DT_F32) {
+        // C is written once and not read back here: non-temporal stores.
         f32x4* dst = (f32x4*)((float*)o.base + idx);
-        dst[0] = w0;
-        dst[1] = w1;
+        __builtin_nontemporal_store(w0, dst);
+        __builtin_nontemporal_store(w1, dst + 1);
       } else {
         i32x4 h;
 #pragma unroll
@@ -1338,7 +1339,7 @@ struct Engine {
             h[e + 2] = (int)(to_bf16_bits(b0) | ((uint32_t)to_bf16_bits(b1) << 16));
           }
         }
-        *(i32x4*)((uint16_t*)o.base + idx) = h;
+        __builtin_nontemporal_store(h, (i32x4*)((uint16_t*)o.base + idx));
       }
     }
   }
@@ -1605,21 +1606,17 @@ struct Engine {
     }
     // Stream-K iterations [it, split) run before the DP tiles and
     // [split, end) after them.  dp / dp_sk: the whole range first.
-    // persistent: first only a first segment that hands its partial on
-    // without folding anything (a tile begun by a lower CTA, and in a tree
-    // an odd position), then the DP tiles, then the segments that fold --
-    // by then the partials they fold were handed on long before, so the
-    // waits cost nothing.  A CTA only waits for first segments of higher
-    // CTAs (pure hand-offs, which never wait, or folds that wait in turn on
-    // still higher CTAs), so every wait ends.
+    // persistent: first only a first segment that continues a tile begun by
+    // a lower CTA (a non-owner: it hands its partial on, in a tree possibly
+    // after folding still higher positions), then the DP tiles, then the
+    // rest -- the owners' segments, whose partners handed on long before, so
+    // their waits cost little.  A non-owner's partners are higher positions
+    // of the same tile, i.e. first segments of higher CTAs, which run first
+    // in those CTAs; all stream-K CTAs are resident, so every wait ends.
     int split = end;
     if (p.mode == MODE_PERSISTENT) {
       split = it;
-      if (it < end && it % p.ipt != 0) {
-        const int t = it / p.ipt, seg_end = min(end, (t + 1) * p.ipt);
-        const Fix fx = fixup(p.dp_tiles + t, it - t * p.ipt, seg_end - t * p.ipt, b);
-        if (fx.nfold == 0) split = seg_end;
-      }
+      if (it < end && it % p.ipt != 0) split = min(end, (it / p.ipt + 1) * p.ipt);
     }
     while (true) {
       int tile, k0, k1, cta;
