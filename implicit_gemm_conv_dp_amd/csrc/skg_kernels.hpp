@@ -1268,9 +1268,24 @@ struct Engine {
   SKG_DEV void fold_regs(const Fix& fx) {
     constexpr int FB = PSLOTS < 32 ? PSLOTS : 32;
     static_assert(PSLOTS % FB == 0, "fold batches");
+    // One round trip reads the flags of the first MAXQ partners (usually
+    // all set by now); a partner seen unset is waited for in turn below.
+    constexpr int MAXQ = 8;
+    uint32_t fl[MAXQ];
+    static_for<0, MAXQ>([&](auto k_) {
+      constexpr int k = decltype(k_)::value;
+      const int c = fx.partner(k < fx.nfold ? k : fx.nfold - 1);
+      fl[k] = __hip_atomic_load(s.flags + c * Cfg::NW + wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+    uint32_t ready = 0;
+    static_for<0, MAXQ>([&](auto k_) {
+      constexpr int k = decltype(k_)::value;
+      if (fl[k] == 1u) ready |= 1u << k;
+    });
     for (int k = 0; k < fx.nfold; ++k) {
       const int c = fx.partner(k);
-      flag_wait(s.flags + c * Cfg::NW + wave);
+      if (k >= MAXQ || !((ready >> k) & 1u)) flag_wait(s.flags + c * Cfg::NW + wave);
+      asm volatile("" ::: "memory");  // partial loads stay after the flag check
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(c);
       const uint32_t base = part_base();
       static_for<0, PSLOTS / FB>([&](auto b_) {
