@@ -86,8 +86,10 @@ enum skg_scale_mode {
  *                       one CTA per data-parallel tile;
  *   SKG_MODE_PERSISTENT grid = the pool; each CTA runs data-parallel tiles
  *                       b, b+grid, ... and its stream-K range: a first
- *                       segment that only hands a partial on runs before
- *                       the data-parallel tiles, the segments it owns after
+ *                       segment that continues a tile begun by a lower CTA
+ *                       (it hands its partial on, in a tree possibly after
+ *                       folding higher positions) runs before the
+ *                       data-parallel tiles, the segments it owns after
  *                       them (so their folds find the partials ready). */
 enum skg_mode {
   SKG_MODE_DP = 0,
