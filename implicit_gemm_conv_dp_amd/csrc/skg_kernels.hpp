@@ -546,7 +546,8 @@ struct WgradGrpLoader {
 
   // dY row q of this thread's A chunk, or kOOB.
   SKG_DEV uint32_t a_off(int q, bool live) const {
-    return (live && a_ok && q < kred) ? (uint32_t)q * k2 + a_chan : kOOB;
+    const bool ok = live & a_ok & (q < kred);
+    return ok ? (uint32_t)q * k2 + a_chan : kOOB;
   }
   // X pixel of q shifted by this thread's filter tap, or kOOB (padding).
   SKG_DEV uint32_t b_off(int q, bool live) const {
@@ -556,8 +557,12 @@ struct WgradGrpLoader {
     const int wo = rem - (int)ho * Wo;
     const int hi = (int)ho * sh - ph + tap_r;
     const int wi = wo * sw - pw + tap_s;
-    const bool ok = live && b_ok && q < kred && hi >= 0 && hi < H && wi >= 0 && wi < W;
-    return ok ? (uint32_t)(((int)img * H + hi) * W + wi) * c2 + b_chan : kOOB;
+    // Evaluated without branches (the offset is computed either way and
+    // selected), so the compiler emits no exec-mask jumps around it.
+    const bool ok = live & b_ok & (q < kred) & (hi >= 0) & (hi < H) & (wi >= 0) & (wi < W);
+    uint32_t off = (uint32_t)(((int)img * H + hi) * W + wi) * c2 + b_chan;
+    asm volatile("" : "+v"(off));
+    return ok ? off : kOOB;
   }
 
   template <bool IS_A>
@@ -583,6 +588,27 @@ struct WgradGrpLoader {
       issue_group<false>(it, slot, live);
   }
   SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
+
+  // Offsets of one group's DMA instructions, computed ahead of the
+  // instructions themselves (among the MFMAs of the iteration before).
+  struct PreA { uint32_t off[UA]; };
+  struct PreB { uint32_t off[UB]; };
+  SKG_DEV void prep_a(int it, bool live, PreA& pr) const {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) pr.off[u] = a_off(it * Cfg::TK + rowa + u * STEPA, live);
+  }
+  SKG_DEV void prep_b(int it, bool live, PreB& pr) const {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) pr.off[u] = b_off(it * Cfg::TK + rowb + u * STEPB, live);
+  }
+  SKG_DEV void issue_a(SKG_LDS char* slot, const PreA& pr) const {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) dma16(rdy, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), pr.off[u]);
+  }
+  SKG_DEV void issue_b(SKG_LDS char* slot, const PreB& pr) const {
+#pragma unroll
+    for (int u = 0; u < UB; ++u) dma16(rx, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), pr.off[u]);
+  }
 
   struct Refill {
     SKG_LDS char* slot_b;
@@ -653,6 +679,13 @@ struct Engine {
   typedef typename Cfg::Op::frag_t Frag;
   typedef Frag FragA[Cfg::FM];
   typedef Frag FragB[Cfg::FN];
+  // Precomputed refill offsets (wgrad loaders); empty elsewhere.
+  template <class L, class = void>
+  struct PreOf { struct A {}; struct B {}; };
+  template <class L>
+  struct PreOf<L, std::void_t<typename L::PreA>> { typedef typename L::PreA A; typedef typename L::PreB B; };
+  typedef typename PreOf<Loader>::A PreAT;
+  typedef typename PreOf<Loader>::B PreBT;
 
   const Params& prm;
   const KPlan& p;
@@ -1107,9 +1140,24 @@ struct Engine {
                               int k0) {
     const SKG_LDS char* sa = slot(2 * i);
     const SKG_LDS char* sb = slot(2 * i + 1);
+    // wgrad: the im2col offsets of this iteration's refill (groups 2i+NSLOT
+    // and 2i+NSLOT+1, one A and one B group) are computed among the MFMAs of
+    // the first k-steps; after the barrier only the DMAs are left to issue.
+    // (Not with 256 accumulators per lane: the offsets would not fit beside them.)
+    constexpr bool PRE = Loader::kTrans && !LAST && Cfg::KSTEPS >= 2 && Cfg::FM * Cfg::FN * Cfg::NACC <= 128;
+    constexpr int ODD = Cfg::NSLOT % 2;  // group 2i+NSLOT is a B group when NSLOT is odd
+    const int jb = 2 * i + Cfg::NSLOT + (1 - ODD), ja = 2 * i + Cfg::NSLOT + ODD;
+    PreBT pb;
+    PreAT pa;
 #pragma unroll
     for (int ks = 0; ks + 1 < Cfg::KSTEPS; ++ks) {
       grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
+      if constexpr (PRE) {
+        // B in k-step 0, A in k-step 1 (or also 0 when that is the only
+        // k-step before the last): both are ready before the barrier.
+        if (ks == 0) ld.prep_b(iter(jb >> 1), jb < G, pb);
+        if (ks == (Cfg::KSTEPS > 2 ? 1 : 0)) ld.prep_a(iter(ja >> 1), ja < G, pa);
+      }
       mma(fa[ks & 1], fb[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
     }
@@ -1118,9 +1166,13 @@ struct Engine {
     if constexpr (!LAST) {
       wait_groups(min(G, 2 * i + Cfg::NSLOT) - (2 * i + 4));
       lds_barrier();
-      if (2 * i + Cfg::NSLOT < G) ld.issue(2 * i + Cfg::NSLOT, iter((2 * i + Cfg::NSLOT) >> 1), slot(2 * i));
-      if (2 * i + Cfg::NSLOT + 1 < G)
-        ld.issue(2 * i + Cfg::NSLOT + 1, iter((2 * i + Cfg::NSLOT + 1) >> 1), slot(2 * i + 1));
+      if constexpr (PRE) {
+        if (jb < G) ld.issue_b(slot(jb), pb);
+        if (ja < G) ld.issue_a(slot(ja), pa);
+      } else {
+        if (jb < G) ld.issue(jb, iter(jb >> 1), slot(2 * i));
+        if (ja < G) ld.issue(ja, iter(ja >> 1), slot(2 * i + 1));
+      }
       grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
     }
     mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
