@@ -110,12 +110,20 @@ struct TileCfg {
   // Grouped direct-to-LDS pipeline (128-byte rows, i.e. whole cache lines
   // per row and MAC iteration): each ring slot holds one operand tile (A or
   // B) of one MAC iteration.  Large tiles take the whole LDS; 128-row tiles
-  // stay within half of it so that two CTAs fit on a CU.
+  // stay within half of it so that two CTAs fit on a CU.  Square tiles use
+  // one ring of NSLOT equal slots; when TM != TN the A and B tiles differ in
+  // size and each gets a ring of its own, NSLOT / 2 slots sized to fit, so
+  // the LDS holds more iterations ahead.
+  static constexpr int SLOT_A = TM * RB, SLOT_B = TN * RB;
+  static constexpr bool SPLIT = TM != TN;
   static constexpr int SLOT = (TM > TN ? TM : TN) * RB;
   static constexpr int LDS_BUDGET = TM * TN >= 256 * 128 ? 160 * 1024 : 80 * 1024;
-  static constexpr int NSLOT = LDS_BUDGET / SLOT > 8 ? 8 : LDS_BUDGET / SLOT;
+  static constexpr int RING_D = LDS_BUDGET / (SLOT_A + SLOT_B);  // iterations, split rings
+  static constexpr int NSLOT = SPLIT ? (2 * RING_D > 8 ? 8 : 2 * RING_D)
+                                     : (LDS_BUDGET / SLOT > 8 ? 8 : LDS_BUDGET / SLOT);
+  static constexpr int RING_BYTES = SPLIT ? NSLOT / 2 * (SLOT_A + SLOT_B) : NSLOT * SLOT;
   static constexpr bool GROUPED = RB == 128 && NSLOT >= 4 && KSTEPS % 2 == 0;
-  static constexpr int LDS_GRP = NSLOT * SLOT > EPI_BYTES ? NSLOT * SLOT : EPI_BYTES;
+  static constexpr int LDS_GRP = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
   // Spread the refill DMAs among the MFMAs (256x256 tiles: one resident
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
@@ -866,13 +874,23 @@ struct Engine {
   }
 
   // Grouped pipeline.  Group j of the segment (A or B of MAC iteration
-  // j/2) lives in ring slot j % NSLOT.  At the end of iteration i the wave
+  // j/2) lives in ring slot j % NSLOT (split rings: A groups in slot
+  // (j/2) % (NSLOT/2) of the A ring, B groups likewise in the B ring, so
+  // group j + NSLOT again takes group j's slot).  At the end of iteration i the wave
   // waits for its own loads of iteration i+1, meets the other waves at the
   // barrier -- after which iteration i+1 is complete in LDS and nobody reads
   // iteration i's two slots any more -- refills those slots with groups
   // 2i+NSLOT and 2i+NSLOT+1 and reads the first fragments of iteration i+1,
   // all inside the last k-step's MFMAs.
-  SKG_DEV SKG_LDS char* slot(int j) const { return lds + (j % Cfg::NSLOT) * Cfg::SLOT; }
+  SKG_DEV SKG_LDS char* slot(int j) const {
+    if constexpr (Cfg::SPLIT) {
+      constexpr int D = Cfg::NSLOT / 2;
+      const int k = (j >> 1) % D;
+      return (j & 1) ? lds + D * Cfg::SLOT_A + k * Cfg::SLOT_B : lds + k * Cfg::SLOT_A;
+    } else {
+      return lds + (j % Cfg::NSLOT) * Cfg::SLOT;
+    }
+  }
 
   // Order of the MAC iterations of a wgrad segment [k0, k0+L): local step
   // i runs iteration k0 + (i + rot) % L, rot = -k0 mod L, i.e. every
@@ -1170,8 +1188,8 @@ struct Engine {
         if (jb < G) ld.issue_b(slot(jb), pb);
         if (ja < G) ld.issue_a(slot(ja), pa);
       } else {
-        if (jb < G) ld.issue(jb, iter(jb >> 1), slot(2 * i));
-        if (ja < G) ld.issue(ja, iter(ja >> 1), slot(2 * i + 1));
+        if (jb < G) ld.issue(jb, iter(jb >> 1), slot(jb));
+        if (ja < G) ld.issue(ja, iter(ja >> 1), slot(ja));
       }
       grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
     }
