@@ -87,9 +87,6 @@ constexpr int kDeviceScope = 16;  // cache-policy bits of a buffer access: sc1
 
 static __device__ uint32_t g_skg_wait_timeouts = 0;
 
-SKG_DEV void store_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, kDeviceScope);
-}
 // a + b for an accumulator that lives in an AGPR: read, add and write back
 // in place, so the register allocator keeps the accumulators in AGPRs (a
 // plain VALU add would move all of them to VGPRs, which do not hold them
@@ -101,16 +98,14 @@ SKG_DEV float add_in_agpr(float a, float b) {
                : "v"(b));
   return a;
 }
-// The same with a wave-uniform byte offset `soff` (an SGPR) added to the
-// per-lane offset, so a run of 16-byte slots shares one VGPR offset.
+// Device-scope 16-byte store / load of a partial: per-lane byte offset
+// `off` plus a wave-uniform one `soff` (an SGPR), so a run of 16-byte slots
+// shares one VGPR offset.
 SKG_DEV void store_dev16_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, soff, kDeviceScope);
 }
 SKG_DEV f32x4 load_dev16_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kDeviceScope));
-}
-SKG_DEV f32x4 load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
 }
 
 SKG_DEV void flag_publish(uint32_t* flag) {

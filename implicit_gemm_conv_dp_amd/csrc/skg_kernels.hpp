@@ -128,9 +128,6 @@ struct TileCfg {
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
   static constexpr bool SPREAD = TM == 256 && TN == 256;
-  // Rolling A fragments in the spread pipeline (fewer live fragment
-  // registers; see Engine::grp_iter_roll).
-  static constexpr bool ROLL = SPREAD;
   // Resident CTAs per CU the register allocation must allow: tiles of up
   // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
   static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
@@ -1008,55 +1005,6 @@ struct Engine {
     });
   }
 
-  // One MAC iteration i of the grouped pipeline.  DMA: refill the two slots
-  // of iteration i-1 (freed by the barrier that started iteration i) with
-  // groups 2i-2+NSLOT (B of iteration i+1+(NSLOT-5)/2) and 2i-1+NSLOT,
-  // spread over the k-steps.  Not in iteration 0 (no slot is free yet) nor
-  // in the last (nothing left to load).
-  template <bool LAST, bool DMA>
-  SKG_DEV void grp_iter_spread(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G,
-                               int k0) {
-    static_assert(Cfg::NSLOT % 2 == 1, "the first refilled group is a B group");
-    constexpr int NDMA = DMA ? Loader::UA + Loader::UB : 0;
-    constexpr int PER = NDMA / Cfg::KSTEPS;  // DMA instructions per k-step
-    static_assert(NDMA % Cfg::KSTEPS == 0, "DMA spread");
-    typename Loader::Refill rf;
-    if constexpr (DMA) {
-      const int jb = 2 * i - 2 + Cfg::NSLOT, ja = jb + 1;
-      rf.slot_b = slot(jb);
-      rf.slot_a = slot(ja);
-      rf.it_b = iter(jb >> 1);
-      rf.it_a = iter(ja >> 1);
-      rf.live_b = jb < G;
-      rf.live_a = ja < G;
-    }
-    const SKG_LDS char* sa = slot(2 * i);
-    const SKG_LDS char* sb = slot(2 * i + 1);
-    static_for<0, Cfg::KSTEPS - 1>([&](auto ks_) {
-      constexpr int ks = decltype(ks_)::value;
-      grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
-      mma_dma<0, Cfg::FM, ks * PER, (ks + 1) * PER>(fa[ks & 1], fb[ks & 1], ld, rf);
-      // Alternate MFMAs and the next k-step's LDS reads from the start of
-      // the k-step, so the reads have the rest of it to land.
-      static_for<0, 8>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      });
-      __builtin_amdgcn_sched_group_barrier(0x008, Cfg::FM * Cfg::FN - 8, 0);
-      __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
-    });
-    constexpr int KL = Cfg::KSTEPS - 1, CB = KL & 1;
-    mma_dma<0, Cfg::FM / 2, KL * PER, (KL + 1) * PER>(fa[CB], fb[CB], ld, rf);
-    if constexpr (!LAST) {
-      // Groups 2i+2 and 2i+3 (iteration i+1) have landed once only the A
-      // group refilled last is younger.
-      wait_vm<Loader::UA>();
-      lds_barrier();
-      grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
-    }
-    mma_dma<Cfg::FM / 2, Cfg::FM, 0, 0>(fa[CB], fb[CB], ld, rf);
-  }
-
   // One A (IS_A) or B fragment `idx` of k-step ks from a grouped GEMM slot.
   template <bool IS_A>
   SKG_DEV Frag one_frag(const SKG_LDS char* st, int idx, int ks) const {
@@ -1067,7 +1015,11 @@ struct Engine {
     return frag_from<Frag>(st + o0 + idx * Cfg::MN * Cfg::RB, st + o1 + idx * Cfg::MN * Cfg::RB);
   }
 
-  // Rolling-fragment variant of grp_iter_spread.  The MFMAs of a k-step run
+  // One MAC iteration i of the grouped pipeline with the refill spread among
+  // the MFMAs (256x256 GEMM tiles).  The refill of iteration i-1's two slots
+  // (groups 2i-2+NSLOT, a B group, and 2i-1+NSLOT) is spread over the
+  // k-steps; not in iteration 0 (no slot is free yet) nor in the last
+  // (nothing left to load).  Fragments roll: the MFMAs of a k-step run
   // row by row (one A fragment each); a row's A fragment is dead once its
   // row is issued, so the next k-step's A fragment of that row is read into
   // the same registers during the following row.  Only B is double
@@ -1079,7 +1031,7 @@ struct Engine {
   //                     that sits before row H = FM/2: A(0, 0..H-1) at row
   //                     H, A(0, f-1) at row f > H, B(0) spread over H..FM-1.
   // The refill DMAs of k-step ks are spread over its rows (over the rows
-  // before the barrier in the last k-step), as in grp_iter_spread.
+  // before the barrier in the last k-step).
   template <bool LAST, bool DMA>
   SKG_DEV void grp_iter_roll(FragA& fa, FragB (&fb)[2], const Loader& ld, int i, int G) {
     static_assert(Cfg::NSLOT % 2 == 1, "the first refilled group is a B group");
@@ -1209,7 +1161,7 @@ struct Engine {
     FragB fb[2];
     // The wgrad refills compute an im2col address per row, which does not
     // fit between the MFMAs next to 256 accumulators: they take the burst.
-    if constexpr (Cfg::SPREAD && !Loader::kTrans && Cfg::ROLL) {
+    if constexpr (Cfg::SPREAD && !Loader::kTrans) {
       // Prologue as below; k-step 0's A fragments but the last (which the
       // first row region reads) and its B fragments.
       static_for<0, Cfg::NSLOT>([&](auto j_) {
@@ -1233,23 +1185,6 @@ struct Engine {
         grp_iter_roll<false, false>(ra, fb, ld, 0, G);
         for (int i = 1; i + 1 < I; ++i) grp_iter_roll<false, true>(ra, fb, ld, i, G);
         grp_iter_roll<true, false>(ra, fb, ld, I - 1, G);
-      }
-      wait_vm<0>();  // zero-fill loads of groups past the segment
-    } else if constexpr (Cfg::SPREAD && !Loader::kTrans) {
-      // Prologue: all NSLOT slots; groups past the segment only zero-fill.
-      static_for<0, Cfg::NSLOT>([&](auto j_) {
-        constexpr int j = decltype(j_)::value;
-        ld.issue_live(j, iter(j >> 1), slot(j), j < G);
-      });
-      wait_groups(Cfg::NSLOT - 2);
-      lds_barrier();
-      grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
-      if (I == 1) {
-        grp_iter_spread<true, false>(fa, fb, ld, 0, G, k0);
-      } else {
-        grp_iter_spread<false, false>(fa, fb, ld, 0, G, k0);
-        for (int i = 1; i + 1 < I; ++i) grp_iter_spread<false, true>(fa, fb, ld, i, G, k0);
-        grp_iter_spread<true, false>(fa, fb, ld, I - 1, G, k0);
       }
       wait_vm<0>();  // zero-fill loads of groups past the segment
     } else {
@@ -1429,10 +1364,23 @@ struct Engine {
     }
   }
 
+  // Row scales of this thread's rows in one pass of a full tile (1 without
+  // scales), loaded before the pass stages its accumulators so that the
+  // loads are in flight during the staging and its barrier.
+  SKG_DEV void row_scales(const OutTile& o, int pass, float (&sav)[NR]) const {
+    const int lr0 = tid / CPRO;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int lr = lr0 + i * RSTEP;
+      const int row = pass * Cfg::WTM + (lr < Cfg::WTM ? lr : 0);
+      sav[i] = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
+    }
+  }
+
   // Copy-out of one pass of a full tile: no bounds checks.
   template <int HOW, int DTC>
   SKG_DEV void copy_full(const OutTile& o, const Fix& fx, float* wsp, int pass, int col,
-                         const f32x4& sb0, const f32x4& sb1) const {
+                         const f32x4& sb0, const f32x4& sb1, const float (&sav)[NR]) const {
     const int lr0 = tid / CPRO;
     if (RSTEP > Cfg::WTM && lr0 >= Cfg::WTM) return;  // fewer rows than threads
 #pragma unroll 4
@@ -1440,8 +1388,7 @@ struct Engine {
       const int lr = lr0 + i * RSTEP, row = pass * Cfg::WTM + lr;
       Row r = staged(lr, col);
       const int tofs = row * Cfg::TN + col;
-      const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
-      emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sa, sb0, sb1);
+      emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sav[i], sb0, sb1);
     }
   }
 
@@ -1537,6 +1484,8 @@ struct Engine {
     const int dt = Prob::dtype_c(prm);
 #pragma unroll
     for (int pass = 0; pass < Cfg::WM; ++pass) {
+      float sav[NR];
+      if (full && fx.how == OUT_STORE) row_scales(o, pass, sav);
       if (wm == pass) {
         // One per-lane base address; every (f, g, q) is a constant offset
         // from it (the column step of element group q is 8 or 4).
@@ -1564,11 +1513,11 @@ struct Engine {
       } else if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC) {
         atomic_full<OUT_ATOMIC>(o, wsp, pass);
       } else if (dt == DT_F32) {
-        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1, sav);
       } else if (dt == DT_F16) {
-        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1, sav);
       } else {
-        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1);
+        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1, sav);
       }
       __syncthreads();
     }
