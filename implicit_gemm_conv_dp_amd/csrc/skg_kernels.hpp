@@ -1162,8 +1162,9 @@ struct Engine {
     // The wgrad refills compute an im2col address per row, which does not
     // fit between the MFMAs next to 256 accumulators: they take the burst.
     if constexpr (Cfg::SPREAD && !Loader::kTrans) {
-      // Prologue as below; k-step 0's A fragments but the last (which the
-      // first row region reads) and its B fragments.
+      // Prologue: all NSLOT slots (groups past the segment only zero-fill),
+      // then k-step 0's A fragments but the last (which the first row region
+      // reads) and its B fragments.
       static_for<0, Cfg::NSLOT>([&](auto j_) {
         constexpr int j = decltype(j_)::value;
         ld.issue_live(j, iter(j >> 1), slot(j), j < G);
