@@ -101,7 +101,7 @@ def test_gemm_plan_equals_oracle(tile, dt):
 
 
 def test_workload_plans():
-    # 256x256x4096 fp16 over a 6-CTA pool: the survey's straddling ranges.
+    # 256x256x4096 fp16 over a 6-CTA pool: ranges that straddle tiles.
     c = skg.plan_gemm(M=256, N=256, K=4096, dtype_ab="f16", dtype_c="f16", tile="128x128x32",
                       mode="dp_sk", reduction="linear", ctas=6)
     assert (c["sk_ctas"], c["iters_per_sk_cta"], c["extra_iters"], c["max_contrib"]) == (6, 85, 2, 3)
