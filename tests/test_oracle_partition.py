@@ -179,3 +179,45 @@ def test_simulator_reports_stall_below_capacity():
     assert S.events(t, 1) == [("pub", 1)]
     assert S.events(t, 2) == [("wait", 3), ("pub", 2)]
     assert S.events(t, 3) == [("pub", 3)]
+
+
+@pytest.mark.parametrize("reduction", ["linear", "tree"])
+def test_persistent_early_segments_only_wait_on_earlier_running_segments(reduction):
+    # Persistent launches run a CTA's first segment before its DP tiles when
+    # that segment continues a tile begun by a lower CTA (a non-owner), and
+    # its other segments after them.  Every wait of such an early segment
+    # must target a segment that also runs early in its own CTA -- the first
+    # segment, in the same tile, of a higher CTA that is a non-owner too --
+    # so the early phase completes on its own and no CTA waits on work
+    # queued behind a DP tile.  The waits are derived here from the tile's
+    # contributor list (linear: none; tree: the binomial partners before the
+    # round in which the position publishes) and must also be the first
+    # events of the CTA in the dispatch model.
+    n = 0
+    for T in range(1, 14):
+        for ipt in (1, 2, 3, 5, 8, 13, 20):
+            for pool in (2, 3, 4, 5, 7, 8, 11, 16, 23):
+                p = P.plan(1, T, ipt, 32, 32, 4, "persistent", reduction, pool)
+                for b in range(p.sk_ctas):
+                    segs = p.segments(b)
+                    if not segs or segs[0][3]:       # starts its tile: not early
+                        continue
+                    contrib = p.contributors(segs[0][0] - p.dp_tiles)
+                    pos = contrib.index(b)
+                    assert pos > 0
+                    partners = []
+                    s = 1
+                    while reduction == "tree" and s < len(contrib):
+                        if pos % (2 * s) == s:
+                            break
+                        if pos + s < len(contrib):
+                            partners.append(contrib[pos + s])
+                        s *= 2
+                    expect = [("wait", c) for c in partners] + [("pub", b)]
+                    assert S.events(p, b)[:len(expect)] == expect
+                    for c in partners:
+                        cs = p.segments(c)
+                        assert c > b and cs[0][0] == segs[0][0] and not cs[0][3]
+                        n += 1
+    if reduction == "tree":
+        assert n > 100
