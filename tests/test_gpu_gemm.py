@@ -114,6 +114,26 @@ def test_plan_reaches_four_contributors():
     assert plan["max_contrib"] >= 3 and plan["tree_rounds"] >= 2
 
 
+@pytest.mark.parametrize("tile,fmt", [("128x128x32", "f16"), ("256x256x64", "bf16"),
+                                      ("256x256x128", "e4m3")])
+def test_many_contributors_integer_exact(tile, fmt):
+    # One ragged tile shared by 20 stream-K CTAs: a linear owner folds 19
+    # partners (more than the flags it checks in its first round trip), a
+    # tree folds over 5 rounds.  Bit-exact on integer-exact inputs, in both
+    # launch modes.
+    tm, tn, tk = map(int, tile.split("x"))
+    M, N, K = tm - 24, tn - 40, 40 * tk
+    A = synth.integer_codes(fmt, M * K, 31, 0.15)
+    B = synth.integer_codes(fmt, N * K, 32, 0.15)
+    R = oracle_gemm(fmt, A, B, M, N, K)
+    assert exact_in("f32", R)
+    for mode in ("dp_sk", "persistent"):
+        for red in ("linear", "tree"):
+            Y, plan = run(A, B, M, N, K, fmt, "f32", tile, mode, red, 20)
+            assert plan["sk_ctas"] == 20 and plan["max_contrib"] == 20, plan
+            assert np.array_equal(Y, R), "%s %s %s %s: not bit-exact" % (tile, fmt, mode, red)
+
+
 def test_unsupported_args_leave_output_untouched():
     M, N, K = 64, 64, 64
     A = synth.to_codes(synth.draw("uniform", M * K, 1), "f16")
