@@ -17,13 +17,15 @@ element type is ``dtype_ab`` / ``dtype_c``.  ``wgrad`` takes NHWC ``x`` and
 from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
                    skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
-                   skg_tile_info, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
+                   skg_tile_info, skg_gemm_workspace_bytes, skg_wgrad_workspace_bytes,
+                   skg_fixup_timeouts, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
 
 __all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
            "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES", "SCALE_MODES",
            "SK_ORDERS",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
-           "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events"]
+           "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events",
+           "skg_gemm_workspace_bytes", "skg_wgrad_workspace_bytes", "skg_fixup_timeouts"]
 
 
 def _enum(table, v, what):
@@ -91,10 +93,22 @@ def workspace_for(plan, device):
     return torch.empty(max(int(plan["workspace_bytes"]), 1), dtype=torch.uint8, device=device)
 
 
-def _stream_ptr(stream):
+def _launch_stream(stream):
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _run(run, args, plan, device, workspace, stream):
+    """One run call.  A workspace the call allocates itself is handed to the
+    caching allocator as used by the launch stream (record_stream), so its
+    memory is not given to another allocation before the kernel is done
+    with it, whichever stream the caller passed."""
+    s = _launch_stream(stream)
+    ws = workspace
+    if ws is None:
+        ws = workspace_for(plan, device)
+        ws.record_stream(s)
+    run(args, ws.data_ptr(), ws.numel() * ws.element_size(), s.cuda_stream)
 
 
 def gemm(A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, **kw):
@@ -102,8 +116,7 @@ def gemm(A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, **kw)
     stream).  Returns the plan (a dict)."""
     args = gemm_args(A, B, C, scale_a=scale_a, scale_b=scale_b, **kw)
     plan = skg_plan_gemm(args).as_dict()
-    ws = workspace if workspace is not None else workspace_for(plan, C.device)
-    skg_run_gemm(args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _run(skg_run_gemm, args, plan, C.device, workspace, stream)
     return plan
 
 
@@ -111,6 +124,5 @@ def wgrad(x, dy, dw, workspace=None, stream=None, **kw):
     """Enqueue dw = wgrad(x, dy) on ``stream``.  Returns the plan (a dict)."""
     args = wgrad_args(x, dy, dw, **kw)
     plan = skg_plan_wgrad(args).as_dict()
-    ws = workspace if workspace is not None else workspace_for(plan, dw.device)
-    skg_run_wgrad(args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _run(skg_run_wgrad, args, plan, dw.device, workspace, stream)
     return plan

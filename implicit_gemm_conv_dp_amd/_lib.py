@@ -87,6 +87,11 @@ EXPORTS = {
     "skg_run_wgrad": (ctypes.c_int, [ctypes.POINTER(skg_wgrad_args_t), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]),
     "skg_profile_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "skg_gemm_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(skg_gemm_args_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "skg_wgrad_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(skg_wgrad_args_t),
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "skg_fixup_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]),
 }
 
 _lib = None
@@ -169,3 +174,21 @@ def skg_run_wgrad(args, ws_ptr, ws_bytes, stream_ptr):
 
 def skg_profile_events(start_ptr, stop_ptr):
     return check(load().skg_profile_events(start_ptr, stop_ptr))
+
+
+def skg_gemm_workspace_bytes(args):
+    out = ctypes.c_size_t()
+    check(load().skg_gemm_workspace_bytes(ctypes.byref(args), ctypes.byref(out)))
+    return out.value
+
+
+def skg_wgrad_workspace_bytes(args):
+    out = ctypes.c_size_t()
+    check(load().skg_wgrad_workspace_bytes(ctypes.byref(args), ctypes.byref(out)))
+    return out.value
+
+
+def skg_fixup_timeouts(reset=False):
+    out = ctypes.c_uint32()
+    check(load().skg_fixup_timeouts(ctypes.byref(out), 1 if reset else 0))
+    return out.value

@@ -6,6 +6,7 @@
 // support, decided before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <mutex>
@@ -80,7 +81,25 @@ int device_capacity(int op, int tile_id, int dtype, int* cus, int* per_cu) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-KPlan to_kplan(const skg_plan_t& pl) {
+// Fault injection for tests of the error paths, read from the environment on
+// every run call: SKG_FAULT=launch makes the call fail with -1 where it would
+// launch the stream-K kernel (after its resets are enqueued, like a real
+// launch failure); SKG_FAULT=handoff runs the kernel with stream-K CTAs that
+// never raise their flags and a spin limit of kFaultSpin polls, so every
+// hand-off wait gives up (counted, and its tile poisoned with NaN) and the
+// kernel still ends.
+enum { INJECT_NONE = 0, INJECT_LAUNCH = 1, INJECT_HANDOFF = 2 };
+constexpr uint32_t kFaultSpin = 64;
+
+int injected_fault() {
+  const char* v = std::getenv("SKG_FAULT");
+  if (!v) return INJECT_NONE;
+  if (std::strcmp(v, "launch") == 0) return INJECT_LAUNCH;
+  if (std::strcmp(v, "handoff") == 0) return INJECT_HANDOFF;
+  return INJECT_NONE;
+}
+
+KPlan to_kplan(const skg_plan_t& pl, int inject) {
   KPlan k;
   k.tiles_m = (int)pl.tiles_m;
   k.tiles_n = (int)pl.tiles_n;
@@ -94,6 +113,8 @@ KPlan to_kplan(const skg_plan_t& pl) {
   k.mode = pl.mode;
   k.reduction = pl.reduction;
   k.sk_order = pl.sk_order == SKG_SK_ORDER_XCD ? SK_ORDER_XCD : SK_ORDER_BLOCK;
+  k.spin_limit = inject == INJECT_HANDOFF ? kFaultSpin : kSpinLimit;
+  k.fault = inject == INJECT_HANDOFF ? FAULT_NO_PUBLISH : FAULT_NONE;
   return k;
 }
 
@@ -212,6 +233,50 @@ int skg_plan_wgrad(const skg_wgrad_args_t* a, skg_plan_t* out) {
   }
 }
 
+int skg_gemm_workspace_bytes(const skg_gemm_args_t* a, size_t* out) {
+  if (!out) {
+    clear_error();
+    return unsupported("null output");
+  }
+  skg_plan_t pl;
+  const int rc = skg_plan_gemm(a, &pl);
+  if (rc) return rc;
+  *out = (size_t)pl.workspace_bytes;
+  return SKG_OK;
+}
+
+int skg_wgrad_workspace_bytes(const skg_wgrad_args_t* a, size_t* out) {
+  if (!out) {
+    clear_error();
+    return unsupported("null output");
+  }
+  skg_plan_t pl;
+  const int rc = skg_plan_wgrad(a, &pl);
+  if (rc) return rc;
+  *out = (size_t)pl.workspace_bytes;
+  return SKG_OK;
+}
+
+int skg_fixup_timeouts(uint32_t* count, int32_t reset) {
+  try {
+    clear_error();
+    if (!count) return unsupported("null output");
+    hipError_t (*const units[])(uint32_t*, bool) = {wait_timeouts_gemm_f16, wait_timeouts_gemm_bf16,
+                                                    wait_timeouts_gemm_f8, wait_timeouts_wgrad};
+    uint32_t total = 0;
+    for (auto fn : units) {
+      uint32_t c = 0;
+      const hipError_t e = fn(&c, reset != 0);
+      if (e != hipSuccess) return hip_failure(std::string("reading the wait counters: ") + hipGetErrorString(e));
+      total += c;
+    }
+    *count = total;
+    return SKG_OK;
+  } catch (...) {
+    return hip_failure("exception in skg_fixup_timeouts");
+  }
+}
+
 int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stream) {
   try {
     clear_error();
@@ -254,7 +319,9 @@ int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stre
     g.sa = a->scale_a;
     g.sb = a->scale_b;
     g.dtype_c = a->dtype_c == SKG_F32 ? DT_F32 : (a->dtype_c == SKG_F16 ? DT_F16 : DT_BF16);
-    hipError_t e = inst.launch(g, to_kplan(pl), carve(pl, ws), st, g_ev_start, g_ev_stop);
+    const int inject = injected_fault();
+    if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
+    hipError_t e = inst.launch(g, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
     if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
     return SKG_OK;
   } catch (const std::exception& ex) {
@@ -319,7 +386,9 @@ int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* st
       hipError_t e = hipMemsetAsync(a->dw, 0, (size_t)a->k * w.gemm_n * 4, st);
       if (e != hipSuccess) return hip_failure(std::string("zeroing dW: ") + hipGetErrorString(e));
     }
-    hipError_t e = inst.launch(w, to_kplan(pl), carve(pl, ws), st, g_ev_start, g_ev_stop);
+    const int inject = injected_fault();
+    if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
+    hipError_t e = inst.launch(w, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
     if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
     return SKG_OK;
   } catch (const std::exception& ex) {

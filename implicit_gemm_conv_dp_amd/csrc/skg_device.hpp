@@ -79,12 +79,20 @@ SKG_DEV void static_for(F&& f) {
 // also throw away every other CTA's cached operands.  Every lane of the
 // wave performs the store and the poll on the same flag word.
 //
-// The poll is bounded: after kSpinLimit polls (a fraction of a second) the wave gives
-// up, counts the event in g_skg_wait_timeouts and continues, so a broken plan
-// produces wrong numbers rather than a hung device.
+// The poll is bounded: after `limit` polls the wave gives up, counts the event
+// in g_skg_wait_timeouts and reports it, and the caller poisons what it was
+// about to fold with NaN, so a broken plan or a pool that is not resident
+// shows as NaN outputs (and a count the host reads with
+// skg_fixup_timeouts) rather than a hung device or silently wrong numbers.
+// The default limit, kSpinLimit, is 2^22 polls; each poll is a device-scope
+// load (a round trip past the L2) followed by a short sleep, so the bound is
+// in the order of seconds, far beyond any legitimate wait.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kDeviceScope = 16;  // cache-policy bits of a buffer access: sc1
 
+// One counter per translation unit that instantiates kernels (the library
+// is built without relocatable device code); each unit exports a host
+// accessor, and skg_fixup_timeouts sums them.
 static __device__ uint32_t g_skg_wait_timeouts = 0;
 
 // a + b for an accumulator that lives in an AGPR: read, add and write back
@@ -113,16 +121,22 @@ SKG_DEV void flag_publish(uint32_t* flag) {
   __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-SKG_DEV void flag_wait(const uint32_t* flag) {
+// Returns false when the wait gave up.
+SKG_DEV bool flag_wait(const uint32_t* flag, uint32_t limit) {
   uint32_t n = 0;
+  bool ok = true;
   while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 1u) {
     __builtin_amdgcn_s_sleep(2);
-    if (++n == kSpinLimit) {
-      __hip_atomic_fetch_add(&g_skg_wait_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (++n >= limit) {
+      // one count per wave: every lane runs this loop
+      if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(&g_skg_wait_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = false;
       break;
     }
   }
   asm volatile("" ::: "memory");  // partial loads stay after the poll
+  return ok;
 }
 
 // ---------------------------------------------------------------------------

@@ -5,4 +5,5 @@ namespace skg {
 GemmInst gemm_instance_bf16(int tile_id, bool tensor_scales) {
   return gemm_inst::by_tile<DT_BF16>(tile_id, tensor_scales);
 }
+hipError_t wait_timeouts_gemm_bf16(uint32_t* out, bool reset) { return unit_wait_timeouts(out, reset); }
 }  // namespace skg

@@ -10,4 +10,5 @@ GemmInst gemm_instance_f8(int tile_id, int dtype, bool tensor_scales) {
     return gemm_inst::make<TileCfg<DT_BF8, 256, 256, 128, 2, 2, 32, 128>>(tensor_scales);
   return {nullptr, nullptr};
 }
+hipError_t wait_timeouts_gemm_f8(uint32_t* out, bool reset) { return unit_wait_timeouts(out, reset); }
 }  // namespace skg

@@ -28,4 +28,5 @@ WgradInst wgrad_instance(int tile_id, int dtype) {
   return {nullptr, nullptr};
 }
 
+hipError_t wait_timeouts_wgrad(uint32_t* out, bool reset) { return unit_wait_timeouts(out, reset); }
 }  // namespace skg

@@ -9,12 +9,14 @@
 // tile's accumulator according to whether its segment started and/or ended the
 // tile.  Data-parallel tiles run whole.
 //
-// Mainloop: operands are staged global -> registers -> LDS (double-buffered,
-// one barrier per MAC iteration) and fed to wave64 MFMA from LDS with the
-// register prefetch of iteration i+1 in flight while iteration i computes.
-// GEMM operands are K-contiguous and copied as 16-byte chunks; wgrad operands
-// are M/N-contiguous (NHWC) and go through an 8x8 register transpose so that
-// LDS always holds K-contiguous rows.
+// Mainloop: operands go straight from global memory into a ring of LDS
+// slots with gfx950's direct-to-LDS buffer loads (one slot per operand tile of
+// a MAC iteration, or per sub-stage for 64-byte rows), several iterations
+// ahead, one CTA barrier per iteration; wave64 MFMAs read their fragments
+// from the slots.  GEMM operands are K-contiguous and read as they are; wgrad
+// operands are M/N-contiguous (NHWC) and are read with the transposing LDS
+// read.  The 128x128x32 wgrad tile keeps a register loader that transposes
+// 8x8 blocks in registers before its LDS stores.
 #pragma once
 
 #include <type_traits>
@@ -27,11 +29,18 @@ namespace skg {
 // Plan as the kernels see it (32-bit; the host checks the ranges).
 enum { SK_ORDER_BLOCK = 0, SK_ORDER_XCD = 1 };
 
+// Forced faults (set only from the host's fault-injection switch): with
+// FAULT_NO_PUBLISH the stream-K CTAs store their partials but never raise
+// their flags, so every wait on them runs into its (then small) spin limit.
+enum { FAULT_NONE = 0, FAULT_NO_PUBLISH = 1 };
+
 struct KPlan {
   int tiles_m, tiles_n, ipt;
   int dp_tiles, sk_tiles, sk_ctas, ipc, extra;
   int grid, mode, reduction;
-  int sk_order;  // SK_ORDER_BLOCK or SK_ORDER_XCD
+  int sk_order;         // SK_ORDER_BLOCK or SK_ORDER_XCD
+  uint32_t spin_limit;  // polls before a flag wait gives up
+  int fault;            // FAULT_*
 };
 
 // The caller's workspace, carved up on the host.
@@ -1263,6 +1272,10 @@ struct Engine {
       constexpr int e = 4 * (j % (Cfg::NACC / 4));
       store_dev16_s(q, base, j * 1024, f32x4{acc[f][g][e], acc[f][g][e + 1], acc[f][g][e + 2], acc[f][g][e + 3]});
     });
+    if (p.fault == FAULT_NO_PUBLISH) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
     flag_publish(s.flags + cta * Cfg::NW + wave);
   }
 
@@ -1270,7 +1283,8 @@ struct Engine {
   // partner in the order Fix::partner gives.  Each wave waits only for the
   // flag of its own wave in the partner CTA.  The loads of a batch are all
   // issued before its first add, so one memory round trip covers FB float4
-  // per lane.
+  // per lane.  If a wait gives up, that partner's values are folded as NaN
+  // (each plus a NaN), so the tile is visibly wrong rather than silently so.
   SKG_DEV void fold_regs(const Fix& fx) {
     constexpr int FB = PSLOTS < 32 ? PSLOTS : 32;
     static_assert(PSLOTS % FB == 0, "fold batches");
@@ -1290,16 +1304,19 @@ struct Engine {
     });
     for (int k = 0; k < fx.nfold; ++k) {
       const int c = fx.partner(k);
-      if (k >= MAXQ || !((ready >> k) & 1u)) flag_wait(s.flags + c * Cfg::NW + wave);
+      bool ok = true;
+      if (k >= MAXQ || !((ready >> k) & 1u)) ok = flag_wait(s.flags + c * Cfg::NW + wave, p.spin_limit);
       asm volatile("" ::: "memory");  // partial loads stay after the flag check
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(c);
       const uint32_t base = part_base();
+      // A partner whose flag never came is folded as NaN.
+      const float poison = ok ? 0.f : __builtin_nanf("");
       static_for<0, PSLOTS / FB>([&](auto b_) {
         constexpr int b = decltype(b_)::value;
         f32x4 t[FB];
         static_for<0, FB>([&](auto i_) {
           constexpr int i = decltype(i_)::value;
-          t[i] = load_dev16_s(q, base, (b * FB + i) * 1024);
+          t[i] = load_dev16_s(q, base, (b * FB + i) * 1024) + poison;
         });
         static_for<0, FB>([&](auto i_) {
           constexpr int i = decltype(i_)::value, j = b * FB + i;

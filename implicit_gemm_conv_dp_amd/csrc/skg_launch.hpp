@@ -27,6 +27,23 @@ GemmInst gemm_instance_bf16(int tile_id, bool tensor_scales);
 GemmInst gemm_instance_f8(int tile_id, int dtype, bool tensor_scales);
 WgradInst wgrad_instance(int tile_id, int dtype);
 
+// Flag-wait give-ups counted by the kernels of one instance unit (read, and
+// reset to zero when `reset`); skg_fixup_timeouts sums the units.
+hipError_t wait_timeouts_gemm_f16(uint32_t* out, bool reset);
+hipError_t wait_timeouts_gemm_bf16(uint32_t* out, bool reset);
+hipError_t wait_timeouts_gemm_f8(uint32_t* out, bool reset);
+hipError_t wait_timeouts_wgrad(uint32_t* out, bool reset);
+
+// The calling unit's own counter (each unit has its copy of the symbol).
+static inline hipError_t unit_wait_timeouts(uint32_t* out, bool reset) {
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_skg_wait_timeouts), sizeof(uint32_t), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !reset) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_skg_wait_timeouts), &zero, sizeof(uint32_t), 0,
+                           hipMemcpyHostToDevice);
+}
+
 // Launches the stream-K kernel of the plan's fix-up family (bracketed by ev0
 // / ev1 when they are set) and, for the workspace reduction, the second
 // stage.

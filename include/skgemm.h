@@ -247,7 +247,12 @@ typedef struct skg_plan {
 } skg_plan_t;
 
 /* Reason for the last non-zero status on this thread ("" if none).  The
- * pointer stays valid until the next call on the same thread. */
+ * pointer stays valid until the next call on the same thread.  The reasons
+ * are fixed strings per cause, as the wgrad launcher's rejections are on
+ * PR #13151 (Technical Details: Constraints, the validator returning a
+ * reason string for every rejected shape) and as the stream-K GEMM bridge
+ * reports why a problem is unsupported (composable_kernel commit
+ * "feat(ck-tile): stream-K GEMM TE to dispatcher bridge", Changes). */
 const char* skg_last_error(void);
 
 /* Tile instance table.  -2 for an unknown tile id. */
@@ -274,7 +279,20 @@ int skg_device_info(int32_t op, int32_t tile_id, int32_t dtype_ab,
 int skg_plan_gemm(const skg_gemm_args_t* args, skg_plan_t* out);
 int skg_plan_wgrad(const skg_wgrad_args_t* args, skg_plan_t* out);
 
-/* Run.  ws must point to at least plan.workspace_bytes of device memory
+/* Bytes of workspace the run call needs for these arguments: the plan's
+ * workspace_bytes (PR #13151, Technical Details: Partitioner -- the flag
+ * table of one int32 per stream-K CTA and wave, rounded up to 256 bytes,
+ * then one fp32 partial tile per stream-K CTA for linear/tree; one fp32
+ * tile per stream-K tile for workspace; nothing for atomic or a plan
+ * without stream-K CTAs).  Same status codes as skg_plan_*. */
+int skg_gemm_workspace_bytes(const skg_gemm_args_t* args, size_t* out);
+int skg_wgrad_workspace_bytes(const skg_wgrad_args_t* args, size_t* out);
+
+/* Run (composable_kernel commit "feat(ck-tile): stream-K GEMM TE to
+ * dispatcher bridge", Changes: one problem per call, 0 / -1 / -2; PR #13151,
+ * Technical Details: Wgrad kernel, for the launch modes, the resets and the
+ * four reductions).
+ * ws must point to at least plan.workspace_bytes of device memory
  * (may be NULL when that is 0); the call resets on the stream whatever the
  * reduction accumulates into: the flags (linear/tree), the scratch
  * (workspace) or C itself (atomic).  Partials and, for linear/tree, C are
@@ -284,6 +302,24 @@ int skg_plan_wgrad(const skg_wgrad_args_t* args, skg_plan_t* out);
  * rejected with -2.  stream is a hipStream_t (NULL: the null stream). */
 int skg_run_gemm(const skg_gemm_args_t* args, void* ws, size_t ws_bytes, void* stream);
 int skg_run_wgrad(const skg_wgrad_args_t* args, void* ws, size_t ws_bytes, void* stream);
+
+/* Hand-off waits that gave up.  A linear/tree wait polls its partner's flag
+ * a bounded number of times (PR #13151, review items: forward progress rests
+ * on in-order dispatch, which the hardware does not promise); a wait that
+ * gives up counts one event here and turns the accumulators it was folding
+ * into NaN, so the tile shows as unwritten instead of silently wrong.  The
+ * count is summed over every kernel instance since the last reset; with
+ * reset != 0 the counters are zeroed after reading.  Call only while no run
+ * call's kernels are executing (after a device or stream synchronisation).
+ * 0, or -1 if the counters cannot be read.
+ *
+ * Fault injection for tests of these paths (environment, read by every run
+ * call): SKG_FAULT=launch makes a run call return -1 where it would launch
+ * the stream-K kernel, after its resets are enqueued; SKG_FAULT=handoff
+ * launches it with stream-K CTAs that store their partials but never raise
+ * their flags and a spin limit of 64 polls, so every hand-off wait gives up
+ * quickly and the kernel still ends. */
+int skg_fixup_timeouts(uint32_t* count, int32_t reset);
 
 /* Timing hook for measurement: while set on the calling thread, every run
  * call records `start` (a hipEvent_t) on its stream immediately before the

@@ -1,7 +1,10 @@
 """Shared test helpers: device upload / download of operand codes and the
 comparison metric.  The metric (max |Y - R| / max |R|, the infinity-norm
 relative error) is our reading of the pages' "max relative error"; it is
-test logic, not part of either implementation."""
+test logic, not part of either implementation.  Alongside it, the
+element-wise relative error over the entries with |R| >= 2^-4 max |R| is
+computed and bounded, Inf and NaN entries fail, and rows holding a NaN are
+reported as unwritten."""
 
 import numpy as np
 import torch
@@ -52,9 +55,37 @@ def unwritten_rows(y2d):
     return np.nonzero(bad)[0].tolist()
 
 
+# Floor of the element-wise diagnostic, relative to max |R|.
+ELEM_FLOOR = 2.0 ** -4
+
+
+def elem_rel_err(y, r, floor=ELEM_FLOOR):
+    """max |Y - R| / |R| over the entries with |R| >= floor * max |R| (0 when
+    no entry qualifies).  Entries that small relative to the largest are left
+    out: on zero-mean data a relative error without a floor is unbounded."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    big = np.abs(r) >= floor * np.max(np.abs(r))
+    if not big.any():
+        return 0.0
+    return float(np.max(np.abs(y[big] - r[big]) / np.abs(r[big])))
+
+
 def assert_close(y2d, r2d, fmt_in, label=""):
     rows = unwritten_rows(y2d)
     assert not rows, "%s: unwritten output rows %s" % (label, rows[:16])
+    assert not np.isinf(y2d).any(), "%s: Inf in the output" % label
     err = rel_err(y2d, r2d)
     assert err <= TOL[fmt_in], "%s: max rel err %.3e > %.1e" % (label, err, TOL[fmt_in])
+    # Entries at least 2^-4 of the largest: their own relative error cannot
+    # exceed 16x the infinity-norm bound; anything beyond that is an entry
+    # computed wrongly, not rounding.
+    e = elem_rel_err(y2d, r2d)
+    assert e <= TOL[fmt_in] / ELEM_FLOOR, "%s: element-wise rel err %.3e (|R| >= 2^-4 max)" % (label, e)
+    DIAGS.append((fmt_in, label, err, e))
     return err
+
+
+# (input format, label, infinity-norm rel err, element-wise rel err) of every
+# assert_close in the session; conftest prints a summary at the end.
+DIAGS = []

@@ -1,10 +1,14 @@
 """Deterministic fix-ups: linear and tree results are bit-identical across 20
-launches when the partials, the flags' neighbourhood and the output are
+launches when the whole workspace (flags and partials) and the output are
 poisoned (all bytes 0xFF, a NaN in every float format) before each launch,
 so a partial read before its release would show up as a NaN or a different
 value (rocm-libraries PR #13151, GPU test plan and the review finding that
-only the flags had been reset between launches).  Also checks the bounded
-flag wait never timed out.
+only the flags had been reset between launches).  Workloads: the fp16 GEMM
+over a 6-CTA pool whose ranges straddle tiles, the bf16 GEMM with 48
+stream-K tiles over 256 CTAs, and both conv wgrad workloads, each in the
+dp_sk and persistent modes.  That no bounded flag wait gave up during these
+launches is checked for every GPU test by the fixture in conftest.py (the
+library counts give-ups; skg_fixup_timeouts).
 """
 
 import numpy as np
@@ -52,14 +56,33 @@ def test_gemm_bf16_large_repeat(mode, reduction):
 
 
 @pytest.mark.parametrize("reduction", ["linear", "tree"])
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent"])
+def test_gemm_f16_pool6_repeat(mode, reduction):
+    wl = synth.WORKLOADS[1]
+    inp = wl.inputs()
+    dA, dB = to_dev(inp["A"], "f16"), to_dev(inp["B"], "f16")
+    C = torch.empty(wl.M * wl.N, dtype=torch.float16, device="cuda")
+    kw = dict(M=wl.M, N=wl.N, K=wl.K, dtype_ab="f16", dtype_c="f16", tile=wl.tile, mode=mode,
+              reduction=reduction, ctas=wl.ctas)
+    plan = skg.plan_gemm(**kw)
+    # 4 tiles x 128 iterations over 6 CTAs: ranges of 85-86 iterations that
+    # straddle tiles; a tile has up to 3 contributors.
+    assert (plan["sk_ctas"], plan["iters_per_sk_cta"], plan["extra_iters"],
+            plan["max_contrib"]) == (6, 85, 2, 3)
+    ws = skg.workspace_for(plan, "cuda")
+    repeat(lambda: skg.gemm(dA, dB, C, workspace=ws, **kw), C, ws)
+
+
+@pytest.mark.parametrize("reduction", ["linear", "tree"])
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent"])
 @pytest.mark.parametrize("index", [3, 4])
-def test_wgrad_repeat(index, reduction):
+def test_wgrad_repeat(index, mode, reduction):
     wl = synth.WORKLOADS[index]
     inp = wl.inputs()
     dx, ddy = to_dev(inp["x"], wl.dtype), to_dev(inp["dy"], wl.dtype)
     dw = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device="cuda")
     kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
-              pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile=wl.tile, mode="dp_sk",
+              pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile=wl.tile, mode=mode,
               reduction=reduction, ctas=wl.ctas)
     plan = skg.plan_wgrad(**kw)
     assert plan["sk_ctas"] > 0 and plan["max_contrib"] >= 2

@@ -4,10 +4,12 @@
 * The C++ planner equals the oracle partitioner field by field over a sweep
   of GEMM and wgrad shapes, tiles, modes, reductions and pools.
 * Unsupported arguments are rejected with -2 and a reason.
-* The built gfx950 code object orders the flag hand-off as the AMDGPU memory
-  model prescribes: L2 write-back before the flag store of a publish, an
-  agent-coherent poll and an L2 invalidate after it (rocm-libraries PR #13151,
-  test plan: flag ordering pinned in the ISA).
+* The built gfx950 code object orders the flag hand-off the way the engine
+  implements release/acquire (rocm-libraries PR #13151, test plan: flag
+  ordering pinned in the ISA): partials stored and loaded at device scope
+  (sc1), every flag store right after a full wait for the wave's earlier
+  stores, device-scope polls -- and no L2-wide write-back or invalidation
+  anywhere (the test asserts their absence).
 """
 
 import os
