@@ -80,13 +80,12 @@ SKG_DEV void static_for(F&& f) {
 // wave performs the store and the poll on the same flag word.
 //
 // The poll is bounded: after `limit` polls the wave gives up, counts the event
-// in g_skg_wait_timeouts and reports it, and the caller poisons what it was
-// about to fold with NaN, so a broken plan or a pool that is not resident
-// shows as NaN outputs (and a count the host reads with
-// skg_fixup_timeouts) rather than a hung device or silently wrong numbers.
-// The default limit, kSpinLimit, is 2^22 polls; each poll is a device-scope
-// load (a round trip past the L2) followed by a short sleep, so the bound is
-// in the order of seconds, far beyond any legitimate wait.
+// once in g_skg_wait_timeouts and returns false, so a broken plan or a pool
+// that is not resident ends as a counted failure the host can read
+// (skg_fixup_timeouts) rather than a hung device.  The default limit,
+// kSpinLimit, is 2^22 polls; each poll is a device-scope load (a round trip
+// past the L2) followed by a short sleep, so the bound is in the order of
+// seconds, far beyond any legitimate wait.
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kDeviceScope = 16;  // cache-policy bits of a buffer access: sc1
 

@@ -1283,8 +1283,13 @@ struct Engine {
   // partner in the order Fix::partner gives.  Each wave waits only for the
   // flag of its own wave in the partner CTA.  The loads of a batch are all
   // issued before its first add, so one memory round trip covers FB float4
-  // per lane.  If a wait gives up, that partner's values are folded as NaN
-  // (each plus a NaN), so the tile is visibly wrong rather than silently so.
+  // per lane.  A wait that gives up (flag_wait) is counted for the host
+  // (skg_fixup_timeouts); the fold then adds whatever the partial buffer
+  // holds, so the tile's values are unspecified.  Marking the tile here
+  // (NaN) costs the folds of every launch: any extra work on the loaded
+  // partials or on the accumulators changes how the compiler schedules the
+  // batched loads or allocates the accumulators; each variant tried slowed
+  // the hand-off kernels by 15-20 %.
   SKG_DEV void fold_regs(const Fix& fx) {
     constexpr int FB = PSLOTS < 32 ? PSLOTS : 32;
     static_assert(PSLOTS % FB == 0, "fold batches");
@@ -1304,19 +1309,16 @@ struct Engine {
     });
     for (int k = 0; k < fx.nfold; ++k) {
       const int c = fx.partner(k);
-      bool ok = true;
-      if (k >= MAXQ || !((ready >> k) & 1u)) ok = flag_wait(s.flags + c * Cfg::NW + wave, p.spin_limit);
+      if (k >= MAXQ || !((ready >> k) & 1u)) flag_wait(s.flags + c * Cfg::NW + wave, p.spin_limit);
       asm volatile("" ::: "memory");  // partial loads stay after the flag check
       const __amdgpu_buffer_rsrc_t q = partial_rsrc(c);
       const uint32_t base = part_base();
-      // A partner whose flag never came is folded as NaN.
-      const float poison = ok ? 0.f : __builtin_nanf("");
       static_for<0, PSLOTS / FB>([&](auto b_) {
         constexpr int b = decltype(b_)::value;
         f32x4 t[FB];
         static_for<0, FB>([&](auto i_) {
           constexpr int i = decltype(i_)::value;
-          t[i] = load_dev16_s(q, base, (b * FB + i) * 1024) + poison;
+          t[i] = load_dev16_s(q, base, (b * FB + i) * 1024);
         });
         static_for<0, FB>([&](auto i_) {
           constexpr int i = decltype(i_)::value, j = b * FB + i;

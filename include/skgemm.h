@@ -306,12 +306,14 @@ int skg_run_wgrad(const skg_wgrad_args_t* args, void* ws, size_t ws_bytes, void*
 /* Hand-off waits that gave up.  A linear/tree wait polls its partner's flag
  * a bounded number of times (PR #13151, review items: forward progress rests
  * on in-order dispatch, which the hardware does not promise); a wait that
- * gives up counts one event here and turns the accumulators it was folding
- * into NaN, so the tile shows as unwritten instead of silently wrong.  The
- * count is summed over every kernel instance since the last reset; with
- * reset != 0 the counters are zeroed after reading.  Call only while no run
- * call's kernels are executing (after a device or stream synchronisation).
- * 0, or -1 if the counters cannot be read.
+ * gives up counts one event per wave here and the fold goes on with whatever
+ * the partner's partial buffer holds, so the values of that tile are then
+ * unspecified: a caller that cannot rule out a pool larger than what stays
+ * resident (another process taking CUs) checks this count.  It is summed
+ * over every kernel instance since the last reset; with reset != 0 the
+ * counters are zeroed after reading.  Call only while no run call's kernels
+ * are executing (after a device or stream synchronisation).  0, or -1 if
+ * the counters cannot be read.
  *
  * Fault injection for tests of these paths (environment, read by every run
  * call): SKG_FAULT=launch makes a run call return -1 where it would launch
