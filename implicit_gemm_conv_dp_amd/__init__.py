@@ -18,14 +18,15 @@ from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
                    skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
                    skg_tile_info, skg_gemm_workspace_bytes, skg_wgrad_workspace_bytes,
-                   skg_fixup_timeouts, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
+                   skg_fixup_timeouts, skg_run_wgrad_static, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
 
 __all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
            "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES", "SCALE_MODES",
            "SK_ORDERS",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
            "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events",
-           "skg_gemm_workspace_bytes", "skg_wgrad_workspace_bytes", "skg_fixup_timeouts"]
+           "skg_gemm_workspace_bytes", "skg_wgrad_workspace_bytes", "skg_fixup_timeouts",
+           "skg_run_wgrad_static"]
 
 
 def _enum(table, v, what):

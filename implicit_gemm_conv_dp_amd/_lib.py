@@ -92,7 +92,11 @@ EXPORTS = {
     "skg_wgrad_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(skg_wgrad_args_t),
                                                  ctypes.POINTER(ctypes.c_size_t)]),
     "skg_fixup_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]),
+    "skg_run_wgrad_static": (ctypes.c_int, [ctypes.POINTER(skg_wgrad_args_t), ctypes.c_void_p]),
 }
+
+# Bytes of the library's own scratch array used by skg_run_wgrad_static.
+STATIC_SCRATCH_BYTES = 33 << 20
 
 _lib = None
 
@@ -186,6 +190,10 @@ def skg_wgrad_workspace_bytes(args):
     out = ctypes.c_size_t()
     check(load().skg_wgrad_workspace_bytes(ctypes.byref(args), ctypes.byref(out)))
     return out.value
+
+
+def skg_run_wgrad_static(args, stream_ptr):
+    return check(load().skg_run_wgrad_static(ctypes.byref(args), stream_ptr))
 
 
 def skg_fixup_timeouts(reset=False):

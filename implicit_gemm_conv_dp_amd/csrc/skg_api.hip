@@ -162,6 +162,128 @@ int reset_scratch(const skg_plan_t& pl, void* ws, hipStream_t st) {
   return SKG_OK;
 }
 
+// Fills `words` 32-bit words with zero.  The allocation-free entry point
+// clears its scratch and outputs with this kernel instead of
+// hipMemsetAsync: a caller may capture the call into a HIP graph, where
+// memset nodes are best avoided.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t words) {
+  const size_t step = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += step) p[i] = 0u;
+}
+
+hipError_t zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const size_t words = bytes / 4;  // every cleared region is a multiple of 4 bytes
+  if (!words) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+// Scratch of skg_run_wgrad_static: a file-scope device array (one copy per
+// device the library runs on, held until the process ends).  Host code
+// never uses the array's name as a device address: the address of each
+// device's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and kept in g_static_scratch.
+constexpr size_t kStaticScratchBytes = SKG_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_static_scratch;  // per device; nullptr until first use
+
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failure(std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_static_scratch.size() <= dev) g_static_scratch.resize(dev + 1, nullptr);
+  if (!g_static_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return hip_failure(std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_static_scratch[dev] = ptr;
+  }
+  *out = g_static_scratch[dev];
+  return SKG_OK;
+}
+
+// The wgrad run call.  kernel_resets: clear flags, scratch and (atomic) dW
+// with zero_fill instead of hipMemsetAsync.
+int run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, hipStream_t st,
+              bool kernel_resets) {
+  int rc = validate_wgrad(a);
+  if (rc) return rc;
+  if (!a->x || !a->dy || !a->dw) return unsupported("null x, dy or dw");
+  if (!aligned(a->x, 16) || !aligned(a->dy, 16) || !aligned(a->dw, 16))
+    return unsupported("x, dy and dw must be 16-byte aligned");
+  const TileDesc* t = tile_desc(a->tile_id);
+  WgradInst inst = wgrad_instance(a->tile_id, a->dtype);
+  if (!inst.launch) return unsupported("no wgrad instance for this tile and dtype");
+  int cus = 0, per_cu = 0;
+  rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
+  if (rc) return rc;
+  skg_plan_t pl;
+  rc = plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
+                   resolve_sk_order(a->sk_order, true), cus, per_cu, &pl);
+  if (rc) return rc;
+  if (kernel_resets && (size_t)pl.workspace_bytes > ws_bytes)
+    return unsupported("the plan needs " + std::to_string(pl.workspace_bytes) +
+                       " bytes of scratch; the static scratch holds " + std::to_string(ws_bytes));
+  rc = check_run(pl, ws, ws_bytes, cus, per_cu);
+  if (rc) return rc;
+  if (kernel_resets) {
+    size_t bytes = 0;
+    if (pl.sk_ctas && (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE))
+      bytes = (size_t)pl.flags_bytes;
+    else if (pl.sk_ctas && pl.reduction == SKG_RED_WORKSPACE)
+      bytes = (size_t)pl.workspace_bytes;
+    hipError_t e = zero_fill(ws, bytes, st);
+    if (e != hipSuccess) return hip_failure(std::string("reset: ") + hipGetErrorString(e));
+  } else {
+    rc = reset_scratch(pl, ws, st);
+    if (rc) return rc;
+  }
+  WgradParams w;
+  w.X = static_cast<const char*>(a->x);
+  w.dY = static_cast<const char*>(a->dy);
+  w.dW = a->dw;
+  w.N = a->n;
+  w.H = a->h;
+  w.W = a->w;
+  w.C = a->c;
+  w.K = a->k;
+  w.R = a->r;
+  w.S = a->s;
+  w.sh = a->stride_h;
+  w.sw = a->stride_w;
+  w.ph = a->pad_h;
+  w.pw = a->pad_w;
+  w.Ho = (a->h + 2 * a->pad_h - a->r) / a->stride_h + 1;
+  w.Wo = (a->w + 2 * a->pad_w - a->s) / a->stride_w + 1;
+  w.cpg = a->c / a->groups;
+  w.kpg = a->k / a->groups;
+  w.mt_per_group = (int)ceil_div(w.kpg, t->tm);
+  w.gemm_n = w.cpg * a->r * a->s;
+  w.kred = a->n * w.Ho * w.Wo;
+  w.x_bytes = (uint32_t)((int64_t)a->n * a->h * a->w * a->c * 2);
+  w.dy_bytes = (uint32_t)((int64_t)w.kred * a->k * 2);
+  w.div_howo = make_fastdiv((uint32_t)(w.Ho * w.Wo));
+  w.div_wo = make_fastdiv((uint32_t)w.Wo);
+  w.div_cpg = make_fastdiv((uint32_t)w.cpg);
+  w.div_s = make_fastdiv((uint32_t)a->s);
+  if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {
+    const size_t bytes = (size_t)a->k * w.gemm_n * 4;
+    hipError_t e = kernel_resets ? zero_fill(a->dw, bytes, st) : hipMemsetAsync(a->dw, 0, bytes, st);
+    if (e != hipSuccess) return hip_failure(std::string("zeroing dW: ") + hipGetErrorString(e));
+  }
+  const int inject = injected_fault();
+  if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
+  hipError_t e = inst.launch(w, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
+  if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
+  return SKG_OK;
+}
+
 }  // namespace
 }  // namespace skg
 
@@ -334,63 +456,22 @@ int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stre
 int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* stream) {
   try {
     clear_error();
-    int rc = validate_wgrad(a);
+    return run_wgrad(a, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+int skg_run_wgrad_static(const skg_wgrad_args_t* a, void* stream) {
+  try {
+    clear_error();
+    if (!a) return unsupported("null arguments");
+    void* ws = nullptr;
+    const int rc = static_scratch(&ws);
     if (rc) return rc;
-    if (!a->x || !a->dy || !a->dw) return unsupported("null x, dy or dw");
-    if (!aligned(a->x, 16) || !aligned(a->dy, 16) || !aligned(a->dw, 16))
-      return unsupported("x, dy and dw must be 16-byte aligned");
-    const TileDesc* t = tile_desc(a->tile_id);
-    WgradInst inst = wgrad_instance(a->tile_id, a->dtype);
-    if (!inst.launch) return unsupported("no wgrad instance for this tile and dtype");
-    int cus = 0, per_cu = 0;
-    rc = device_capacity(SKG_OP_WGRAD, a->tile_id, a->dtype, &cus, &per_cu);
-    if (rc) return rc;
-    skg_plan_t pl;
-    rc = plan_launch(wgrad_shape(a, *t), *t, a->mode, a->reduction, a->ctas,
-                     resolve_sk_order(a->sk_order, true), cus, per_cu, &pl);
-    if (rc) return rc;
-    rc = check_run(pl, ws, ws_bytes, cus, per_cu);
-    if (rc) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    rc = reset_scratch(pl, ws, st);
-    if (rc) return rc;
-    WgradParams w;
-    w.X = static_cast<const char*>(a->x);
-    w.dY = static_cast<const char*>(a->dy);
-    w.dW = a->dw;
-    w.N = a->n;
-    w.H = a->h;
-    w.W = a->w;
-    w.C = a->c;
-    w.K = a->k;
-    w.R = a->r;
-    w.S = a->s;
-    w.sh = a->stride_h;
-    w.sw = a->stride_w;
-    w.ph = a->pad_h;
-    w.pw = a->pad_w;
-    w.Ho = (a->h + 2 * a->pad_h - a->r) / a->stride_h + 1;
-    w.Wo = (a->w + 2 * a->pad_w - a->s) / a->stride_w + 1;
-    w.cpg = a->c / a->groups;
-    w.kpg = a->k / a->groups;
-    w.mt_per_group = (int)ceil_div(w.kpg, t->tm);
-    w.gemm_n = w.cpg * a->r * a->s;
-    w.kred = a->n * w.Ho * w.Wo;
-    w.x_bytes = (uint32_t)((int64_t)a->n * a->h * a->w * a->c * 2);
-    w.dy_bytes = (uint32_t)((int64_t)w.kred * a->k * 2);
-    w.div_howo = make_fastdiv((uint32_t)(w.Ho * w.Wo));
-    w.div_wo = make_fastdiv((uint32_t)w.Wo);
-    w.div_cpg = make_fastdiv((uint32_t)w.cpg);
-    w.div_s = make_fastdiv((uint32_t)a->s);
-    if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {
-      hipError_t e = hipMemsetAsync(a->dw, 0, (size_t)a->k * w.gemm_n * 4, st);
-      if (e != hipSuccess) return hip_failure(std::string("zeroing dW: ") + hipGetErrorString(e));
-    }
-    const int inject = injected_fault();
-    if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
-    hipError_t e = inst.launch(w, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
-    if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
-    return SKG_OK;
+    return run_wgrad(a, ws, kStaticScratchBytes, static_cast<hipStream_t>(stream), true);
   } catch (const std::exception& ex) {
     return hip_failure(std::string("exception: ") + ex.what());
   } catch (...) {

@@ -303,6 +303,23 @@ int skg_wgrad_workspace_bytes(const skg_wgrad_args_t* args, size_t* out);
 int skg_run_gemm(const skg_gemm_args_t* args, void* ws, size_t ws_bytes, void* stream);
 int skg_run_wgrad(const skg_wgrad_args_t* args, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free wgrad, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, plan and results as skg_run_wgrad, but the
+ * flags, partials or scratch live in one library-owned device array of
+ * SKG_STATIC_SCRATCH_BYTES per device (allocated with the library's code
+ * object on that device and held until the process ends), and the resets are
+ * done by a small fill kernel instead of hipMemsetAsync.  The call itself
+ * allocates nothing.  A plan whose workspace_bytes exceeds the array is
+ * rejected with -2 (the reason names both sizes); e.g. the 256x128x64 tile
+ * on N=32 56x56 C=K=256 3x3 fits with every reduction at a pool of 256.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind: two calls that overlap in time on one device (different
+ * streams, or different host threads) race and give wrong results; calls
+ * on one stream are ordered and safe.  Status codes as skg_run_wgrad. */
+#define SKG_STATIC_SCRATCH_BYTES (33u << 20)
+int skg_run_wgrad_static(const skg_wgrad_args_t* args, void* stream);
+
 /* Hand-off waits that gave up.  A linear/tree wait polls its partner's flag
  * a bounded number of times (PR #13151, review items: forward progress rests
  * on in-order dispatch, which the hardware does not promise); a wait that
