@@ -15,6 +15,8 @@ algorithm written out step by step):
                    rcr layout (row-major A, column-major B).
 * ``wgrad``     -- the backward-weight convolution by its definition (NHWC
                    activations, KRSC filter gradient, grouped, strided, padded).
+* ``conv``      -- the forward convolution and the input gradient (dgrad) by
+                   their definitions, same layouts.
 * ``partition`` -- the data-parallel + stream-K split of output tiles and MAC
                    iterations over a CTA pool, plus a brute-force invariant
                    checker.
@@ -29,4 +31,4 @@ GPU's fp32 summation order is not reproduced bit for bit on random data (the
 oracle is fp64; the bar there is the tolerance).
 """
 
-from . import codecs, gemm, wgrad, partition, simulate  # noqa: F401
+from . import codecs, gemm, wgrad, conv, partition, simulate  # noqa: F401

@@ -206,6 +206,23 @@ def wgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups,
             ceil_div(N * ho * wo, tk))
 
 
+def fwd_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk):
+    """Implicit-GEMM view of a forward convolution: GEMM-M = output pixels
+    N*Ho*Wo, GEMM-N = output channels folded per group (the tile count is
+    per group, so an N tile never crosses a group), reduction = R*S*Cpg."""
+    ho = (H + 2 * pad_h - R) // stride_h + 1
+    wo = (W + 2 * pad_w - S) // stride_w + 1
+    kpg, cpg = K // groups, C // groups
+    return (ceil_div(N * ho * wo, tm), groups * ceil_div(kpg, tn), ceil_div(R * S * cpg, tk))
+
+
+def dgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk):
+    """Implicit-GEMM view of the input gradient: GEMM-M = input pixels
+    N*H*W, GEMM-N = input channels folded per group, reduction = R*S*Kpg."""
+    kpg, cpg = K // groups, C // groups
+    return (ceil_div(N * H * W, tm), groups * ceil_div(cpg, tn), ceil_div(R * S * kpg, tk))
+
+
 def check_plan(p):
     """Brute-force the invariants of a plan over an explicit coverage array.
     Returns a list of violated properties (empty when the plan is sound)."""
