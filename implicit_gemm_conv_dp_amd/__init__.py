@@ -18,15 +18,19 @@ from . import _lib
 from ._lib import (SkgError, skg_default_pool, skg_device_info, skg_plan_gemm,  # noqa: F401
                    skg_plan_wgrad, skg_profile_events, skg_run_gemm, skg_run_wgrad,
                    skg_tile_info, skg_gemm_workspace_bytes, skg_wgrad_workspace_bytes,
-                   skg_fixup_timeouts, skg_run_wgrad_static, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES, SK_ORDERS)
+                   skg_fixup_timeouts, skg_run_wgrad_static, skg_plan_fwd, skg_plan_dgrad,
+                   skg_run_fwd, skg_run_dgrad, MODES, REDUCTIONS, DTYPES, TILES, SCALE_MODES,
+                   SK_ORDERS)
 
-__all__ = ["gemm", "wgrad", "plan_gemm", "plan_wgrad", "gemm_args", "wgrad_args",
+__all__ = ["gemm", "wgrad", "fwd", "dgrad", "plan_gemm", "plan_wgrad", "plan_fwd", "plan_dgrad",
+           "gemm_args", "wgrad_args", "conv_args",
            "workspace_for", "SkgError", "MODES", "REDUCTIONS", "DTYPES", "TILES", "SCALE_MODES",
            "SK_ORDERS",
            "skg_default_pool", "skg_device_info", "skg_plan_gemm", "skg_plan_wgrad",
            "skg_run_gemm", "skg_run_wgrad", "skg_tile_info", "skg_profile_events",
            "skg_gemm_workspace_bytes", "skg_wgrad_workspace_bytes", "skg_fixup_timeouts",
-           "skg_run_wgrad_static"]
+           "skg_run_wgrad_static", "skg_plan_fwd", "skg_plan_dgrad", "skg_run_fwd",
+           "skg_run_dgrad"]
 
 
 def _enum(table, v, what):
@@ -80,12 +84,40 @@ def wgrad_args(x=None, dy=None, dw=None, *, n, h, w, c, k, r, s, stride=(1, 1), 
     return a
 
 
+def conv_args(act=None, filt=None, out=None, *, n, h, w, c, k, r, s, stride=(1, 1), pad=(0, 0),
+              groups=1, dtype, dtype_out, tile, mode, reduction, ctas, sk_order="auto"):
+    """Arguments of a forward convolution (act = X, out = Y) or of its input
+    gradient (act = dY, out = dX); filt is the KRSC filter W either way."""
+    a = _lib.skg_conv_args_t()
+    a.n, a.h, a.w, a.c, a.k, a.r, a.s = n, h, w, c, k, r, s
+    a.stride_h, a.stride_w = stride
+    a.pad_h, a.pad_w = pad
+    a.groups = groups
+    a.dtype = _enum(DTYPES, dtype, "dtype")
+    a.dtype_out = _enum(DTYPES, dtype_out, "dtype")
+    a.act, a.filt, a.out = _ptr(act), _ptr(filt), _ptr(out)
+    a.tile_id = _enum(TILES, tile, "tile")
+    a.mode = _enum(MODES, mode, "mode")
+    a.reduction = _enum(REDUCTIONS, reduction, "reduction")
+    a.ctas = ctas
+    a.sk_order = _enum(SK_ORDERS, sk_order, "stream-K order")
+    return a
+
+
 def plan_gemm(**kw):
     return skg_plan_gemm(gemm_args(**kw)).as_dict()
 
 
 def plan_wgrad(**kw):
     return skg_plan_wgrad(wgrad_args(**kw)).as_dict()
+
+
+def plan_fwd(**kw):
+    return skg_plan_fwd(conv_args(**kw)).as_dict()
+
+
+def plan_dgrad(**kw):
+    return skg_plan_dgrad(conv_args(**kw)).as_dict()
 
 
 def workspace_for(plan, device):
@@ -126,4 +158,22 @@ def wgrad(x, dy, dw, workspace=None, stream=None, **kw):
     args = wgrad_args(x, dy, dw, **kw)
     plan = skg_plan_wgrad(args).as_dict()
     _run(skg_run_wgrad, args, plan, dw.device, workspace, stream)
+    return plan
+
+
+def fwd(x, filt, y, workspace=None, stream=None, **kw):
+    """Enqueue the forward convolution y = conv(x, filt) on ``stream``.
+    Returns the plan (a dict)."""
+    args = conv_args(x, filt, y, **kw)
+    plan = skg_plan_fwd(args).as_dict()
+    _run(skg_run_fwd, args, plan, y.device, workspace, stream)
+    return plan
+
+
+def dgrad(dy, filt, dx, workspace=None, stream=None, **kw):
+    """Enqueue the input gradient dx = dgrad(dy, filt) on ``stream``.
+    Returns the plan (a dict)."""
+    args = conv_args(dy, filt, dx, **kw)
+    plan = skg_plan_dgrad(args).as_dict()
+    _run(skg_run_dgrad, args, plan, dx.device, workspace, stream)
     return plan

@@ -15,7 +15,7 @@ F16, BF16, F8E4M3, F32, F8E5M2 = 0, 1, 2, 3, 4
 SCALE_ROWCOL, SCALE_TENSOR = 0, 1
 MODE_DP, MODE_DP_SK, MODE_PERSISTENT, MODE_SPLITK, MODE_AUTO = 0, 1, 2, 3, 4
 RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO = 0, 1, 2, 3, 4
-OP_GEMM, OP_WGRAD = 0, 1
+OP_GEMM, OP_WGRAD, OP_FWD, OP_DGRAD = 0, 1, 2, 3
 TILE_128x128x32, TILE_256x256x64, TILE_256x256x128, TILE_32x64x64, TILE_128x128x64, \
     TILE_256x128x64 = range(6)
 TILE_COUNT = 6
@@ -36,7 +36,7 @@ TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
 class skg_tile_info_t(ctypes.Structure):
     _fields_ = [("tm", ctypes.c_int32), ("tn", ctypes.c_int32), ("tk", ctypes.c_int32),
                 ("n_waves", ctypes.c_int32), ("gemm_dtypes", ctypes.c_int32),
-                ("wgrad_dtypes", ctypes.c_int32)]
+                ("wgrad_dtypes", ctypes.c_int32), ("conv_dtypes", ctypes.c_int32)]
 
 
 class skg_gemm_args_t(ctypes.Structure):
@@ -59,6 +59,14 @@ class skg_wgrad_args_t(ctypes.Structure):
                [(n, ctypes.c_int32) for n in ("tile_id", "mode", "reduction", "ctas", "sk_order")]
 
 
+class skg_conv_args_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n", "h", "w", "c", "k", "r", "s", "stride_h", "stride_w", "pad_h", "pad_w",
+                 "groups", "dtype", "dtype_out")] + \
+               [("act", ctypes.c_void_p), ("filt", ctypes.c_void_p), ("out", ctypes.c_void_p)] + \
+               [(n, ctypes.c_int32) for n in ("tile_id", "mode", "reduction", "ctas", "sk_order")]
+
+
 class skg_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("tm", "tn", "tk", "n_waves", "mode", "reduction")] + \
                [(n, ctypes.c_int64) for n in
@@ -66,7 +74,8 @@ class skg_plan_t(ctypes.Structure):
                  "sk_ctas", "sk_iters", "iters_per_sk_cta", "extra_iters", "grid", "max_contrib",
                  "linear_partners", "tree_rounds", "flags_bytes", "partials_bytes",
                  "workspace_bytes")] + \
-               [(n, ctypes.c_int32) for n in ("requested_mode", "slices", "sk_order")]
+               [(n, ctypes.c_int32) for n in ("requested_mode", "slices", "sk_order")] + \
+               [("aux_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -93,6 +102,12 @@ EXPORTS = {
                                                  ctypes.POINTER(ctypes.c_size_t)]),
     "skg_fixup_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]),
     "skg_run_wgrad_static": (ctypes.c_int, [ctypes.POINTER(skg_wgrad_args_t), ctypes.c_void_p]),
+    "skg_plan_fwd": (ctypes.c_int, [ctypes.POINTER(skg_conv_args_t), ctypes.POINTER(skg_plan_t)]),
+    "skg_plan_dgrad": (ctypes.c_int, [ctypes.POINTER(skg_conv_args_t), ctypes.POINTER(skg_plan_t)]),
+    "skg_run_fwd": (ctypes.c_int, [ctypes.POINTER(skg_conv_args_t), ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "skg_run_dgrad": (ctypes.c_int, [ctypes.POINTER(skg_conv_args_t), ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 # Bytes of the library's own scratch array used by skg_run_wgrad_static.
@@ -200,3 +215,23 @@ def skg_fixup_timeouts(reset=False):
     out = ctypes.c_uint32()
     check(load().skg_fixup_timeouts(ctypes.byref(out), 1 if reset else 0))
     return out.value
+
+
+def skg_plan_fwd(args):
+    out = skg_plan_t()
+    check(load().skg_plan_fwd(ctypes.byref(args), ctypes.byref(out)))
+    return out
+
+
+def skg_plan_dgrad(args):
+    out = skg_plan_t()
+    check(load().skg_plan_dgrad(ctypes.byref(args), ctypes.byref(out)))
+    return out
+
+
+def skg_run_fwd(args, ws_ptr, ws_bytes, stream_ptr):
+    return check(load().skg_run_fwd(ctypes.byref(args), ws_ptr, ws_bytes, stream_ptr))
+
+
+def skg_run_dgrad(args, ws_ptr, ws_bytes, stream_ptr):
+    return check(load().skg_run_dgrad(ctypes.byref(args), ws_ptr, ws_bytes, stream_ptr))

@@ -29,7 +29,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 SOURCES = ["skg_host.cpp", "skg_api.hip", "skg_inst_gemm.hip", "skg_inst_gemm_f16.hip",
-           "skg_inst_gemm_bf16.hip", "skg_inst_gemm_f8.hip", "skg_inst_wgrad.hip"]
+           "skg_inst_gemm_bf16.hip", "skg_inst_gemm_f8.hip", "skg_inst_wgrad.hip",
+           "skg_inst_fwd.hip", "skg_inst_dgrad.hip"]
 
 
 def _compile(src):

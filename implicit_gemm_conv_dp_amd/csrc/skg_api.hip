@@ -69,6 +69,10 @@ int device_capacity(int op, int tile_id, int dtype, int* cus, int* per_cu) {
     WgradInst in = wgrad_instance(tile_id, dtype);
     if (!in.occupancy) return unsupported("no wgrad instance for this tile and dtype");
     e = in.occupancy(&occ);
+  } else if (op == SKG_OP_FWD || op == SKG_OP_DGRAD) {
+    ConvInst in = op == SKG_OP_FWD ? fwd_instance(tile_id, dtype) : dgrad_instance(tile_id, dtype);
+    if (!in.occupancy) return unsupported("no convolution instance for this tile and dtype");
+    e = in.occupancy(&occ);
   } else {
     return unsupported("unknown op");
   }
@@ -151,13 +155,26 @@ int check_run(const skg_plan_t& pl, void* ws, size_t ws_bytes, int cus, int per_
   return SKG_OK;
 }
 
+// The conv plan once the device capacity is known (used only for ctas = -1).
+int plan_conv_with(const skg_conv_args_t* a, bool dgrad, const TileDesc& t, int cus, int per_cu,
+                   skg_plan_t* out) {
+  const int rc = plan_launch(conv_shape(a, t, dgrad), t, a->mode, a->reduction, a->ctas,
+                             resolve_sk_order(a->sk_order, false), cus, per_cu, out);
+  if (rc) return rc;
+  if (dgrad) {
+    out->aux_bytes = dgrad_filter_bytes(a);
+    out->workspace_bytes += out->aux_bytes;
+  }
+  return SKG_OK;
+}
+
 int reset_scratch(const skg_plan_t& pl, void* ws, hipStream_t st) {
   if (!pl.sk_ctas) return SKG_OK;
   hipError_t e = hipSuccess;
   if (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE)
     e = hipMemsetAsync(ws, 0, (size_t)pl.flags_bytes, st);
   else if (pl.reduction == SKG_RED_WORKSPACE)
-    e = hipMemsetAsync(ws, 0, (size_t)pl.workspace_bytes, st);
+    e = hipMemsetAsync(ws, 0, (size_t)(pl.workspace_bytes - pl.aux_bytes), st);
   if (e != hipSuccess) return hip_failure(std::string("reset: ") + hipGetErrorString(e));
   return SKG_OK;
 }
@@ -237,7 +254,7 @@ int run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, hipStream_t 
     if (pl.sk_ctas && (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE))
       bytes = (size_t)pl.flags_bytes;
     else if (pl.sk_ctas && pl.reduction == SKG_RED_WORKSPACE)
-      bytes = (size_t)pl.workspace_bytes;
+      bytes = (size_t)(pl.workspace_bytes - pl.aux_bytes);
     hipError_t e = zero_fill(ws, bytes, st);
     if (e != hipSuccess) return hip_failure(std::string("reset: ") + hipGetErrorString(e));
   } else {
@@ -280,6 +297,129 @@ int run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, hipStream_t 
   const int inject = injected_fault();
   if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
   hipError_t e = inst.launch(w, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
+  if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
+  return SKG_OK;
+}
+
+// Wt[g][c][r][s][k'] = W[g*Kpg + k'][r][s][c]: per group and tap, a Kpg x Cpg
+// block transposed through a 32x33 LDS tile (reads along c, writes along k',
+// both coalesced).  Grid: (ceil(Cpg/32), ceil(Kpg/32), groups*R*S), 32x8 threads.
+__global__ __launch_bounds__(256) void transpose_filter_kernel(const uint16_t* __restrict__ w,
+                                                              uint16_t* __restrict__ wt, int kpg,
+                                                              int cpg, int rs) {
+  __shared__ uint16_t t[32][33];
+  const int g = blockIdx.z / rs, tap = blockIdx.z - g * rs;
+  const int c0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int k = k0 + ty + i, c = c0 + tx;
+    if (k < kpg && c < cpg) t[ty + i][tx] = w[((size_t)(g * kpg + k) * rs + tap) * cpg + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int c = c0 + ty + i, k = k0 + tx;
+    if (k < kpg && c < cpg) wt[((size_t)(g * cpg + c) * rs + tap) * kpg + k] = t[tx][ty + i];
+  }
+}
+
+
+int plan_conv(const skg_conv_args_t* a, bool dgrad, skg_plan_t* out) {
+  int rc = validate_conv(a, dgrad);
+  if (rc) return rc;
+  if (!out) return unsupported("null output");
+  const TileDesc* t = tile_desc(a->tile_id);
+  int cus = 0, per_cu = 0;
+  if (a->ctas == -1) {
+    rc = device_capacity(dgrad ? SKG_OP_DGRAD : SKG_OP_FWD, a->tile_id, a->dtype, &cus, &per_cu);
+    if (rc) return rc;
+  }
+  return plan_conv_with(a, dgrad, *t, cus, per_cu, out);
+}
+
+int run_conv(const skg_conv_args_t* a, bool dgrad, void* ws, size_t ws_bytes, hipStream_t st) {
+  int rc = validate_conv(a, dgrad);
+  if (rc) return rc;
+  if (!a->act || !a->filt || !a->out) return unsupported("null act, filt or out");
+  if (!aligned(a->act, 16) || !aligned(a->filt, 16) || !aligned(a->out, 16))
+    return unsupported("act, filt and out must be 16-byte aligned");
+  const TileDesc* t = tile_desc(a->tile_id);
+  ConvInst inst = dgrad ? dgrad_instance(a->tile_id, a->dtype) : fwd_instance(a->tile_id, a->dtype);
+  if (!inst.launch) return unsupported("no convolution instance for this tile and dtype");
+  int cus = 0, per_cu = 0;
+  rc = device_capacity(dgrad ? SKG_OP_DGRAD : SKG_OP_FWD, a->tile_id, a->dtype, &cus, &per_cu);
+  if (rc) return rc;
+  skg_plan_t pl;
+  rc = plan_conv_with(a, dgrad, *t, cus, per_cu, &pl);
+  if (rc) return rc;
+  rc = check_run(pl, ws, ws_bytes, cus, per_cu);
+  if (rc) return rc;
+  rc = reset_scratch(pl, ws, st);
+  if (rc) return rc;
+  const int ho = (a->h + 2 * a->pad_h - a->r) / a->stride_h + 1;
+  const int wo = (a->w + 2 * a->pad_w - a->s) / a->stride_w + 1;
+  const int cpg = a->c / a->groups, kpg = a->k / a->groups;
+  ConvParams c;
+  c.act = static_cast<const char*>(a->act);
+  c.out = static_cast<char*>(a->out);
+  c.dtype_out = a->dtype_out == SKG_F32 ? DT_F32 : (a->dtype_out == SKG_F16 ? DT_F16 : DT_BF16);
+  c.S = a->s;
+  c.sh = a->stride_h;
+  c.sw = a->stride_w;
+  c.ph = a->pad_h;
+  c.pw = a->pad_w;
+  const int eo = a->dtype_out == SKG_F32 ? 4 : 2;
+  if (!dgrad) {
+    c.filt = static_cast<const char*>(a->filt);
+    c.gm = a->n * ho * wo;
+    c.npg = kpg;
+    c.kred = a->r * a->s * cpg;
+    c.cin = cpg;
+    c.act_c = a->c;
+    c.out_c = a->k;
+    c.act_h = a->h;
+    c.act_w = a->w;
+    c.pix_w = wo;
+    c.div_pix_hw = make_fastdiv((uint32_t)(ho * wo));
+    c.act_bytes = (uint32_t)((int64_t)a->n * a->h * a->w * a->c * 2);
+  } else {
+    // The filter transposed per group into the workspace after the fix-up
+    // region: Wt[g][c][r][s][k'] = W[g*Kpg + k'][r][s][c].
+    char* wt = static_cast<char*>(ws) + (pl.workspace_bytes - pl.aux_bytes);
+    const dim3 grid((unsigned)ceil_div(cpg, 32), (unsigned)ceil_div(kpg, 32), (unsigned)(a->groups * a->r * a->s));
+    hipLaunchKernelGGL(transpose_filter_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a->filt), reinterpret_cast<uint16_t*>(wt), kpg, cpg,
+                       a->r * a->s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_failure(std::string("filter transpose: ") + hipGetErrorString(e));
+    c.filt = wt;
+    c.gm = a->n * a->h * a->w;
+    c.npg = cpg;
+    c.kred = a->r * a->s * kpg;
+    c.cin = kpg;
+    c.act_c = a->k;
+    c.out_c = a->c;
+    c.act_h = ho;
+    c.act_w = wo;
+    c.pix_w = a->w;
+    c.div_pix_hw = make_fastdiv((uint32_t)(a->h * a->w));
+    c.act_bytes = (uint32_t)((int64_t)a->n * ho * wo * a->k * 2);
+  }
+  c.nt_per_group = (int)ceil_div(c.npg, t->tn);
+  c.filt_bytes = (uint32_t)((int64_t)a->k * a->r * a->s * cpg * 2);
+  c.div_pix_w = make_fastdiv((uint32_t)c.pix_w);
+  c.div_cin = make_fastdiv((uint32_t)c.cin);
+  c.div_s = make_fastdiv((uint32_t)a->s);
+  c.div_sh = make_fastdiv((uint32_t)a->stride_h);
+  c.div_sw = make_fastdiv((uint32_t)a->stride_w);
+  if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {
+    hipError_t e = hipMemsetAsync(a->out, 0, (size_t)c.gm * c.out_c * eo, st);
+    if (e != hipSuccess) return hip_failure(std::string("zeroing the output: ") + hipGetErrorString(e));
+  }
+  const int inject = injected_fault();
+  if (inject == INJECT_LAUNCH) return hip_failure("launch: failure injected by SKG_FAULT=launch");
+  hipError_t e = inst.launch(c, to_kplan(pl, inject), carve(pl, ws), st, g_ev_start, g_ev_stop);
   if (e != hipSuccess) return hip_failure(std::string("launch: ") + hipGetErrorString(e));
   return SKG_OK;
 }
@@ -384,7 +524,8 @@ int skg_fixup_timeouts(uint32_t* count, int32_t reset) {
     clear_error();
     if (!count) return unsupported("null output");
     hipError_t (*const units[])(uint32_t*, bool) = {wait_timeouts_gemm_f16, wait_timeouts_gemm_bf16,
-                                                    wait_timeouts_gemm_f8, wait_timeouts_wgrad};
+                                                    wait_timeouts_gemm_f8,  wait_timeouts_wgrad,
+                                                    wait_timeouts_fwd,      wait_timeouts_dgrad};
     uint32_t total = 0;
     for (auto fn : units) {
       uint32_t c = 0;
@@ -457,6 +598,46 @@ int skg_run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, void* st
   try {
     clear_error();
     return run_wgrad(a, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+int skg_plan_fwd(const skg_conv_args_t* a, skg_plan_t* out) {
+  try {
+    clear_error();
+    return plan_conv(a, false, out);
+  } catch (...) {
+    return hip_failure("exception in skg_plan_fwd");
+  }
+}
+
+int skg_plan_dgrad(const skg_conv_args_t* a, skg_plan_t* out) {
+  try {
+    clear_error();
+    return plan_conv(a, true, out);
+  } catch (...) {
+    return hip_failure("exception in skg_plan_dgrad");
+  }
+}
+
+int skg_run_fwd(const skg_conv_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    return run_conv(a, false, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& ex) {
+    return hip_failure(std::string("exception: ") + ex.what());
+  } catch (...) {
+    return hip_failure("unknown exception");
+  }
+}
+
+int skg_run_dgrad(const skg_conv_args_t* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    clear_error();
+    return run_conv(a, true, ws, ws_bytes, static_cast<hipStream_t>(stream));
   } catch (const std::exception& ex) {
     return hip_failure(std::string("exception: ") + ex.what());
   } catch (...) {

@@ -1,0 +1,235 @@
+// Forward convolution and input gradient (dgrad) as implicit GEMMs on the
+// stream-K engine (rocm-libraries PR #13151 "feat(rocke): stream-K for
+// implicit-GEMM conv wgrad": the docs commit points the forward-convolution
+// future-work note at the stream-K port, review items 2-3 ask for forward
+// convolution on the family-agnostic partitioner).
+//
+// Both are GEMMs whose operands are K-contiguous in NHWC / KRSC memory, so
+// they run the GEMM mainloop (whole 128-byte rows per MAC iteration straight
+// into LDS, ds_read_b128 fragments):
+//   forward  Y[m][k]  = sum_q A[m][q] * W[k][q]   m = (n, ho, wo), q = (r, s, c')
+//            A[m][q]  = X[n][ho*sh - ph + r][wo*sw - pw + s][g*Cpg + c'] (0 outside)
+//   dgrad    dX[m][c] = sum_q A[m][q] * Wt[c][q]  m = (n, h, w),   q = (r, s, k')
+//            A[m][q]  = dY[n][(h + ph - r)/sh][(w + pw - s)/sw][g*Kpg + k'] when both
+//                       divisions are exact and inside the output image, else 0
+//            Wt[g][c][r][s][k'] = W[g*Kpg + k'][r][s][c]   (written into the workspace
+//                       by the run call before the stream-K kernel)
+// Groups fold into GEMM-N with the tile count per group, so an N tile never
+// crosses a group.  The reduction index q runs over (r, s) taps with the
+// channel fastest, so a 16-byte chunk (8 channels; channels per group are
+// multiples of 8) lies inside one tap.
+#pragma once
+
+#include "skg_kernels.hpp"
+
+namespace skg {
+
+struct ConvParams {
+  const char* act;    // forward: X (N,H,W,C); dgrad: dY (N,Ho,Wo,K)
+  const char* filt;   // forward: W (K,R,S,Cpg); dgrad: Wt (groups,Cpg,R,S,Kpg)
+  char* out;          // forward: Y (N,Ho,Wo,K); dgrad: dX (N,H,W,C)
+  int dtype_out;
+  int gm;             // GEMM-M: output pixels (forward) or input pixels (dgrad)
+  int npg;            // GEMM-N per group: Kpg (forward) or Cpg (dgrad)
+  int nt_per_group;   // ceil(npg / TN)
+  int kred;           // reduction: R*S*Cpg (forward) or R*S*Kpg (dgrad)
+  int cin;            // gathered channels per group: Cpg (forward) or Kpg (dgrad)
+  int act_c, out_c;   // channels of the activation and of the output tensor
+  int act_h, act_w;   // spatial size of the activation tensor
+  int pix_w;          // row length of the GEMM-M pixel grid (Wo forward, W dgrad)
+  int S, sh, sw, ph, pw;
+  uint32_t act_bytes, filt_bytes;
+  FastDiv div_pix_hw, div_pix_w, div_cin, div_s, div_sh, div_sw;
+};
+
+// Operand loader of the grouped pipeline.  Group j of a segment is the A
+// tile (j even: TM rows of the gathered activation, 128 bytes of the
+// reduction each) or the B tile (j odd: TN filter rows) of MAC iteration
+// j/2.  A thread owns one 16-byte chunk position of a row and the rows
+// row(tid) + u*STEP; the pixel of each of its A rows is decomposed once per
+// tile, the tap and channel of its chunk once per group.  Padding, pixels
+// past GEMM-M, filter rows past the group and the reduction tail come back
+// as zero (out-of-range buffer offsets).
+template <class Cfg, bool DGRAD>
+struct ConvGrpLoader {
+  static constexpr bool kDma = true, kGrouped = true, kTrans = false;
+  static_assert(Cfg::RB == 128 && Cfg::ESZ == 2, "whole-line rows of 16-bit elements");
+  static constexpr int CPR = Cfg::RB / 16;
+  static constexpr int STEP = Cfg::THREADS / CPR;
+  static constexpr int UA = Cfg::TM / STEP, UB = Cfg::TN / STEP;
+  static_assert(UA * STEP == Cfg::TM && UB * STEP == Cfg::TN, "DMA mapping");
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t offb, stepb, limb;  // B: this thread's first chunk, STEP rows, K limit (bytes)
+  int wave, chunk;
+  int pn[UA];                  // n * act_h, or -1 for a row past GEMM-M
+  int py[UA], px[UA];          // forward: ho*sh - ph, wo*sw - pw; dgrad: h + ph, w + pw
+  int act_h, act_w, kred, cin, S, sh, sw;
+  uint32_t act_c2, chan0;      // bytes per activation pixel; byte offset of the group's channels
+  FastDiv div_cin, div_s, div_sh, div_sw;
+
+  SKG_DEV void init(const ConvParams& c, int group, int m0, int n0, int tid) {
+    ra = make_rsrc(c.act, c.act_bytes);
+    const uint32_t rowb = (uint32_t)c.kred * 2;
+    const int rows_b = c.npg - n0;
+    // The filter is below 2 GiB: a 32-bit offset, kept scalar so the
+    // resource stays in SGPRs.
+    const uint32_t boff = __builtin_amdgcn_readfirstlane((uint32_t)(group * c.npg + n0) * rowb);
+    const uint32_t brec = __builtin_amdgcn_readfirstlane((uint32_t)rows_b * rowb);
+    rb = make_rsrc(c.filt + boff, brec);
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int row;
+    lds_slot<128>(tid, row, chunk);
+    offb = (uint32_t)row * rowb + chunk * 16;
+    stepb = STEP * rowb;
+    limb = rowb - chunk * 16;
+    act_h = c.act_h;
+    act_w = c.act_w;
+    kred = c.kred;
+    cin = c.cin;
+    S = c.S;
+    sh = c.sh;
+    sw = c.sw;
+    act_c2 = (uint32_t)c.act_c * 2;
+    chan0 = (uint32_t)(group * c.cin) * 2;
+    div_cin = c.div_cin;
+    div_s = c.div_s;
+    div_sh = c.div_sh;
+    div_sw = c.div_sw;
+    const int pix_w = c.pix_w;
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int m = m0 + row + u * STEP;
+      const uint32_t n = fdiv((uint32_t)m, c.div_pix_hw);
+      const int rem = m - (int)n * (int)c.div_pix_hw.d;
+      const int y = (int)fdiv((uint32_t)rem, c.div_pix_w);
+      const int x = rem - y * pix_w;
+      pn[u] = m < c.gm ? (int)n * act_h : -1;
+      py[u] = DGRAD ? y + c.ph : y * c.sh - c.ph;
+      px[u] = DGRAD ? x + c.pw : x * c.sw - c.pw;
+    }
+  }
+
+  // Tap and channel of this thread's chunk in MAC iteration `it`.
+  struct Tap {
+    int r, s;
+    uint32_t cofs;  // byte offset of the chunk's channels within a pixel
+    bool ok;        // inside the reduction
+  };
+  SKG_DEV Tap tap_of(int it) const {
+    const int kk = it * Cfg::TK + chunk * 8;
+    const uint32_t t = fdiv((uint32_t)kk, div_cin);
+    const int ci = kk - (int)t * cin;
+    const uint32_t r = fdiv(t, div_s);
+    Tap tp;
+    tp.r = (int)r;
+    tp.s = (int)t - (int)r * S;
+    tp.cofs = chan0 + (uint32_t)ci * 2;
+    tp.ok = kk < kred;
+    return tp;
+  }
+
+  // Activation row u of this thread for tap tp, or kOOB.  Evaluated without
+  // branches.
+  SKG_DEV uint32_t a_off(int u, const Tap& tp, bool live) const {
+    int hi, wi;
+    bool ok = live & tp.ok & (pn[u] >= 0);
+    if constexpr (!DGRAD) {
+      hi = py[u] + tp.r;
+      wi = px[u] + tp.s;
+    } else {
+      const int t = py[u] - tp.r, v = px[u] - tp.s;
+      hi = (int)fdiv((uint32_t)t, div_sh);
+      wi = (int)fdiv((uint32_t)v, div_sw);
+      ok = ok & (t >= 0) & (v >= 0) & (hi * sh == t) & (wi * sw == v);
+    }
+    ok = ok & ((uint32_t)hi < (uint32_t)act_h) & ((uint32_t)wi < (uint32_t)act_w);
+    uint32_t off = (uint32_t)((pn[u] + hi) * act_w + wi) * act_c2 + tp.cofs;
+    asm volatile("" : "+v"(off));
+    return ok ? off : kOOB;
+  }
+
+  template <bool IS_A>
+  SKG_DEV void issue_group(int it, SKG_LDS char* slot, bool live) const {
+    if constexpr (IS_A) {
+      const Tap tp = tap_of(it);
+#pragma unroll
+      for (int u = 0; u < UA; ++u)
+        dma16(ra, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), a_off(u, tp, live));
+    } else {
+      const uint32_t kb = (uint32_t)it * Cfg::RB;
+      const bool ok = live && kb < limb;
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        dma16(rb, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), ok ? offb + u * stepb + kb : kOOB);
+    }
+  }
+
+  SKG_DEV void issue_live(int j, int it, SKG_LDS char* slot, bool live) const {
+    if ((j & 1) == 0)
+      issue_group<true>(it, slot, live);
+    else
+      issue_group<false>(it, slot, live);
+  }
+  SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
+
+  // Spread refill (256x256 tiles): B group of one iteration, A group of the
+  // next, one DMA instruction at a time among the MFMAs.
+  struct Refill {
+    SKG_LDS char* slot_b;
+    SKG_LDS char* slot_a;
+    int it_b, it_a;
+    bool live_b, live_a;
+    Tap tap_a;
+  };
+  SKG_DEV void finish_refill(Refill& r) const { r.tap_a = tap_of(r.it_a); }
+  template <int N>
+  SKG_DEV void refill(const Refill& r) const {
+    if constexpr (N < UB) {
+      const uint32_t kb = (uint32_t)r.it_b * Cfg::RB;
+      const bool ok = r.live_b && kb < limb;
+      dma16(rb, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + wave * 1024), ok ? offb + N * stepb + kb : kOOB);
+    } else {
+      constexpr int U = N - UB;
+      dma16(ra, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + wave * 1024), a_off(U, r.tap_a, r.live_a));
+    }
+  }
+};
+
+template <class Cfg, bool DGRAD>
+struct ConvProblem {
+  typedef ConvParams Params;
+  static constexpr int kScaleInc = 1;  // no scales
+  typedef ConvGrpLoader<Cfg, DGRAD> Loader;
+
+  SKG_DEV static void coords(const Params& c, const KPlan& p, int tile, int& group, int& m0, int& n0) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    group = tn / c.nt_per_group;
+    n0 = (tn - group * c.nt_per_group) * Cfg::TN;
+    m0 = tm * Cfg::TM;
+  }
+  SKG_DEV static void setup(const Params& c, const KPlan& p, int tile, Loader& ld, OutTile& out, int tid) {
+    int group, m0, n0;
+    coords(c, p, tile, group, m0, n0);
+    ld.init(c, group, m0, n0, tid);
+    out = out_tile(c, p, tile);
+  }
+  SKG_DEV static OutTile out_tile(const Params& c, const KPlan& p, int tile) {
+    int group, m0, n0;
+    coords(c, p, tile, group, m0, n0);
+    const int esz = c.dtype_out == DT_F32 ? 4 : 2;
+    OutTile o;
+    // The output is GEMM-M rows of out_c channels; the group's GEMM-N
+    // columns start at channel group * npg.
+    o.base = c.out + ((size_t)m0 * c.out_c + group * c.npg + n0) * esz;
+    o.sa = nullptr;
+    o.sb = nullptr;
+    o.ld = c.out_c;
+    o.rows = c.gm - m0;
+    o.cols = c.npg - n0;
+    return o;
+  }
+  SKG_DEV static int dtype_c(const Params& c) { return c.dtype_out; }
+};
+
+}  // namespace skg

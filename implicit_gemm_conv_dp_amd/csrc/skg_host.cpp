@@ -24,12 +24,12 @@ constexpr int M_F8 = 1 << SKG_F8E4M3 | 1 << SKG_F8E5M2;
 
 // Must agree with the kernel instances compiled in skg_api.hip.
 const TileDesc kTiles[SKG_TILE_COUNT] = {
-    /* 128x128x32  */ {128, 128, 32, 4, M_F16 | M_BF16, M_F16 | M_BF16},
-    /* 256x256x64  */ {256, 256, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16},
-    /* 256x256x128 */ {256, 256, 128, 4, M_F8, 0},
-    /* 32x64x64    */ {32, 64, 64, 4, 0, M_F16 | M_BF16},
-    /* 128x128x64  */ {128, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16},
-    /* 256x128x64  */ {256, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16},
+    /* 128x128x32  */ {128, 128, 32, 4, M_F16 | M_BF16, M_F16 | M_BF16, 0},
+    /* 256x256x64  */ {256, 256, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
+    /* 256x256x128 */ {256, 256, 128, 4, M_F8, 0, 0},
+    /* 32x64x64    */ {32, 64, 64, 4, 0, M_F16 | M_BF16, 0},
+    /* 128x128x64  */ {128, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
+    /* 256x128x64  */ {256, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
 };
 
 // Offsets inside one buffer are 32-bit on the device (buffer resources).
@@ -268,6 +268,22 @@ GemmShape wgrad_shape(const skg_wgrad_args_t* a, const TileDesc& t) {
           ceil_div(int64_t(a->n) * ho * wo, t.tk)};
 }
 
+GemmShape conv_shape(const skg_conv_args_t* a, const TileDesc& t, bool dgrad) {
+  const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
+  const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
+  const int64_t kpg = a->k / a->groups, cpg = a->c / a->groups;
+  // Groups fold into GEMM-N with the tile count per group.
+  if (!dgrad)
+    return {ceil_div(int64_t(a->n) * ho * wo, t.tm), int64_t(a->groups) * ceil_div(kpg, t.tn),
+            ceil_div(a->r * a->s * cpg, t.tk)};
+  return {ceil_div(int64_t(a->n) * a->h * a->w, t.tm), int64_t(a->groups) * ceil_div(cpg, t.tn),
+          ceil_div(a->r * a->s * kpg, t.tk)};
+}
+
+int64_t dgrad_filter_bytes(const skg_conv_args_t* a) {
+  return ceil_div(int64_t(a->k) * a->r * a->s * (a->c / a->groups) * 2, 256) * 256;
+}
+
 int validate_gemm(const skg_gemm_args_t* a) {
   if (!a) return unsupported("null arguments");
   const TileDesc* t = tile_desc(a->tile_id);
@@ -329,6 +345,42 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
   return SKG_OK;
 }
 
+int validate_conv(const skg_conv_args_t* a, bool dgrad) {
+  if (!a) return unsupported("null arguments");
+  const TileDesc* t = tile_desc(a->tile_id);
+  if (!t) return unsupported("unknown tile id");
+  if (a->dtype != SKG_F16 && a->dtype != SKG_BF16) return unsupported("unsupported convolution dtype");
+  if (a->dtype_out != SKG_F16 && a->dtype_out != SKG_BF16 && a->dtype_out != SKG_F32)
+    return unsupported("unsupported output dtype");
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+    return unsupported("unknown stream-K CTA order");
+  if (!(t->conv_mask & (1 << a->dtype))) return unsupported("tile has no convolution instance for this dtype");
+  int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);
+  if (rc) return rc;
+  if (a->reduction == SKG_RED_ATOMIC && a->dtype_out != SKG_F32)
+    return unsupported("atomic reduction needs an fp32 output");
+  if (a->n <= 0 || a->h <= 0 || a->w <= 0 || a->c <= 0 || a->k <= 0 || a->r <= 0 || a->s <= 0)
+    return unsupported("sizes must be positive");
+  if (a->stride_h <= 0 || a->stride_w <= 0 || a->pad_h < 0 || a->pad_w < 0)
+    return unsupported("bad stride or padding");
+  if (a->groups <= 0 || a->c % a->groups || a->k % a->groups)
+    return unsupported("groups must divide C and K");
+  const int64_t cpg = a->c / a->groups, kpg = a->k / a->groups;
+  if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
+  const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
+  const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
+  if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)
+    return unsupported("empty output image");
+  const int eb = elem_bytes(a->dtype), eo = elem_bytes(a->dtype_out);
+  const int64_t xpix = int64_t(a->n) * a->h * a->w, ypix = int64_t(a->n) * ho * wo;
+  const int64_t act = (dgrad ? ypix * a->k : xpix * a->c) * eb;
+  const int64_t out = (dgrad ? xpix * a->c : ypix * a->k) * eo;
+  if (act > kMaxBufferBytes || out > kMaxBufferBytes)
+    return unsupported("activation tensor too large for 32-bit offsets");
+  if (int64_t(a->k) * a->r * a->s * cpg * eb > kMaxBufferBytes) return unsupported("filter too large");
+  return SKG_OK;
+}
+
 }  // namespace skg
 
 using namespace skg;
@@ -348,6 +400,7 @@ int skg_tile_info(int32_t tile_id, skg_tile_info_t* out) {
   out->n_waves = t->n_waves;
   out->gemm_dtypes = t->gemm_mask;
   out->wgrad_dtypes = t->wgrad_mask;
+  out->conv_dtypes = t->conv_mask;
   return SKG_OK;
 }
 

@@ -22,6 +22,7 @@ struct TileDesc {
   int tm, tn, tk, n_waves;
   int gemm_mask;   // 1 << skg_dtype accepted as GEMM A/B
   int wgrad_mask;  // 1 << skg_dtype accepted as wgrad X/dY
+  int conv_mask;   // 1 << skg_dtype accepted for forward conv / dgrad
 };
 
 const TileDesc* tile_desc(int tile_id);
@@ -47,9 +48,14 @@ int resolve_sk_order(int requested, bool wgrad);
 // Argument checks that need no device (a0 of the hot path).
 int validate_gemm(const skg_gemm_args_t* a);
 int validate_wgrad(const skg_wgrad_args_t* a);
+int validate_conv(const skg_conv_args_t* a, bool dgrad);
 
 GemmShape gemm_shape(const skg_gemm_args_t* a, const TileDesc& t);
 GemmShape wgrad_shape(const skg_wgrad_args_t* a, const TileDesc& t);
+GemmShape conv_shape(const skg_conv_args_t* a, const TileDesc& t, bool dgrad);
+// Bytes of the per-group transposed filter a dgrad run writes into the
+// workspace after the fix-up region (multiple of 256).
+int64_t dgrad_filter_bytes(const skg_conv_args_t* a);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -320,6 +320,8 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
       this->template issue_rows<false, true>(kb, nullptr, slot);
   }
   SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
+  // Per-refill set-up once its groups are known (nothing for plain rows).
+  SKG_DEV void finish_refill(Refill&) const {}
 };
 
 // ---------------------------------------------------------------------------
@@ -1058,6 +1060,7 @@ struct Engine {
       rf.it_a = iter(ja >> 1);
       rf.live_b = jb < G;
       rf.live_a = ja < G;
+      ld.finish_refill(rf);
     }
     const SKG_LDS char* sa = slot(2 * i);
     const SKG_LDS char* sb = slot(2 * i + 1);

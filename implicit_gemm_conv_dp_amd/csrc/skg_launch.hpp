@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "skg_conv.hpp"
 #include "skg_kernels.hpp"
 
 namespace skg {
@@ -19,6 +20,12 @@ struct WgradInst {
   hipError_t (*occupancy)(int*);
 };
 
+struct ConvInst {
+  hipError_t (*launch)(const ConvParams&, const KPlan&, const Scratch&, hipStream_t, hipEvent_t,
+                       hipEvent_t);
+  hipError_t (*occupancy)(int*);
+};
+
 // {nullptr, nullptr} when the (tile, dtype) pair has no compiled instance.
 // tensor_scales selects the per-tensor scale instances.
 GemmInst gemm_instance(int tile_id, int dtype, bool tensor_scales);
@@ -26,6 +33,8 @@ GemmInst gemm_instance_f16(int tile_id, bool tensor_scales);
 GemmInst gemm_instance_bf16(int tile_id, bool tensor_scales);
 GemmInst gemm_instance_f8(int tile_id, int dtype, bool tensor_scales);
 WgradInst wgrad_instance(int tile_id, int dtype);
+ConvInst fwd_instance(int tile_id, int dtype);
+ConvInst dgrad_instance(int tile_id, int dtype);
 
 // Flag-wait give-ups counted by the kernels of one instance unit (read, and
 // reset to zero when `reset`); skg_fixup_timeouts sums the units.
@@ -33,6 +42,8 @@ hipError_t wait_timeouts_gemm_f16(uint32_t* out, bool reset);
 hipError_t wait_timeouts_gemm_bf16(uint32_t* out, bool reset);
 hipError_t wait_timeouts_gemm_f8(uint32_t* out, bool reset);
 hipError_t wait_timeouts_wgrad(uint32_t* out, bool reset);
+hipError_t wait_timeouts_fwd(uint32_t* out, bool reset);
+hipError_t wait_timeouts_dgrad(uint32_t* out, bool reset);
 
 // The calling unit's own counter (each unit has its copy of the symbol).
 static inline hipError_t unit_wait_timeouts(uint32_t* out, bool reset) {

@@ -163,13 +163,14 @@ enum skg_tile {
   SKG_TILE_COUNT = 6
 };
 
-enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1 };
+enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1, SKG_OP_FWD = 2, SKG_OP_DGRAD = 3 };
 
 typedef struct skg_tile_info {
   int32_t tm, tn, tk;      /* tile in elements */
   int32_t n_waves;         /* wave64s per CTA (one flag per CTA and wave) */
   int32_t gemm_dtypes;     /* bit mask of 1 << skg_dtype accepted for GEMM A/B */
   int32_t wgrad_dtypes;    /* bit mask accepted for wgrad X/dY (0: no wgrad) */
+  int32_t conv_dtypes;     /* bit mask accepted for forward conv and dgrad (0: none) */
 } skg_tile_info_t;
 
 /* GEMM problem.  A is M x K row-major with leading dimension lda (elements),
@@ -221,6 +222,40 @@ typedef struct skg_wgrad_args {
   int32_t sk_order;        /* enum skg_sk_order */
 } skg_wgrad_args_t;
 
+/* Forward convolution and input gradient (dgrad) as implicit GEMMs on the
+ * same engine (PR #13151: the "docs" commit points the forward-convolution
+ * future-work note at the stream-K port; review items 2-3 ask for forward
+ * convolution on the family-agnostic partitioner).  Layouts as for wgrad:
+ * NHWC activations, KRSC filter W (K x R x S x C/groups, the filter that
+ * skg_run_wgrad differentiates), Ho = (h + 2*pad_h - r)/stride_h + 1,
+ * dilation 1, group g maps input channels [g*C/groups, (g+1)*C/groups) to
+ * output channels [g*K/groups, (g+1)*K/groups).
+ *   forward  act = X (n,h,w,c), out = Y (n,Ho,Wo,k):
+ *            Y[n][ho][wo][k] = sum_{r,s,c'} X[n][ho*sh-ph+r][wo*sw-pw+s][g*Cpg+c'] W[k][r][s][c']
+ *            GEMM M = n*Ho*Wo, N = K/groups per group, reduction R*S*Cpg;
+ *   dgrad    act = dY (n,Ho,Wo,k), out = dX (n,h,w,c): the adjoint of the
+ *            forward map in X; GEMM M = n*h*w, N = C/groups per group,
+ *            reduction R*S*Kpg.  Its run call first writes the filter
+ *            transposed per group into the workspace (plan.aux_bytes), so
+ *            both operands are contiguous along the reduction; with a stride
+ *            above 1 the taps that reach no output pixel are multiplied as
+ *            zeros (the MAC iterations are those of the stride-1 problem).
+ * act and filt have type dtype (f16 or bf16); out has dtype_out (f16, bf16,
+ * or f32, which the atomic reduction needs).  Channels per group (C/groups
+ * and K/groups) must be multiples of 8; act, filt, out 16-byte aligned.  The
+ * tiles are those whose skg_tile_info.conv_dtypes is non-zero. */
+typedef struct skg_conv_args {
+  int32_t n, h, w, c, k, r, s;
+  int32_t stride_h, stride_w, pad_h, pad_w, groups;
+  int32_t dtype;           /* SKG_F16 or SKG_BF16 (act and filt) */
+  int32_t dtype_out;       /* SKG_F16, SKG_BF16 or SKG_F32 */
+  const void* act;         /* forward: X; dgrad: dY */
+  const void* filt;        /* W, K x R x S x C/groups */
+  void* out;               /* forward: Y; dgrad: dX */
+  int32_t tile_id, mode, reduction, ctas;
+  int32_t sk_order;        /* enum skg_sk_order */
+} skg_conv_args_t;
+
 /* Resolved launch plan, returned by value so that no derived quantity is
  * recomputed elsewhere with different rounding (PR #13151, commit adding the
  * iteration partitioner).  Iterations are MAC iterations: one TM x TN x TK
@@ -244,6 +279,9 @@ typedef struct skg_plan {
   int32_t requested_mode;    /* the mode asked for; `mode` is what runs */
   int32_t slices;            /* split-K slices per tile (1 unless split-K) */
   int32_t sk_order;          /* SKG_SK_ORDER_BLOCK or SKG_SK_ORDER_XCD */
+  int64_t aux_bytes;         /* workspace after the fix-up region that the op
+                                itself uses (dgrad: the transposed filter);
+                                included in workspace_bytes */
 } skg_plan_t;
 
 /* Reason for the last non-zero status on this thread ("" if none).  The
@@ -278,6 +316,8 @@ int skg_device_info(int32_t op, int32_t tile_id, int32_t dtype_ab,
  * skg_last_error). */
 int skg_plan_gemm(const skg_gemm_args_t* args, skg_plan_t* out);
 int skg_plan_wgrad(const skg_wgrad_args_t* args, skg_plan_t* out);
+int skg_plan_fwd(const skg_conv_args_t* args, skg_plan_t* out);
+int skg_plan_dgrad(const skg_conv_args_t* args, skg_plan_t* out);
 
 /* Bytes of workspace the run call needs for these arguments: the plan's
  * workspace_bytes (PR #13151, Technical Details: Partitioner -- the flag
@@ -302,6 +342,8 @@ int skg_wgrad_workspace_bytes(const skg_wgrad_args_t* args, size_t* out);
  * rejected with -2.  stream is a hipStream_t (NULL: the null stream). */
 int skg_run_gemm(const skg_gemm_args_t* args, void* ws, size_t ws_bytes, void* stream);
 int skg_run_wgrad(const skg_wgrad_args_t* args, void* ws, size_t ws_bytes, void* stream);
+int skg_run_fwd(const skg_conv_args_t* args, void* ws, size_t ws_bytes, void* stream);
+int skg_run_dgrad(const skg_conv_args_t* args, void* ws, size_t ws_bytes, void* stream);
 
 /* Allocation-free wgrad, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

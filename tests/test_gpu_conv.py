@@ -1,0 +1,143 @@
+"""GPU parity of the forward convolution and input gradient (dgrad) as
+implicit GEMMs on the stream-K engine, against the oracle (through the C ABI).
+
+Dense, strided (dgrad: taps that reach no output pixel), grouped and
+rectangular shapes with partial M and N tiles and reduction tails; every
+conv tile x launch mode x fix-up; random data within 5e-3 (bf16 or f16
+outputs, fp32 accumulate) and integer-exact data bit for bit (fp32 outputs);
+the layer shapes of the two wgrad workloads at full size in the benchmark's
+launch of each op.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_conv_dp_amd as skg
+from implicit_gemm_conv_dp_amd import synth
+from oracle.conv import dgrad as oracle_dgrad, forward as oracle_forward
+from oracle.wgrad import out_size
+
+from helpers import assert_close, decode_out, out_buffer, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["dp", "dp_sk", "persistent"]
+REDS = ["linear", "tree", "atomic", "workspace"]
+TILES = ["256x256x64", "128x128x64", "256x128x64"]
+
+# N, H, W, C, K, R, S, stride, pad, groups
+SHAPES = {
+    "dense": (2, 9, 9, 16, 24, 3, 3, (1, 1), (1, 1), 1),
+    "strided": (3, 11, 10, 32, 16, 3, 3, (2, 2), (1, 1), 1),
+    "grouped": (2, 12, 12, 64, 32, 3, 3, (2, 2), (1, 1), 4),
+    "wide": (1, 17, 15, 144, 40, 3, 2, (1, 2), (1, 0), 1),
+    "deep": (2, 8, 8, 264, 136, 3, 3, (1, 1), (1, 1), 1),
+}
+
+
+def inputs(op, shape, fmt, integer, seed):
+    n, h, w, c, k, r, s, st, pd, g = shape
+    ho, wo = out_size(h, w, r, s, st[0], st[1], pd[0], pd[1])
+    na = n * h * w * c if op == "fwd" else n * ho * wo * k
+    nw = k * r * s * (c // g)
+    if integer:
+        act = synth.integer_codes(fmt, na, seed, 0.5)
+        filt = synth.integer_codes(fmt, nw, seed + 1, 0.5)
+    else:
+        act = synth.to_codes(synth.draw("uniform", na, seed), fmt)
+        filt = synth.to_codes(synth.draw("uniform", nw, seed + 1), fmt)
+    if op == "fwd":
+        R = oracle_forward(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    else:
+        R = oracle_dgrad(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    return act, filt, R.reshape(-1, R.shape[-1])
+
+
+def run(op, act, filt, shape, fmt, fmt_out, tile, mode, red, ctas, ws=None):
+    n, h, w, c, k, r, s, st, pd, g = shape
+    ho, wo = out_size(h, w, r, s, st[0], st[1], pd[0], pd[1])
+    nout = n * ho * wo * k if op == "fwd" else n * h * w * c
+    out = out_buffer(fmt_out, nout)
+    call = skg.fwd if op == "fwd" else skg.dgrad
+    plan = call(to_dev(act, fmt), to_dev(filt, fmt), out, workspace=ws, n=n, h=h, w=w, c=c, k=k,
+                r=r, s=s, stride=st, pad=pd, groups=g, dtype=fmt, dtype_out=fmt_out, tile=tile,
+                mode=mode, reduction=red, ctas=ctas)
+    torch.cuda.synchronize()
+    cols = k if op == "fwd" else c
+    return decode_out(out, fmt_out).reshape(-1, cols), plan
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_random_all_modes_and_fixups(op, name, tile):
+    shape = SHAPES[name]
+    fmt = "bf16" if name in ("grouped", "wide") else "f16"
+    act, filt, R = inputs(op, shape, fmt, False, 5)
+    k = 0
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            for ctas in (3, 5, 11):
+                fmt_out = "f32" if red == "atomic" else ("bf16", "f16", "f32")[k % 3]
+                k += 1
+                Y, plan = run(op, act, filt, shape, fmt, fmt_out, tile, mode, red, ctas)
+                assert_close(Y, R, fmt, "%s %s %s %s %s ctas=%d -> %s" % (op, name, tile, mode, red,
+                                                                         ctas, fmt_out))
+                if mode == "dp":
+                    break
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_integer_exact_all_modes_and_fixups(op, name, tile):
+    shape = SHAPES[name]
+    act, filt, R = inputs(op, shape, "bf16", True, 31)
+    assert np.array_equal(R.astype(np.float32).astype(np.float64), R)
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            Y, plan = run(op, act, filt, shape, "bf16", "f32", tile, mode, red, 7)
+            if mode != "dp":
+                assert plan["sk_ctas"] in (0, 7)
+            assert np.array_equal(Y, R), "%s %s %s %s %s not bit-exact" % (op, name, tile, mode, red)
+
+
+def test_plans_reach_shared_tiles():
+    # The matrix above must exercise stream-K tiles shared by several CTAs.
+    n, h, w, c, k, r, s, st, pd, g = SHAPES["deep"]
+    for call in (skg.plan_fwd, skg.plan_dgrad):
+        p = call(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st, pad=pd, groups=g, dtype="bf16",
+                 dtype_out="f32", tile="128x128x64", mode="dp_sk", reduction="tree", ctas=7)
+        assert p["sk_ctas"] == 7 and p["max_contrib"] >= 2, p
+
+
+LAYERS = {
+    "n32_56x56_c256_k256_3x3": (32, 56, 56, 256, 256, 3, 3, (1, 1), (1, 1), 1, "f16"),
+    "n64_28x28_c512_k512_g32_3x3_s2": (64, 28, 28, 512, 512, 3, 3, (2, 2), (1, 1), 32, "bf16"),
+}
+
+
+@pytest.mark.parametrize("layer", list(LAYERS))
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_layer_full_size(op, layer):
+    *shape, fmt = LAYERS[layer]
+    shape = tuple(shape)
+    n, h, w, c, k, r, s, st, pd, g = shape
+    ho, wo = out_size(h, w, r, s, st[0], st[1], pd[0], pd[1])
+    na = n * h * w * c if op == "fwd" else n * ho * wo * k
+    act = synth.to_codes(synth.draw("uniform", na, 91), fmt)
+    filt = synth.to_codes(synth.draw("uniform", k * r * s * (c // g), 92), fmt)
+    if op == "fwd":
+        R = oracle_forward(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    else:
+        R = oracle_dgrad(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    R = R.reshape(-1, R.shape[-1])
+    tile = "256x256x64" if g == 1 else "128x128x64"
+    for mode, red in (("dp_sk", "tree"), ("persistent", "workspace")):
+        Y, plan = run(op, act, filt, shape, fmt, "f32", tile, mode, red, 256)
+        assert_close(Y, R, fmt, "%s %s %s %s" % (op, layer, mode, red))
