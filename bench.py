@@ -49,8 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="headline workload (value, roofline, cpu_baseline)")
+    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 10)),
+                    help="headline workload (value, roofline, cpu_baseline); 6-9 are the "
+                         "forward and dgrad convolutions of the two wgrad layers")
     ap.add_argument("--no-table", action="store_true",
                     help="time the headline workload only (no table of all five)")
     ap.add_argument("--mode", default=None)
@@ -118,6 +119,12 @@ def measured_traffic(path, name, tile, mode, red, ctas):
 
 def alg_bytes(wl):
     """Each input read once plus the output written once."""
+    if wl.op in ("fwd", "dgrad"):
+        ho, wo = wl.out_hw
+        x, y = wl.n * wl.h * wl.w * wl.c, wl.n * ho * wo * wl.k
+        eo = 4 if wl.dtype_out == "f32" else 2
+        filt = 2 * wl.k * wl.r * wl.s * (wl.c // wl.groups)
+        return (2 * x + eo * y if wl.op == "fwd" else 2 * y + eo * x) + filt
     if wl.op == "gemm":
         eab = 1 if wl.dtype_ab in ("e4m3", "e5m2") else 2
         ec = 4 if wl.dtype_c == "f32" else 2
@@ -234,7 +241,14 @@ class Runner:
             a = a.view(np.uint8) if a.dtype.itemsize == 1 else a.view(np.int16)
             return torch.from_numpy(a).to(dev)
 
-        if wl.op == "gemm":
+        if wl.op in ("fwd", "dgrad"):
+            ho, wo = wl.out_hw
+            self.a, self.b = up(self.inp["act"]), up(self.inp["filt"])
+            nout = wl.n * ho * wo * wl.k if wl.op == "fwd" else wl.n * wl.h * wl.w * wl.c
+            self.out = torch.empty(nout, dtype=torch.float32 if wl.dtype_out == "f32" else torch.int16,
+                                   device=dev)
+            self.dtype = wl.dtype
+        elif wl.op == "gemm":
             self.a, self.b = up(self.inp["A"]), up(self.inp["B"])
             self.sa = torch.from_numpy(self.inp["scale_a"]).to(dev) if wl.scales else None
             self.sb = torch.from_numpy(self.inp["scale_b"]).to(dev) if wl.scales else None
@@ -251,7 +265,13 @@ class Runner:
     def set_launch(self, tile, mode, red, ctas, sk_order):
         wl, skg = self.wl, self.skg
         self.tile, self.mode, self.red, self.ctas = tile, mode, red, ctas
-        if wl.op == "gemm":
+        if wl.op in ("fwd", "dgrad"):
+            self.kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s,
+                           stride=wl.stride, pad=wl.pad, groups=wl.groups, dtype=wl.dtype,
+                           dtype_out=wl.dtype_out, tile=tile, mode=mode, reduction=red, ctas=ctas,
+                           sk_order=sk_order)
+            self.plan = (skg.plan_fwd if wl.op == "fwd" else skg.plan_dgrad)(**self.kw)
+        elif wl.op == "gemm":
             self.kw = dict(M=wl.M, N=wl.N, K=wl.K, dtype_ab=wl.dtype_ab, dtype_c=wl.dtype_c,
                            tile=tile, mode=mode, reduction=red, ctas=ctas,
                            scale_mode=wl.scale_mode, sk_order=sk_order)
@@ -264,7 +284,10 @@ class Runner:
         self.ws = skg.workspace_for(self.plan, self.dev)
 
     def step(self):
-        if self.wl.op == "gemm":
+        if self.wl.op in ("fwd", "dgrad"):
+            (self.skg.fwd if self.wl.op == "fwd" else self.skg.dgrad)(
+                self.a, self.b, self.out, workspace=self.ws, **self.kw)
+        elif self.wl.op == "gemm":
             self.skg.gemm(self.a, self.b, self.out, self.sa, self.sb, workspace=self.ws, **self.kw)
         else:
             self.skg.wgrad(self.a, self.b, self.out, workspace=self.ws, **self.kw)
@@ -300,7 +323,7 @@ class Runner:
 def roofline_of(wl, kernel_ms, dtype, tile, mode, red, ctas, traffic_path, pool=None):
     """Bound, achieved rate, peak and fraction of one kernel time."""
     flops = wl.flops()
-    if wl.op == "wgrad" and wl.groups > 1:
+    if wl.op != "gemm" and wl.groups > 1:
         achieved = alg_bytes(wl) / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
@@ -328,8 +351,10 @@ def table(args, dev, headline_runner):
     import torch
     from implicit_gemm_conv_dp_amd import synth
     rows = []
-    for i in sorted(synth.WORKLOADS):
-        wl = synth.WORKLOADS[i]
+    allw = dict(synth.WORKLOADS)
+    allw.update(synth.LAYER_WORKLOADS)
+    for i in sorted(allw):
+        wl = allw[i]
         t0 = time.perf_counter()
         if headline_runner is not None and i == args.workload:
             r = headline_runner
@@ -351,7 +376,7 @@ def table(args, dev, headline_runner):
         for key in ("pool_cap", "frac_of_pool_cap", "traffic"):
             if key in roof:
                 row[key] = roof[key]
-        if wl.op == "wgrad":
+        if wl.op != "gemm":
             # The same kernel with every tile data-parallel (grid = tiles).
             r.set_launch(wl.tile, "dp", "linear", wl.ctas, "auto")
             dk, ds = r.timed(TABLE_WARMUP // 5, TABLE_REPEAT // 5)
@@ -359,7 +384,7 @@ def table(args, dev, headline_runner):
                               "step_us": stats_us(ds)}
             row["speedup_vs_dp_only"] = row["dp_only"]["step_us"]["median"] / \
                 row["step_us"]["median"]
-            if wl.groups > 1:
+            if wl.op == "wgrad" and wl.groups > 1:
                 # Cold caches: a 512 MB scrub buffer rewritten before every
                 # launch (outside the timed region).
                 r.set_launch(wl.tile, wl.modes[0], wl.reductions[0], wl.ctas, "auto")
@@ -396,7 +421,7 @@ def main():
     import implicit_gemm_conv_dp_amd as skg
     from implicit_gemm_conv_dp_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS.get(args.workload) or synth.LAYER_WORKLOADS[args.workload]
     if args.dtype or args.scale_mode:
         if wl.op != "gemm" or not wl.scales:
             sys.exit("--dtype / --scale-mode apply to the fp8 GEMM workload only")

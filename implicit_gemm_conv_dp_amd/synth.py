@@ -147,6 +147,57 @@ class WgradWorkload:
         }
 
 
+@dataclass
+class ConvWorkload:
+    """Forward convolution (op "fwd": act = X, out = Y) or its input gradient
+    (op "dgrad": act = dY, out = dX) of one layer; filt is the KRSC filter."""
+    index: int
+    name: str
+    op: str
+    n: int
+    h: int
+    w: int
+    c: int
+    k: int
+    r: int
+    s: int
+    stride: tuple
+    pad: tuple
+    groups: int
+    dtype: str
+    dtype_out: str
+    dist: str
+    tile: str
+    modes: tuple
+    reductions: tuple
+    ctas: int
+
+    @property
+    def seed(self):
+        return 1000 + self.index
+
+    @property
+    def out_hw(self):
+        ho = (self.h + 2 * self.pad[0] - self.r) // self.stride[0] + 1
+        wo = (self.w + 2 * self.pad[1] - self.s) // self.stride[1] + 1
+        return ho, wo
+
+    def flops(self):
+        """Algorithmic FLOPs of the layer (the same for both ops)."""
+        ho, wo = self.out_hw
+        return 2.0 * self.n * ho * wo * self.k * self.r * self.s * (self.c // self.groups)
+
+    def inputs(self):
+        ho, wo = self.out_hw
+        s = self.seed * 10
+        na = self.n * self.h * self.w * self.c if self.op == "fwd" else self.n * ho * wo * self.k
+        return {
+            "act": to_codes(draw(self.dist, na, s + 0), self.dtype),
+            "filt": to_codes(draw(self.dist, self.k * self.r * self.s * (self.c // self.groups),
+                                  s + 1), self.dtype),
+        }
+
+
 # The five workloads.  Tiles for 1, 2 and 4 are the ones the workloads name;
 # 3 and 5 use the tiles measured fastest for them.  Workload 4 runs its pool
 # at the resident capacity of the 32x64x64 tile (two CTAs per CU), which
@@ -165,4 +216,23 @@ WORKLOADS = {
     5: GemmWorkload(5, "gemm_e4m3_8192x8192x8192_rowcol_scales", 8192, 8192, 8192, "e4m3",
                     "bf16", "normal", "256x256x128", ("persistent",), ("workspace",), 256,
                     scales=True),
+}
+
+# The other two convolutions of the two wgrad layers (forward and input
+# gradient), on the same engine, in the launches measured fastest: 256x256x64
+# tiles, persistent, tree fix-up for the dense layer; 128x128x64 tiles for
+# the grouped one (16 channels per group; every plan is all-DP there).
+LAYER_WORKLOADS = {
+    6: ConvWorkload(6, "fwd_f16_n32_56x56_c256_k256_3x3", "fwd", 32, 56, 56, 256, 256, 3, 3,
+                    (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
+                    ("tree",), 256),
+    7: ConvWorkload(7, "dgrad_f16_n32_56x56_c256_k256_3x3", "dgrad", 32, 56, 56, 256, 256, 3, 3,
+                    (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
+                    ("tree",), 256),
+    8: ConvWorkload(8, "fwd_bf16_n64_28x28_c512_k512_g32_3x3_s2", "fwd", 64, 28, 28, 512, 512, 3,
+                    3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
+                    ("tree",), 256),
+    9: ConvWorkload(9, "dgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", "dgrad", 64, 28, 28, 512, 512,
+                    3, 3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
+                    ("tree",), 256),
 }
