@@ -16,6 +16,11 @@ stored mantissa bits:
                E=5, B=15, M=2, infinities and NaNs as in IEEE-754; its codes
                are the upper bytes of binary16 codes.
 
+* ``e8m0``  -- the OCP Microscaling (MX) shared block scale: an unsigned
+               8-bit exponent with bias 127 and no mantissa, value
+               2^(code - 127) for codes 0..254; code 255 is NaN (decode only,
+               ``decode_e8m0``: scales are drawn as codes, never rounded).
+
 Decoding is exact in float64.  Encoding rounds to nearest, ties to even.
 Values beyond the largest finite number become +/-inf for f16 / bf16 / e5m2
 (IEEE overflow under round-to-nearest) and saturate to +/-448 for e4m3 (our reading:
@@ -109,3 +114,12 @@ def encode(fmt, x):
     code = np.where(np.isnan(x), nan_code, code)
     code = code | (sign << (ebits + mbits))
     return code.astype(storage_dtype(fmt))
+
+
+def decode_e8m0(codes):
+    """Exact float64 value of OCP MX E8M0 scale codes: 2^(code - 127), NaN
+    for 255."""
+    c = np.asarray(codes).astype(np.int64)
+    if ((c < 0) | (c > 255)).any():
+        raise ValueError("e8m0 codes are bytes")
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))

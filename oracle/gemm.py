@@ -21,7 +21,7 @@ float64 matmul (a library primitive); there is no blocking or reordering here.
 
 import numpy as np
 
-from .codecs import decode
+from .codecs import decode, decode_e8m0
 
 
 def operand_matrix(fmt, codes, rows, cols, ld):
@@ -95,3 +95,48 @@ def gemm_entry(fmt, a_codes, b_codes, m, n, K, lda=None, ldb=None,
     if scale_b is not None:
         v *= float(np.asarray(scale_b).reshape(-1)[n_s])
     return v
+
+
+# OCP Microscaling: one shared scale per block of this many consecutive
+# elements along the reduction.
+MX_BLOCK = 32
+
+
+def gemm_mx(fmt, a_codes, b_codes, sa_codes, sb_codes, M, N, K):
+    """float64 ``R`` (M x N) of a block-scaled (MX) GEMM in the rcr layout:
+
+        R[m][n] = sum over blocks b of K (32 elements each) of
+                  2^(sa[m][b] - 127) * 2^(sb[n][b] - 127)
+                  * sum_{k in block b} a(m, k) * b(k, n)
+
+    with ``sa`` M x K/32 and ``sb`` N x K/32 E8M0 codes, row-major (the
+    scaled-operand definition of the OCP Microscaling formats, applied to
+    each operand's 32-element blocks along K; the gfx950 scaled f8f6f4 MFMA
+    takes one such scale per 32-element block, the "mfma.scale...f8f6f4"
+    instruction named in the wgrad page's arch table, for the MX / microscaling
+    bquant variants of the "gemm_rowcolquant dispatcher bridge" PR's combined
+    follow-up).  K must be a multiple of 32."""
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of the MX block")
+    nb = K // MX_BLOCK
+    a = operand_matrix(fmt, a_codes, M, K, K)
+    bt = operand_matrix(fmt, b_codes, N, K, K)
+    sa = decode_e8m0(np.asarray(sa_codes).reshape(M, nb))
+    sb = decode_e8m0(np.asarray(sb_codes).reshape(N, nb))
+    r = np.zeros((M, N))
+    for blk in range(nb):
+        ks = slice(blk * MX_BLOCK, (blk + 1) * MX_BLOCK)
+        r += (sa[:, blk:blk + 1] * sb[:, blk][None, :]) * (a[:, ks] @ bt[:, ks].T)
+    return r
+
+
+def gemm_mx_entry(fmt, a_codes, b_codes, sa_codes, sb_codes, m, n, K):
+    """One output element of ``gemm_mx`` computed on its own."""
+    nb = K // MX_BLOCK
+    a_row = decode(fmt, np.asarray(a_codes).reshape(-1)[m * K:(m + 1) * K])
+    b_col = decode(fmt, np.asarray(b_codes).reshape(-1)[n * K:(n + 1) * K])
+    sa = decode_e8m0(np.asarray(sa_codes).reshape(-1)[m * nb:(m + 1) * nb])
+    sb = decode_e8m0(np.asarray(sb_codes).reshape(-1)[n * nb:(n + 1) * nb])
+    return float(sum(sa[b] * sb[b] * np.dot(a_row[b * MX_BLOCK:(b + 1) * MX_BLOCK],
+                                            b_col[b * MX_BLOCK:(b + 1) * MX_BLOCK])
+                     for b in range(nb)))

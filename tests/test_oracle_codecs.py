@@ -122,3 +122,15 @@ def test_overflow_rules():
     assert codecs.decode("e5m2", codecs.encode("e5m2", [61439.0]))[0] == 57344.0
     t = torch.tensor([61440.0, 61439.0]).to(torch.float8_e5m2).double().numpy()
     assert np.isinf(t[0]) and t[1] == 57344.0
+
+
+def test_e8m0_every_code_against_torch():
+    # The OCP MX shared-scale format, all 256 codes, against torch's own
+    # float8_e8m0fnu decoding (a library routine).
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = codecs.decode_e8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[126] == 0.5

@@ -96,3 +96,85 @@ def test_per_tensor_scales_by_triple_loop(fmt):
         gemm(fmt, a, b, M, N, K, scale_a=[sa, sa], scale_mode="tensor")
     with pytest.raises(ValueError):
         gemm(fmt, a, b, M, N, K, scale_mode="block")
+
+
+# --- MX (e8m0 block-scaled) GEMM -------------------------------------------
+from oracle.gemm import MX_BLOCK, gemm_mx, gemm_mx_entry  # noqa: E402
+
+
+def mx_operands(rng, M, N, K, fmt="e4m3", lo=120, hi=134):
+    a = codecs.encode(fmt, rng.integers(-6, 7, size=M * K).astype(np.float64) / 4)
+    b = codecs.encode(fmt, rng.integers(-6, 7, size=N * K).astype(np.float64) / 4)
+    sa = rng.integers(lo, hi + 1, size=M * (K // MX_BLOCK)).astype(np.uint8)
+    sb = rng.integers(lo, hi + 1, size=N * (K // MX_BLOCK)).astype(np.uint8)
+    return a, b, sa, sb
+
+
+def test_mx_equal_block_scales_is_per_tensor():
+    # Every block scale equal: 2^(ea-127) * 2^(eb-127) times the plain GEMM,
+    # which is the per-tensor scaled GEMM of the pinned oracle.
+    rng = np.random.default_rng(21)
+    M, N, K = 9, 7, 128
+    a, b, _, _ = mx_operands(rng, M, N, K)
+    sa = np.full(M * 4, 130, np.uint8)
+    sb = np.full(N * 4, 124, np.uint8)
+    got = gemm_mx("e4m3", a, b, sa, sb, M, N, K)
+    ref = gemm("e4m3", a, b, M, N, K, scale_a=[2.0 ** 3], scale_b=[2.0 ** -3], scale_mode="tensor")
+    assert np.array_equal(got, ref)
+
+
+def test_mx_row_constant_scales_are_rowcol():
+    # Scales that vary by row (column) but not by block: the per-row /
+    # per-column scaled GEMM.
+    rng = np.random.default_rng(22)
+    M, N, K = 6, 5, 96
+    a, b, _, _ = mx_operands(rng, M, N, K, "e5m2")
+    ea = rng.integers(120, 135, size=M)
+    eb = rng.integers(120, 135, size=N)
+    sa = np.repeat(ea, K // MX_BLOCK).astype(np.uint8)
+    sb = np.repeat(eb, K // MX_BLOCK).astype(np.uint8)
+    got = gemm_mx("e5m2", a, b, sa, sb, M, N, K)
+    ref = gemm("e5m2", a, b, M, N, K, scale_a=2.0 ** (ea - 127.0), scale_b=2.0 ** (eb - 127.0))
+    assert np.array_equal(got, ref)
+
+
+def test_mx_blocks_split_the_reduction():
+    # R = sum over blocks of each block's scales times the plain GEMM of that
+    # block's K slice (so a scale applied to the wrong block, or a block of
+    # the wrong width, fails).
+    rng = np.random.default_rng(23)
+    M, N, K = 5, 4, 160
+    a, b, sa, sb = mx_operands(rng, M, N, K)
+    nb = K // MX_BLOCK
+    A2, B2 = a.reshape(M, K), b.reshape(N, K)
+    S_a, S_b = sa.reshape(M, nb), sb.reshape(N, nb)
+    ref = np.zeros((M, N))
+    for blk in range(nb):
+        sl = slice(blk * MX_BLOCK, (blk + 1) * MX_BLOCK)
+        part = gemm("e4m3", np.ascontiguousarray(A2[:, sl]), np.ascontiguousarray(B2[:, sl]),
+                    M, N, MX_BLOCK)
+        ref += part * (2.0 ** (S_a[:, blk:blk + 1] - 127.0)) * (2.0 ** (S_b[:, blk][None, :] - 127.0))
+    assert np.array_equal(gemm_mx("e4m3", a, b, sa, sb, M, N, K), ref)
+
+
+def test_mx_triple_loop_and_entry():
+    rng = np.random.default_rng(24)
+    M, N, K = 3, 4, 64
+    a, b, sa, sb = mx_operands(rng, M, N, K)
+    ad = codecs.decode("e4m3", a).reshape(M, K)
+    bd = codecs.decode("e4m3", b).reshape(N, K)
+    R = gemm_mx("e4m3", a, b, sa, sb, M, N, K)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += ad[m, k] * bd[n, k] * 2.0 ** (int(sa[m * 2 + k // 32]) - 127) * \
+                    2.0 ** (int(sb[n * 2 + k // 32]) - 127)
+            assert R[m, n] == acc
+            assert gemm_mx_entry("e4m3", a, b, sa, sb, m, n, K) == R[m, n]
+
+
+def test_mx_rejects_partial_blocks():
+    with pytest.raises(ValueError):
+        gemm_mx("e4m3", np.zeros(40, np.uint8), np.zeros(40, np.uint8), np.zeros(1, np.uint8),
+                np.zeros(1, np.uint8), 1, 1, 40)
