@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 10)),
+    ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 11)),
                     help="headline workload (value, roofline, cpu_baseline); 6-9 are the "
-                         "forward and dgrad convolutions of the two wgrad layers")
+                         "forward and dgrad convolutions of the two wgrad layers, 10 the fp8 "
+                         "GEMM with MX block scales")
     ap.add_argument("--no-table", action="store_true",
                     help="time the headline workload only (no table of all five)")
     ap.add_argument("--mode", default=None)
@@ -128,7 +129,10 @@ def alg_bytes(wl):
     if wl.op == "gemm":
         eab = 1 if wl.dtype_ab in ("e4m3", "e5m2") else 2
         ec = 4 if wl.dtype_c == "f32" else 2
-        extra = (4 * (wl.M + wl.N) if wl.scale_mode == "rowcol" else 8) if wl.scales else 0
+        extra = 0
+        if wl.scales:
+            extra = {"rowcol": 4 * (wl.M + wl.N), "tensor": 8,
+                     "mx": (wl.M + wl.N) * (wl.K // 32)}[wl.scale_mode]
         return eab * (wl.M * wl.K + wl.N * wl.K) + ec * wl.M * wl.N + extra
     ho, wo = wl.out_hw
     return 2 * (wl.n * wl.h * wl.w * wl.c + wl.n * ho * wo * wl.k) + \
@@ -352,7 +356,7 @@ def table(args, dev, headline_runner):
     from implicit_gemm_conv_dp_amd import synth
     rows = []
     allw = dict(synth.WORKLOADS)
-    allw.update(synth.LAYER_WORKLOADS)
+    allw.update(synth.NEXT_WORKLOADS)
     for i in sorted(allw):
         wl = allw[i]
         t0 = time.perf_counter()
@@ -421,7 +425,7 @@ def main():
     import implicit_gemm_conv_dp_amd as skg
     from implicit_gemm_conv_dp_amd import synth
 
-    wl = synth.WORKLOADS.get(args.workload) or synth.LAYER_WORKLOADS[args.workload]
+    wl = synth.WORKLOADS.get(args.workload) or synth.NEXT_WORKLOADS[args.workload]
     if args.dtype or args.scale_mode:
         if wl.op != "gemm" or not wl.scales:
             sys.exit("--dtype / --scale-mode apply to the fp8 GEMM workload only")

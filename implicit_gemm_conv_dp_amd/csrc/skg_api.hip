@@ -62,7 +62,7 @@ int device_capacity(int op, int tile_id, int dtype, int* cus, int* per_cu) {
   int occ = 0;
   hipError_t e;
   if (op == SKG_OP_GEMM) {
-    GemmInst in = gemm_instance(tile_id, dtype, false);
+    GemmInst in = gemm_instance(tile_id, dtype, SKG_SCALE_ROWCOL);
     if (!in.occupancy) return unsupported("no GEMM instance for this tile and dtype");
     e = in.occupancy(&occ);
   } else if (op == SKG_OP_WGRAD) {
@@ -551,7 +551,9 @@ int skg_run_gemm(const skg_gemm_args_t* a, void* ws, size_t ws_bytes, void* stre
     if ((a->scale_a && !aligned(a->scale_a, 16)) || (a->scale_b && !aligned(a->scale_b, 16)))
       return unsupported("scales must be 16-byte aligned");
     const TileDesc* t = tile_desc(a->tile_id);
-    GemmInst inst = gemm_instance(a->tile_id, a->dtype_ab, a->scale_mode == SKG_SCALE_TENSOR);
+    if (a->scale_mode == SKG_SCALE_MX_E8M0 && (!a->scale_a || !a->scale_b))
+      return unsupported("MX block scales need both scale arrays");
+    GemmInst inst = gemm_instance(a->tile_id, a->dtype_ab, a->scale_mode);
     if (!inst.launch) return unsupported("no GEMM instance for this tile and dtype");
     int cus = 0, per_cu = 0;
     rc = device_capacity(SKG_OP_GEMM, a->tile_id, a->dtype_ab, &cus, &per_cu);

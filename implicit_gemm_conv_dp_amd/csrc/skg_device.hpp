@@ -54,6 +54,15 @@ SKG_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voff) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane straight into LDS (lane i at lds_base + 4*i); ordered
+// like dma16, by the engine's own vmcnt waits.
+SKG_DEV void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(lds_base), "s"(r)
+               : "memory", "m0");
+}
+
 SKG_DEV uint32_t lds_addr(const SKG_LDS void* p) { return (uint32_t)(uintptr_t)p; }
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
@@ -213,6 +222,12 @@ struct MfmaF8x32 {
   typedef i32x8 frag_t;
   SKG_DEV static void run(acc_t& c, const frag_t& a, const frag_t& b) {
     c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
+  }
+  // With OCP MX block scales: each lane's operand data is one 32-element
+  // block along K (32 bytes), and the lane's E8M0 scale byte (bits 7:0 of
+  // sa / sb) multiplies that block: 2^(code - 127).
+  SKG_DEV static void run_scaled(acc_t& c, const frag_t& a, const frag_t& b, uint32_t sa, uint32_t sb) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, (int)sa, 0, (int)sb);
   }
 };
 template <int FMT>

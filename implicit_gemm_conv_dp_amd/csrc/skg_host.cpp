@@ -30,6 +30,7 @@ const TileDesc kTiles[SKG_TILE_COUNT] = {
     /* 32x64x64    */ {32, 64, 64, 4, 0, M_F16 | M_BF16, 0},
     /* 128x128x64  */ {128, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
     /* 256x128x64  */ {256, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
+    /* 128x128x128 */ {128, 128, 128, 4, M_F8, 0, 0},
 };
 
 // Offsets inside one buffer are 32-bit on the device (buffer resources).
@@ -291,8 +292,15 @@ int validate_gemm(const skg_gemm_args_t* a) {
   if (a->dtype_ab != SKG_F16 && a->dtype_ab != SKG_BF16 && a->dtype_ab != SKG_F8E4M3 &&
       a->dtype_ab != SKG_F8E5M2)
     return unsupported("unsupported A/B dtype");
-  if (a->scale_mode != SKG_SCALE_ROWCOL && a->scale_mode != SKG_SCALE_TENSOR)
+  if (a->scale_mode != SKG_SCALE_ROWCOL && a->scale_mode != SKG_SCALE_TENSOR &&
+      a->scale_mode != SKG_SCALE_MX_E8M0)
     return unsupported("unknown scale mode");
+  if (a->scale_mode == SKG_SCALE_MX_E8M0) {
+    if (a->dtype_ab != SKG_F8E4M3 && a->dtype_ab != SKG_F8E5M2)
+      return unsupported("MX block scales need fp8 or bf8 inputs");
+    if (a->tile_id != SKG_TILE_128x128x128) return unsupported("MX block scales need the 128x128x128 tile");
+    if (a->K % 128) return unsupported("MX block scales need K to be a multiple of 128");
+  }
   if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
     return unsupported("unknown stream-K CTA order");
   if (a->dtype_c != SKG_F16 && a->dtype_c != SKG_BF16 && a->dtype_c != SKG_F32)

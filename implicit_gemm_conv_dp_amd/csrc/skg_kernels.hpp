@@ -85,9 +85,13 @@ struct WgradParams {
 };
 
 // ---------------------------------------------------------------------------
-template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64>
+// MX_: the operand slots also hold each row's E8M0 block scales of the
+// iteration (4 bytes per row after the row data).
+template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64, bool MX_ = false>
 struct TileCfg {
   static constexpr int DT = DT_, TM = TM_, TN = TN_, TK = TK_, WM = WM_, WN = WN_, MN = MN_;
+  static constexpr bool MX = MX_;
+  static constexpr int SCB = MX_ ? 4 : 0;  // scale bytes per row in a slot
   static constexpr int ESZ = DT == DT_F8 || DT == DT_BF8 ? 1 : 2;
   static constexpr int RB = TK * ESZ;  // LDS row bytes (K contiguous)
   static constexpr int CPR = RB / 16;  // 16-byte chunks per row
@@ -123,9 +127,9 @@ struct TileCfg {
   // one ring of NSLOT equal slots; when TM != TN the A and B tiles differ in
   // size and each gets a ring of its own, NSLOT / 2 slots sized to fit, so
   // the LDS holds more iterations ahead.
-  static constexpr int SLOT_A = TM * RB, SLOT_B = TN * RB;
+  static constexpr int SLOT_A = TM * (RB + SCB), SLOT_B = TN * (RB + SCB);
   static constexpr bool SPLIT = TM != TN;
-  static constexpr int SLOT = (TM > TN ? TM : TN) * RB;
+  static constexpr int SLOT = (TM > TN ? TM : TN) * (RB + SCB);
   static constexpr int LDS_BUDGET = TM * TN >= 256 * 128 ? 160 * 1024 : 80 * 1024;
   static constexpr int RING_D = LDS_BUDGET / (SLOT_A + SLOT_B);  // iterations, split rings
   static constexpr int NSLOT = SPLIT ? (2 * RING_D > 8 ? 8 : 2 * RING_D)
@@ -136,7 +140,7 @@ struct TileCfg {
   // Spread the refill DMAs among the MFMAs (256x256 tiles: one resident
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
-  static constexpr bool SPREAD = TM == 256 && TN == 256;
+  static constexpr bool SPREAD = TM == 256 && TN == 256 && !MX_;
   // Resident CTAs per CU the register allocation must allow: tiles of up
   // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
   static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
@@ -324,6 +328,59 @@ struct GemmGrpLoader : DmaRows<Cfg, Cfg::RB> {
   SKG_DEV void finish_refill(Refill&) const {}
 };
 
+// GEMM with OCP MX block scales (fp8 / bf8, K a multiple of the tile's K):
+// each group also carries the E8M0 scale words of its rows for the MAC
+// iteration (4 bytes = the 4 blocks of 32 K elements a 128-byte row holds,
+// at row*(K/32) + it*4 of the row-major M x K/32 or N x K/32 scale array),
+// one 4-byte direct-to-LDS instruction per wave placed after the slot's row
+// data, so the engine's waits and barriers order them with the tile.
+template <class Cfg>
+struct MxGrpLoader : GemmGrpLoader<Cfg> {
+  typedef GemmGrpLoader<Cfg> Base;
+  typedef DmaRows<Cfg, Cfg::RB> Rows;
+  static constexpr bool kMx = true;
+  static_assert(Cfg::MX && Cfg::RB == 128 && Cfg::TK == 128, "MX: 4 scale blocks per 128-byte row");
+  static_assert(Cfg::TM % 64 == 0 && Cfg::TN % 64 == 0 && (Cfg::TM / 64) <= Cfg::NW &&
+                    Cfg::NW % (Cfg::TM / 64) == 0 && Cfg::NW % (Cfg::TN / 64) == 0,
+                "one 64-row scale chunk per wave");
+  // DMA instructions per group and thread: the rows plus one scale word.
+  static constexpr int UA = Rows::UA + 1, UB = Rows::UB + 1;
+
+  __amdgpu_buffer_rsrc_t rsa, rsb;
+  uint32_t sofa, sofb;  // this lane's scale-row byte offset (row * K/32)
+  int cha, chb;         // 64-row chunk of the tile this wave's scale DMA fills
+
+  SKG_DEV void init(const GemmParams& g, int m0, int n0, int tid) {
+    Base::init(g, m0, n0, tid);
+    const uint32_t kb32 = (uint32_t)g.K / 32;
+    const char* sa = (const char*)g.sa;
+    const char* sb = (const char*)g.sb;
+    rsa = make_rsrc(sa + (size_t)m0 * kb32, (uint32_t)(g.M - m0) * kb32);
+    rsb = make_rsrc(sb + (size_t)n0 * kb32, (uint32_t)(g.N - n0) * kb32);
+    const int lane = tid & 63;
+    cha = this->wave % (Cfg::TM / 64);
+    chb = this->wave % (Cfg::TN / 64);
+    sofa = (uint32_t)(cha * 64 + lane) * kb32;
+    sofb = (uint32_t)(chb * 64 + lane) * kb32;
+  }
+
+  SKG_DEV void scales_a(int it, SKG_LDS char* slot, bool live) const {
+    dma4(rsa, lds_addr(slot + Cfg::TM * Cfg::RB + cha * 256), live ? sofa + (uint32_t)it * 4 : kOOB);
+  }
+  SKG_DEV void scales_b(int it, SKG_LDS char* slot, bool live) const {
+    dma4(rsb, lds_addr(slot + Cfg::TN * Cfg::RB + chb * 256), live ? sofb + (uint32_t)it * 4 : kOOB);
+  }
+
+  SKG_DEV void issue_live(int j, int it, SKG_LDS char* slot, bool live) const {
+    Base::issue_live(j, it, slot, live);
+    if ((j & 1) == 0)
+      scales_a(it, slot, live);
+    else
+      scales_b(it, slot, live);
+  }
+  SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
+};
+
 // ---------------------------------------------------------------------------
 // wgrad operand loader.  GEMM-A = dY^T (row m = output channel of the group,
 // K index q = (image, ho, wo)); GEMM-B^T = im2col(X) (row = (r, s, c') with c'
@@ -470,6 +527,29 @@ struct GemmProblem {
     o.ld = g.ldc;
     o.rows = g.M - m0;
     o.cols = g.N - n0;
+    return o;
+  }
+  SKG_DEV static int dtype_c(const Params& g) { return g.dtype_c; }
+};
+
+// GEMM with MX block scales: scale_a / scale_b are the E8M0 arrays the
+// loader moves with the tiles; the epilogue applies no further scale.
+template <class Cfg>
+struct GemmMxProblem {
+  typedef GemmParams Params;
+  static constexpr int kScaleInc = 1;
+  typedef MxGrpLoader<Cfg> Loader;
+
+  SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
+                            int tid) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    ld.init(g, tm * Cfg::TM, tn * Cfg::TN, tid);
+    out = out_tile(g, p, tile);
+  }
+  SKG_DEV static OutTile out_tile(const Params& g, const KPlan& p, int tile) {
+    OutTile o = GemmProblem<Cfg>::out_tile(g, p, tile);
+    o.sa = nullptr;
+    o.sb = nullptr;
     return o;
   }
   SKG_DEV static int dtype_c(const Params& g) { return g.dtype_c; }
@@ -687,6 +767,16 @@ struct WgradProblem {
 // Data-parallel-only launches use FIX_HANDOFF.
 enum { FIX_HANDOFF = 0, FIX_ATOMIC = 1 };
 
+// Loaders that move MX block scales with the tiles declare kMx.
+template <class L, class = void>
+struct LoaderMx {
+  static constexpr bool value = false;
+};
+template <class L>
+struct LoaderMx<L, std::void_t<decltype(L::kMx)>> {
+  static constexpr bool value = L::kMx;
+};
+
 template <class Cfg, class Prob, int FIX>
 struct Engine {
   typedef typename Cfg::acc_t acc_t;
@@ -709,6 +799,11 @@ struct Engine {
   SKG_LDS char* lds;
   int tid, lane, wave, wm, wn;
   acc_t acc[Cfg::FM][Cfg::FN];
+  // MX: this iteration's and the next one's scale words per fragment, each
+  // already shifted so that byte 0 is the lane's block of k-step 0 and
+  // byte 2 that of k-step 1.
+  static constexpr bool kMx = LoaderMx<Loader>::value;
+  uint32_t msa[Cfg::FM], msb[Cfg::FN], nsa[Cfg::FM], nsb[Cfg::FN];
 
   SKG_DEV Engine(const Params& prm_, const KPlan& p_, const Scratch& s_, SKG_LDS char* lds_)
       : prm(prm_), p(p_), s(s_), lds(lds_) {
@@ -742,8 +837,16 @@ struct Engine {
                              const SKG_LDS char* sb, int ks) const {
     static_assert(RBX == 128 || Cfg::MN == 32, "block offsets keep the 64-byte swizzle");
     const int lrow = lane % Cfg::MN, lk = (lane / Cfg::MN) * Cfg::Op::OPB;
-    const int chunk0 = (ks * Cfg::Op::KB + lk) >> 4;
-    const int h1 = Cfg::OPC - 1;  // second chunk of a 32-byte operand
+    // A 32-byte fp8 operand is two 16-byte chunks.  The scaled f8f6f4 MFMA
+    // reads the first chunk of every lane as its first 32-element K block
+    // (lanes 0-31 the first 16, lanes 32-63 the next 16) and the second
+    // chunk as its second block, scaled by the upper lanes' scales (measured
+    // lane layout).  Unscaled, any arrangement common to A and B works, and
+    // the lane reads 32 contiguous bytes; with MX block scales the lane of
+    // half h reads chunks 4ks + h and 4ks + h + 2, so the instruction's
+    // blocks are the operands' blocks 2ks and 2ks + 1.
+    const int chunk0 = kMx ? ((ks * Cfg::Op::KB) >> 4) + lane / Cfg::MN : (ks * Cfg::Op::KB + lk) >> 4;
+    const int h1 = kMx ? 2 : Cfg::OPC - 1;  // second chunk of a 32-byte operand
     const uint32_t oa0 = lds_off<RBX>(wm * Cfg::WTM + lrow, chunk0);
     const uint32_t oa1 = lds_off<RBX>(wm * Cfg::WTM + lrow, chunk0 + h1);
     const uint32_t ob0 = lds_off<RBX>(wn * Cfg::WTN + lrow, chunk0);
@@ -756,14 +859,40 @@ struct Engine {
       fb[g] = frag_from<Frag>(sb + ob0 + g * Cfg::MN * RBX, sb + ob1 + g * Cfg::MN * RBX);
   }
 
-  SKG_DEV void mma(const FragA& fa, const FragB& fb) { mma_rows(fa, fb, 0, Cfg::FM); }
+  SKG_DEV void mma(const FragA& fa, const FragB& fb, int ks = 0) { mma_rows(fa, fb, 0, Cfg::FM, ks); }
 
-  SKG_DEV void mma_rows(const FragA& fa, const FragB& fb, int f0, int f1) {
+  // One MFMA of block (f, g); the B fragment goes first (transposed block),
+  // and with MX its scale is the instruction's first scale operand.
+  SKG_DEV void mfma(int f, int g, const Frag& a, const Frag& b, int ks) {
+    if constexpr (kMx)
+      Cfg::Op::run_scaled(acc[f][g], b, a, (msb[g] >> (16 * ks)) & 0xffu, (msa[f] >> (16 * ks)) & 0xffu);
+    else
+      Cfg::Op::run(acc[f][g], b, a);
+  }
+
+  SKG_DEV void mma_rows(const FragA& fa, const FragB& fb, int f0, int f1, int ks = 0) {
 #pragma unroll
     for (int f = 0; f < Cfg::FM; ++f)
       if (f >= f0 && f < f1)
 #pragma unroll
-        for (int g = 0; g < Cfg::FN; ++g) Cfg::Op::run(acc[f][g], fb[g], fa[f]);  // transposed block
+        for (int g = 0; g < Cfg::FN; ++g) mfma(f, g, fa[f], fb[g], ks);
+  }
+
+  // MX: the scale words of the iteration in slots sa (A) and sb (B): the
+  // word of the lane's row (A) or column (B), shifted right by 8 bits in
+  // the upper half of the wave, whose operand data is the second block of
+  // each k-step.
+  SKG_DEV void read_scales(uint32_t (&ra)[Cfg::FM], uint32_t (&rb)[Cfg::FN], const SKG_LDS char* sa,
+                           const SKG_LDS char* sb) const {
+    if constexpr (kMx) {
+      const int r = lane % Cfg::MN, sh = 8 * (lane / Cfg::MN);
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f)
+        ra[f] = *(const SKG_LDS uint32_t*)(sa + Cfg::TM * Cfg::RB + (wm * Cfg::WTM + f * Cfg::MN + r) * 4) >> sh;
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g)
+        rb[g] = *(const SKG_LDS uint32_t*)(sb + Cfg::TN * Cfg::RB + (wn * Cfg::WTN + g * Cfg::MN + r) * 4) >> sh;
+    }
   }
 
   // acc += A_tile * B_tile for the stage in LDS.  Fragments are double
@@ -1140,11 +1269,11 @@ struct Engine {
         if (ks == 0) ld.prep_b(iter(jb >> 1), jb < G, pb);
         if (ks == (Cfg::KSTEPS > 2 ? 1 : 0)) ld.prep_a(iter(ja >> 1), ja < G, pa);
       }
-      mma(fa[ks & 1], fb[ks & 1]);
+      mma(fa[ks & 1], fb[ks & 1], ks);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
     }
-    constexpr int CB = (Cfg::KSTEPS - 1) & 1;
-    mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2);
+    constexpr int CB = (Cfg::KSTEPS - 1) & 1, KL = Cfg::KSTEPS - 1;
+    mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2, KL);
     if constexpr (!LAST) {
       wait_groups(min(G, 2 * i + Cfg::NSLOT) - (2 * i + 4));
       lds_barrier();
@@ -1156,8 +1285,15 @@ struct Engine {
         if (ja < G) ld.issue(ja, iter(ja >> 1), slot(ja));
       }
       grp_frags(fa[CB ^ 1], fb[CB ^ 1], slot(2 * i + 2), slot(2 * i + 3), 0);
+      read_scales(nsa, nsb, slot(2 * i + 2), slot(2 * i + 3));
     }
-    mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM);
+    mma_rows(fa[CB], fb[CB], Cfg::FM / 2, Cfg::FM, KL);
+    if constexpr (kMx && !LAST) {
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f) msa[f] = nsa[f];
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g) msb[g] = nsb[g];
+    }
   }
 
   SKG_DEV void mainloop_grp(const Loader& ld, int k0, int k1) {
@@ -1207,6 +1343,7 @@ struct Engine {
       wait_groups(min(Cfg::NSLOT, G) - 2);
       lds_barrier();
       grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
+      read_scales(msa, msb, slot(0), slot(1));
       for (int i = 0; i + 1 < I; ++i) grp_iter_burst<false>(fa, fb, ld, i, G, k0);
       grp_iter_burst<true>(fa, fb, ld, I - 1, G, k0);
     }

@@ -26,12 +26,12 @@ struct ConvInst {
   hipError_t (*occupancy)(int*);
 };
 
-// {nullptr, nullptr} when the (tile, dtype) pair has no compiled instance.
-// tensor_scales selects the per-tensor scale instances.
-GemmInst gemm_instance(int tile_id, int dtype, bool tensor_scales);
+// {nullptr, nullptr} when the (tile, dtype, scale mode) has no compiled
+// instance; scale_mode is an enum skg_scale_mode.
+GemmInst gemm_instance(int tile_id, int dtype, int scale_mode);
 GemmInst gemm_instance_f16(int tile_id, bool tensor_scales);
 GemmInst gemm_instance_bf16(int tile_id, bool tensor_scales);
-GemmInst gemm_instance_f8(int tile_id, int dtype, bool tensor_scales);
+GemmInst gemm_instance_f8(int tile_id, int dtype, int scale_mode);
 WgradInst wgrad_instance(int tile_id, int dtype);
 ConvInst fwd_instance(int tile_id, int dtype);
 ConvInst dgrad_instance(int tile_id, int dtype);

@@ -78,7 +78,7 @@ class GemmWorkload:
     ctas: int
     scales: bool = False
     op: str = "gemm"
-    scale_mode: str = "rowcol"   # or "tensor": one scale per operand
+    scale_mode: str = "rowcol"   # "tensor": one scale per operand; "mx": E8M0 block scales
 
     @property
     def seed(self):
@@ -95,7 +95,13 @@ class GemmWorkload:
             "A": to_codes(draw(self.dist, self.M * self.K, s + 0), self.dtype_ab),
             "B": to_codes(draw(self.dist, self.N * self.K, s + 1), self.dtype_ab),
         }
-        if self.scales:
+        if self.scales and self.scale_mode == "mx":
+            # E8M0 block scales 2^-3 .. 2^3, one per 32 K elements of a row
+            # of A / a column of B.
+            nb = self.K // 32
+            out["scale_a"] = (127 + rng(s + 2).integers(-3, 4, self.M * nb)).astype(np.uint8)
+            out["scale_b"] = (127 + rng(s + 3).integers(-3, 4, self.N * nb)).astype(np.uint8)
+        elif self.scales:
             per = self.scale_mode == "rowcol"
             out["scale_a"] = draw("scale", self.M if per else 1, s + 2).astype(np.float32)
             out["scale_b"] = draw("scale", self.N if per else 1, s + 3).astype(np.float32)
@@ -218,11 +224,13 @@ WORKLOADS = {
                     scales=True),
 }
 
-# The other two convolutions of the two wgrad layers (forward and input
-# gradient), on the same engine, in the launches measured fastest: 256x256x64
-# tiles, persistent, tree fix-up for the dense layer; 128x128x64 tiles for
-# the grouped one (16 channels per group; every plan is all-DP there).
-LAYER_WORKLOADS = {
+# Workloads of the rows built after the five: the other two convolutions of
+# the two wgrad layers (forward and input gradient), on the same engine, in
+# the launches measured fastest (256x256x64 tiles, persistent, tree fix-up
+# for the dense layer; 128x128x64 tiles for the grouped one, 16 channels per
+# group, where every plan is all-DP), and the fp8 GEMM of workload 5 with OCP
+# MX (E8M0) block scales instead of row/column scales.
+NEXT_WORKLOADS = {
     6: ConvWorkload(6, "fwd_f16_n32_56x56_c256_k256_3x3", "fwd", 32, 56, 56, 256, 256, 3, 3,
                     (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
                     ("tree",), 256),
@@ -235,4 +243,10 @@ LAYER_WORKLOADS = {
     9: ConvWorkload(9, "dgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", "dgrad", 64, 28, 28, 512, 512,
                     3, 3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
                     ("tree",), 256),
+    10: GemmWorkload(10, "gemm_e4m3_8192x8192x8192_mx_e8m0", 8192, 8192, 8192, "e4m3", "bf16",
+                     "normal", "128x128x128", ("persistent",), ("workspace",), 512, scales=True,
+                     scale_mode="mx"),
 }
+
+# Earlier name of the first four of them.
+LAYER_WORKLOADS = {i: w for i, w in NEXT_WORKLOADS.items() if i in (6, 7, 8, 9)}

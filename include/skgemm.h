@@ -76,7 +76,20 @@ enum skg_dtype {
  * Either pointer may be NULL (scale 1) in both modes. */
 enum skg_scale_mode {
   SKG_SCALE_ROWCOL = 0,
-  SKG_SCALE_TENSOR = 1
+  SKG_SCALE_TENSOR = 1,
+  /* SKG_SCALE_MX_E8M0  OCP Microscaling block scales (the MX / microscaling
+   *                    variants named for the bquant bridge in the combined
+   *                    follow-up of the "gemm_rowcolquant dispatcher bridge"
+   *                    PR; the gfx950 scaled f8f6f4 MFMA of PR #13151's arch
+   *                    table): scale_a points to M x K/32 and scale_b to
+   *                    N x K/32 bytes, row-major, each an E8M0 code (value
+   *                    2^(code-127), 255 = NaN) for one block of 32
+   *                    consecutive K elements of a row of A or a column of B:
+   *                    C[m][n] = round(sum_b 2^(sa[m][b]-127) 2^(sb[n][b]-127)
+   *                    sum_{k in b} a(m,k) b(k,n)).  fp8 / bf8 inputs, the
+   *                    128x128x128 tile, K a multiple of 128, both pointers
+   *                    non-NULL and 16-byte aligned; no further scale. */
+  SKG_SCALE_MX_E8M0 = 2
 };
 
 /* Launch modes (PR #13151, Technical Details: Wgrad kernel, launch modes).
@@ -160,7 +173,8 @@ enum skg_tile {
   SKG_TILE_32x64x64 = 3,     /* f16/bf16 wgrad (small per-group M), 4 waves */
   SKG_TILE_128x128x64 = 4,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_256x128x64 = 5,   /* f16/bf16 GEMM and wgrad, 4 waves */
-  SKG_TILE_COUNT = 6
+  SKG_TILE_128x128x128 = 6,  /* fp8 GEMM (also with MX block scales), 4 waves */
+  SKG_TILE_COUNT = 7
 };
 
 enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1, SKG_OP_FWD = 2, SKG_OP_DGRAD = 3 };
@@ -193,8 +207,9 @@ typedef struct skg_gemm_args {
   int64_t ldb;
   void* C;
   int64_t ldc;
-  const float* scale_a;    /* device pointer (16-byte aligned) or NULL */
-  const float* scale_b;    /* device pointer (16-byte aligned) or NULL */
+  const float* scale_a;    /* device pointer (16-byte aligned) or NULL; with
+                              SKG_SCALE_MX_E8M0 the E8M0 byte array */
+  const float* scale_b;    /* likewise */
   int32_t tile_id;         /* enum skg_tile */
   int32_t mode;            /* enum skg_mode */
   int32_t reduction;       /* enum skg_reduction */

@@ -28,7 +28,8 @@ MODES = ["dp", "dp_sk", "persistent"]
 REDS = ["linear", "tree", "atomic", "workspace"]
 TILE_DT = [("128x128x32", "f16"), ("128x128x32", "bf16"), ("256x256x64", "bf16"),
            ("256x256x64", "f16"), ("128x128x64", "bf16"), ("256x128x64", "f16"),
-           ("256x256x128", "e4m3"), ("256x256x128", "e5m2")]
+           ("256x256x128", "e4m3"), ("256x256x128", "e5m2"), ("128x128x128", "e4m3"),
+           ("128x128x128", "e5m2")]
 FP8 = ("e4m3", "e5m2")
 
 

@@ -78,7 +78,7 @@ def same_plan(c, o):
 
 
 GEMM_TILE_DT = [("128x128x32", "f16"), ("256x256x64", "bf16"), ("256x256x128", "e4m3"),
-                ("256x256x128", "e5m2"),
+                ("256x256x128", "e5m2"), ("128x128x128", "e4m3"),
                 ("128x128x64", "bf16"), ("256x128x64", "f16")]
 
 
@@ -167,7 +167,7 @@ def test_gemm_validation_rejects():
     assert "instance" in bad(tile="256x256x128")
     assert "instance" in bad(dtype_ab="e4m3")
     assert "instance" in bad(dtype_ab="e5m2")
-    assert "scale mode" in bad(scale_mode=2)
+    assert "scale mode" in bad(scale_mode=3)
     assert "dtype" in bad(dtype_c="e4m3")
     assert "positive" in bad(M=0)
     assert "16 bytes" in bad(K=100)
