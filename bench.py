@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--ctas", type=int, default=None)
     ap.add_argument("--tile", default=None)
-    ap.add_argument("--sk-order", default="auto", choices=["auto", "block", "xcd"],
+    ap.add_argument("--sk-order", default="auto", choices=["auto", "block", "xcd", "kmajor"],
                     help="stream-K CTA order (auto: xcd for wgrad, block for GEMM)")
     ap.add_argument("--dtype", default=None, choices=["e4m3", "e5m2"],
                     help="fp8 operand format of the fp8 GEMM workload (default e4m3)")

@@ -26,8 +26,9 @@ REDUCTIONS = {"linear": RED_LINEAR, "tree": RED_TREE, "atomic": RED_ATOMIC,
               "workspace": RED_WORKSPACE, "auto": RED_AUTO}
 DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32, "e5m2": F8E5M2}
 SCALE_MODES = {"rowcol": SCALE_ROWCOL, "tensor": SCALE_TENSOR, "mx": SCALE_MX_E8M0}
-SK_ORDER_AUTO, SK_ORDER_BLOCK, SK_ORDER_XCD = 0, 1, 2
-SK_ORDERS = {"auto": SK_ORDER_AUTO, "block": SK_ORDER_BLOCK, "xcd": SK_ORDER_XCD}
+SK_ORDER_AUTO, SK_ORDER_BLOCK, SK_ORDER_XCD, SK_ORDER_KMAJOR = 0, 1, 2, 3
+SK_ORDERS = {"auto": SK_ORDER_AUTO, "block": SK_ORDER_BLOCK, "xcd": SK_ORDER_XCD,
+             "kmajor": SK_ORDER_KMAJOR}
 TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
          "256x256x128": TILE_256x256x128, "32x64x64": TILE_32x64x64,
          "128x128x64": TILE_128x128x64, "256x128x64": TILE_256x128x64,

@@ -116,7 +116,10 @@ KPlan to_kplan(const skg_plan_t& pl, int inject) {
   k.grid = (int)pl.grid;
   k.mode = pl.mode;
   k.reduction = pl.reduction;
-  k.sk_order = pl.sk_order == SKG_SK_ORDER_XCD ? SK_ORDER_XCD : SK_ORDER_BLOCK;
+  k.sk_order = pl.sk_order == SKG_SK_ORDER_XCD      ? SK_ORDER_XCD
+               : pl.sk_order == SKG_SK_ORDER_KMAJOR ? SK_ORDER_KMAJOR
+                                                    : SK_ORDER_BLOCK;
+  k.sk_slices = pl.sk_order == SKG_SK_ORDER_KMAJOR ? (int)(pl.iters_per_tile / pl.iters_per_sk_cta) : 1;
   k.spin_limit = inject == INJECT_HANDOFF ? kFaultSpin : kSpinLimit;
   k.fault = inject == INJECT_HANDOFF ? FAULT_NO_PUBLISH : FAULT_NONE;
   return k;
@@ -287,6 +290,7 @@ int run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, hipStream_t 
   w.dy_bytes = (uint32_t)((int64_t)w.kred * a->k * 2);
   w.div_howo = make_fastdiv((uint32_t)(w.Ho * w.Wo));
   w.div_wo = make_fastdiv((uint32_t)w.Wo);
+  w.div_ho = make_fastdiv((uint32_t)w.Ho);
   w.div_cpg = make_fastdiv((uint32_t)w.cpg);
   w.div_s = make_fastdiv((uint32_t)a->s);
   if (pl.reduction == SKG_RED_ATOMIC && pl.sk_ctas) {

@@ -37,6 +37,18 @@ SKG_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// make_rsrc of a base and size the caller knows to be wave-uniform, made
+// scalar explicitly (the direct-to-LDS loads take the resource in SGPRs,
+// and the compiler cannot always prove that values derived from the tile
+// index are uniform).
+SKG_DEV __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
+}
+
 SKG_DEV i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }

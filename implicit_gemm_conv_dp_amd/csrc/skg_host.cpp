@@ -145,6 +145,15 @@ int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, 
   if (rc) return rc;
   out->requested_mode = requested;
   out->slices = slices;
+  // Slice-major order needs every stream-K CTA to hold one whole slice of
+  // one tile; otherwise the XCD runs are taken over the CTAs themselves.
+  if (sk_order == SKG_SK_ORDER_KMAJOR) {
+    const skg_plan_t& p = *out;
+    const bool aligned = p.sk_ctas > 0 && p.extra_iters == 0 &&
+                         p.iters_per_tile % p.iters_per_sk_cta == 0 &&
+                         p.sk_ctas == p.sk_tiles * (p.iters_per_tile / p.iters_per_sk_cta);
+    if (!aligned) sk_order = SKG_SK_ORDER_XCD;
+  }
   out->sk_order = sk_order;
   return SKG_OK;
 }
@@ -301,7 +310,7 @@ int validate_gemm(const skg_gemm_args_t* a) {
     if (a->tile_id != SKG_TILE_128x128x128) return unsupported("MX block scales need the 128x128x128 tile");
     if (a->K % 128) return unsupported("MX block scales need K to be a multiple of 128");
   }
-  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_KMAJOR)
     return unsupported("unknown stream-K CTA order");
   if (a->dtype_c != SKG_F16 && a->dtype_c != SKG_BF16 && a->dtype_c != SKG_F32)
     return unsupported("unsupported C dtype");
@@ -327,7 +336,7 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
   const TileDesc* t = tile_desc(a->tile_id);
   if (!t) return unsupported("unknown tile id");
   if (a->dtype != SKG_F16 && a->dtype != SKG_BF16) return unsupported("unsupported wgrad dtype");
-  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_KMAJOR)
     return unsupported("unknown stream-K CTA order");
   if (!(t->wgrad_mask & (1 << a->dtype))) return unsupported("tile has no wgrad instance for this dtype");
   int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);
@@ -360,7 +369,7 @@ int validate_conv(const skg_conv_args_t* a, bool dgrad) {
   if (a->dtype != SKG_F16 && a->dtype != SKG_BF16) return unsupported("unsupported convolution dtype");
   if (a->dtype_out != SKG_F16 && a->dtype_out != SKG_BF16 && a->dtype_out != SKG_F32)
     return unsupported("unsupported output dtype");
-  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_XCD)
+  if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_KMAJOR)
     return unsupported("unknown stream-K CTA order");
   if (!(t->conv_mask & (1 << a->dtype))) return unsupported("tile has no convolution instance for this dtype");
   int rc = check_launch_knobs(a->mode, a->reduction, a->ctas, true);

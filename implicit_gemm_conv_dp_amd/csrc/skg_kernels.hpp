@@ -27,7 +27,7 @@ namespace skg {
 
 // ---------------------------------------------------------------------------
 // Plan as the kernels see it (32-bit; the host checks the ranges).
-enum { SK_ORDER_BLOCK = 0, SK_ORDER_XCD = 1 };
+enum { SK_ORDER_BLOCK = 0, SK_ORDER_XCD = 1, SK_ORDER_KMAJOR = 2 };
 
 // Forced faults (set only from the host's fault-injection switch): with
 // FAULT_NO_PUBLISH the stream-K CTAs store their partials but never raise
@@ -38,7 +38,8 @@ struct KPlan {
   int tiles_m, tiles_n, ipt;
   int dp_tiles, sk_tiles, sk_ctas, ipc, extra;
   int grid, mode, reduction;
-  int sk_order;         // SK_ORDER_BLOCK or SK_ORDER_XCD
+  int sk_order;         // SK_ORDER_*
+  int sk_slices;        // SK_ORDER_KMAJOR: slices per tile (sk_ctas = sk_tiles * sk_slices)
   uint32_t spin_limit;  // polls before a flag wait gives up
   int fault;            // FAULT_*
 };
@@ -81,7 +82,7 @@ struct WgradParams {
   int N, H, W, C, K, R, S, sh, sw, ph, pw;
   int Ho, Wo, cpg, kpg, mt_per_group, gemm_n, kred;
   uint32_t x_bytes, dy_bytes;
-  FastDiv div_howo, div_wo, div_cpg, div_s;
+  FastDiv div_howo, div_wo, div_ho, div_cpg, div_s;
 };
 
 // ---------------------------------------------------------------------------
@@ -233,8 +234,10 @@ struct DmaRows {
 
   SKG_DEV void init(const GemmParams& g, int m0, int n0, int tid) {
     const int rows_a = g.M - m0, rows_b = g.N - n0;
-    ra = make_rsrc(g.A + (size_t)m0 * g.lda_b, (uint32_t)min((int64_t)rows_a * g.lda_b, (int64_t)0x7fffffff));
-    rb = make_rsrc(g.B + (size_t)n0 * g.ldb_b, (uint32_t)min((int64_t)rows_b * g.ldb_b, (int64_t)0x7fffffff));
+    ra = make_rsrc_uniform(g.A + (size_t)m0 * g.lda_b,
+                           (uint32_t)min((int64_t)rows_a * g.lda_b, (int64_t)0x7fffffff));
+    rb = make_rsrc_uniform(g.B + (size_t)n0 * g.ldb_b,
+                           (uint32_t)min((int64_t)rows_b * g.ldb_b, (int64_t)0x7fffffff));
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int row, chunk;
     lds_slot<RBX>(tid, row, chunk);
@@ -595,15 +598,24 @@ struct WgradGrpLoader {
                 "wgrad DMA mapping");
 
   __amdgpu_buffer_rsrc_t rx, rdy;
-  uint32_t a_chan;  // byte offset of this thread's A chunk within a dY row
-  uint32_t b_chan;  // byte offset of its B chunk within an X pixel
-  int rowa, rowb;   // first tile row of its chunks
-  int tap_r, tap_s;
-  bool a_ok, b_ok;  // the chunk's channels exist
   int wave;
+  // Row d (< TK) of an iteration is reduction index q0 + d.  The CTA-uniform
+  // q0 is split into (image, ho, wo) once per iteration on the scalar unit;
+  // each lane holds the same split of its own rows d_u = row + u * STEP
+  // (radix Wo, then Ho) and adds the two digit by digit, with at most one
+  // carry per digit, so the hot loop needs no division and no 32-bit
+  // multiply.  Byte offsets follow in uint32 arithmetic: X offset of
+  // (img, ho, wo) shifted by the thread's tap = img*HWc2 + ho*sh*Wc2 +
+  // wo*sw*c2 + ((r - ph)*W + (s - pw))*c2 + channel bytes, where the last
+  // two terms and the lane's own digits are folded into boff[u].
+  uint32_t aoff_l;     // rowa * K*2 + A channel bytes
+  int qrow_a, qrow_b;  // the lane's first row, or past any reduction when its chunk is empty
+  uint32_t boff[Cfg::TK / STEPB];
+  uint32_t bwo[Cfg::TK / STEPB], bho[Cfg::TK / STEPB];  // digits of the lane's rows
+  int tr_ph, ts_pw;  // r - ph, s - pw of the lane's tap
   // problem constants (uniform)
-  uint32_t k2, c2;
-  int kred, H, W, Ho, Wo, sh, sw, ph, pw;
+  uint32_t k2, hwc2, shwc2, swc2, cw1, cw2, howo;
+  int kred, H, W, Ho, Wo, sh, sw;
   FastDiv div_howo, div_wo;
 
   SKG_DEV void init(const WgradParams& w, int group, int mrow0, int n0, int tid) {
@@ -611,7 +623,7 @@ struct WgradGrpLoader {
     rdy = make_rsrc(w.dY, w.dy_bytes);
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     k2 = (uint32_t)w.K * 2;
-    c2 = (uint32_t)w.C * 2;
+    const uint32_t c2 = (uint32_t)w.C * 2;
     kred = w.kred;
     H = w.H;
     W = w.W;
@@ -619,59 +631,94 @@ struct WgradGrpLoader {
     Wo = w.Wo;
     sh = w.sh;
     sw = w.sw;
-    ph = w.ph;
-    pw = w.pw;
+    howo = (uint32_t)(w.Ho * w.Wo);
+    hwc2 = (uint32_t)(w.H * w.W) * c2;
+    shwc2 = (uint32_t)(w.sh * w.W) * c2;
+    swc2 = (uint32_t)w.sw * c2;
+    cw1 = shwc2 - (uint32_t)w.Wo * swc2;  // wo wrapped: wo - Wo, ho + 1
+    cw2 = hwc2 - (uint32_t)w.Ho * shwc2;  // ho wrapped: ho - Ho, img + 1
     div_howo = w.div_howo;
     div_wo = w.div_wo;
-    rowa = tid / CPRA;
+    constexpr int kPast = 1 << 30;
+    const int rowa = tid / CPRA;
     const int lca = (tid % CPRA) ^ tr_swz<PA, Cfg::MN>(rowa);
     const int m = mrow0 + lca * 8;
-    a_ok = m < w.kpg;
-    a_chan = (uint32_t)(group * w.kpg + m) * 2;
-    rowb = tid / CPRB;
+    qrow_a = m < w.kpg ? rowa : kPast;
+    aoff_l = (uint32_t)rowa * k2 + (uint32_t)(group * w.kpg + m) * 2;
+    const int rowb = tid / CPRB;
     const int lcb = (tid % CPRB) ^ tr_swz<PB, Cfg::MN>(rowb);
     const int nidx = n0 + lcb * 8;
-    b_ok = nidx < w.gemm_n;
+    qrow_b = nidx < w.gemm_n ? rowb : kPast;
     const uint32_t rs = fdiv((uint32_t)nidx, w.div_cpg);
     const int cc = nidx - (int)rs * w.cpg;
     const uint32_t r = fdiv(rs, w.div_s);
-    tap_r = (int)r;
-    tap_s = (int)(rs - r * w.S);
-    b_chan = (uint32_t)(group * w.cpg + cc) * 2;
+    tr_ph = (int)r - w.ph;
+    ts_pw = (int)(rs - r * w.S) - w.pw;
+    const uint32_t tap = (uint32_t)tr_ph * ((uint32_t)w.W * c2) + (uint32_t)ts_pw * c2 +
+                         (uint32_t)(group * w.cpg + cc) * 2;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const uint32_t d = (uint32_t)(rowb + u * STEPB);
+      const uint32_t t = fdiv(d, div_wo);
+      const uint32_t img = fdiv(t, w.div_ho);
+      bwo[u] = d - t * (uint32_t)Wo;
+      bho[u] = t - img * (uint32_t)Ho;
+      boff[u] = img * hwc2 + bho[u] * shwc2 + bwo[u] * swc2 + tap;
+    }
   }
 
-  // dY row q of this thread's A chunk, or kOOB.
-  SKG_DEV uint32_t a_off(int q, bool live) const {
-    const bool ok = live & a_ok & (q < kred);
-    return ok ? (uint32_t)q * k2 + a_chan : kOOB;
+  // The scalar part of iteration it's rows.
+  struct QBase {
+    uint32_t wo0, ho0, boff, aoff;
+    int lim;  // rows d < lim are inside the reduction (0 when not live)
+  };
+  SKG_DEV QBase qbase(int it, bool live) const {
+    const uint32_t q0 = __builtin_amdgcn_readfirstlane((uint32_t)it * Cfg::TK);
+    const uint32_t img = fdiv(q0, div_howo);
+    const uint32_t rem = q0 - img * howo;
+    const uint32_t ho = fdiv(rem, div_wo);
+    QBase b;
+    b.wo0 = rem - ho * (uint32_t)Wo;
+    b.ho0 = ho;
+    b.boff = img * hwc2 + ho * shwc2 + b.wo0 * swc2;
+    b.aoff = q0 * k2;
+    b.lim = live ? kred - (int)q0 : 0;
+    return b;
   }
-  // X pixel of q shifted by this thread's filter tap, or kOOB (padding).
-  SKG_DEV uint32_t b_off(int q, bool live) const {
-    const uint32_t img = fdiv((uint32_t)q, div_howo);
-    const int rem = q - (int)img * Ho * Wo;
-    const uint32_t ho = fdiv((uint32_t)rem, div_wo);
-    const int wo = rem - (int)ho * Wo;
-    const int hi = (int)ho * sh - ph + tap_r;
-    const int wi = wo * sw - pw + tap_s;
-    // Evaluated without branches (the offset is computed either way and
-    // selected), so the compiler emits no exec-mask jumps around it.
-    const bool ok = live & b_ok & (q < kred) & (hi >= 0) & (hi < H) & (wi >= 0) & (wi < W);
-    uint32_t off = (uint32_t)(((int)img * H + hi) * W + wi) * c2 + b_chan;
-    asm volatile("" : "+v"(off));
+
+  // dY row of this thread's A chunk u, or kOOB.
+  SKG_DEV uint32_t a_off(const QBase& b, int u) const {
+    const uint32_t off = aoff_l + (b.aoff + (uint32_t)(u * STEPA) * k2);
+    return qrow_a < b.lim - u * STEPA ? off : kOOB;
+  }
+  // X pixel of this thread's B row u shifted by its filter tap, or kOOB
+  // (zero padding, past the reduction, past the group's channels).
+  SKG_DEV uint32_t b_off(const QBase& b, int u) const {
+    uint32_t wo = b.wo0 + bwo[u];
+    const bool c1 = wo >= (uint32_t)Wo;
+    wo = c1 ? wo - (uint32_t)Wo : wo;
+    uint32_t ho = b.ho0 + bho[u] + (c1 ? 1u : 0u);
+    const bool c2 = ho >= (uint32_t)Ho;
+    ho = c2 ? ho - (uint32_t)Ho : ho;
+    const uint32_t off = b.boff + boff[u] + (c1 ? cw1 : 0u) + (c2 ? cw2 : 0u);
+    const int hi = __mul24((int)ho, sh) + tr_ph;
+    const int wi = __mul24((int)wo, sw) + ts_pw;
+    const bool ok = ((uint32_t)hi < (uint32_t)H) & ((uint32_t)wi < (uint32_t)W) &
+                    (qrow_b < b.lim - u * STEPB);
     return ok ? off : kOOB;
   }
 
   template <bool IS_A>
   SKG_DEV void issue_group(int it, SKG_LDS char* slot, bool live) const {
-    const int q0 = it * Cfg::TK;
+    const QBase b = qbase(it, live);
     if constexpr (IS_A) {
 #pragma unroll
       for (int u = 0; u < UA; ++u)
-        dma16(rdy, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), a_off(q0 + rowa + u * STEPA, live));
+        dma16(rdy, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), a_off(b, u));
     } else {
 #pragma unroll
       for (int u = 0; u < UB; ++u)
-        dma16(rx, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), b_off(q0 + rowb + u * STEPB, live));
+        dma16(rx, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), b_off(b, u));
     }
   }
 
@@ -685,42 +732,26 @@ struct WgradGrpLoader {
   }
   SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
 
-  // Offsets of one group's DMA instructions, computed ahead of the
-  // instructions themselves (among the MFMAs of the iteration before).
-  struct PreA { uint32_t off[UA]; };
-  struct PreB { uint32_t off[UB]; };
-  SKG_DEV void prep_a(int it, bool live, PreA& pr) const {
-#pragma unroll
-    for (int u = 0; u < UA; ++u) pr.off[u] = a_off(it * Cfg::TK + rowa + u * STEPA, live);
-  }
-  SKG_DEV void prep_b(int it, bool live, PreB& pr) const {
-#pragma unroll
-    for (int u = 0; u < UB; ++u) pr.off[u] = b_off(it * Cfg::TK + rowb + u * STEPB, live);
-  }
-  SKG_DEV void issue_a(SKG_LDS char* slot, const PreA& pr) const {
-#pragma unroll
-    for (int u = 0; u < UA; ++u) dma16(rdy, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), pr.off[u]);
-  }
-  SKG_DEV void issue_b(SKG_LDS char* slot, const PreB& pr) const {
-#pragma unroll
-    for (int u = 0; u < UB; ++u) dma16(rx, lds_addr(slot + u * Cfg::THREADS * 16 + wave * 1024), pr.off[u]);
-  }
-
+  // A refill spread among the MFMAs: the B group of iteration it_b into
+  // slot_b (DMA instructions [0, UB)), then the A group of it_a.
   struct Refill {
     SKG_LDS char* slot_b;
     SKG_LDS char* slot_a;
     int it_b, it_a;
     bool live_b, live_a;
+    QBase qb, qa;
   };
+  SKG_DEV void finish_refill(Refill& r) const {
+    r.qb = qbase(r.it_b, r.live_b);
+    r.qa = qbase(r.it_a, r.live_a);
+  }
   template <int N>
   SKG_DEV void refill(const Refill& r) const {
     if constexpr (N < UB) {
-      dma16(rx, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + wave * 1024),
-            b_off(r.it_b * Cfg::TK + rowb + N * STEPB, r.live_b));
+      dma16(rx, lds_addr(r.slot_b + N * Cfg::THREADS * 16 + wave * 1024), b_off(r.qb, N));
     } else {
       constexpr int U = N - UB;
-      dma16(rdy, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + wave * 1024),
-            a_off(r.it_a * Cfg::TK + rowa + U * STEPA, r.live_a));
+      dma16(rdy, lds_addr(r.slot_a + U * Cfg::THREADS * 16 + wave * 1024), a_off(r.qa, U));
     }
   }
 };
@@ -785,13 +816,6 @@ struct Engine {
   typedef typename Cfg::Op::frag_t Frag;
   typedef Frag FragA[Cfg::FM];
   typedef Frag FragB[Cfg::FN];
-  // Precomputed refill offsets (wgrad loaders); empty elsewhere.
-  template <class L, class = void>
-  struct PreOf { struct A {}; struct B {}; };
-  template <class L>
-  struct PreOf<L, std::void_t<typename L::PreA>> { typedef typename L::PreA A; typedef typename L::PreB B; };
-  typedef typename PreOf<Loader>::A PreAT;
-  typedef typename PreOf<Loader>::B PreBT;
 
   const Params& prm;
   const KPlan& p;
@@ -803,6 +827,9 @@ struct Engine {
   // already shifted so that byte 0 is the lane's block of k-step 0 and
   // byte 2 that of k-step 1.
   static constexpr bool kMx = LoaderMx<Loader>::value;
+  // One CTA per CU: the burst schedule spreads its refills among the MFMAs
+  // (grp_iter_burst).  Not with MX scales (mma_dma issues plain MFMAs).
+  static constexpr bool kDefer = Cfg::MIN_CTAS == 1 && !kMx;
   uint32_t msa[Cfg::FM], msb[Cfg::FN], nsa[Cfg::FM], nsb[Cfg::FN];
 
   SKG_DEV Engine(const Params& prm_, const KPlan& p_, const Scratch& s_, SKG_LDS char* lds_)
@@ -1060,13 +1087,26 @@ struct Engine {
     }
   }
 
+  // Per-lane LDS addresses of the transposing fragment reads of one slot.
+  struct TrBase {
+    uint32_t a[Cfg::FM], b[Cfg::FN];
+  };
+
   // Fragments of k-step ks of the grouped pipeline from the A tile at sa
   // and the B tile at sb: K-contiguous rows (GEMM) read directly, q-row
   // tiles (wgrad) with the transposing read.
   SKG_DEV void grp_frags(FragA& fa, FragB& fb, const SKG_LDS char* sa, const SKG_LDS char* sb,
                          int ks) const {
     if constexpr (Loader::kTrans)
-      load_frags_tr(fa, fb, sa, sb, ks);
+      load_frags_tr(fa, fb, tr_bases(sa, sb), ks);
+    else
+      load_frags_ab<Cfg::RB>(fa, fb, sa, sb, ks);
+  }
+  // Same, with the transposing reads' bases of the slots formed already.
+  SKG_DEV void grp_frags(FragA& fa, FragB& fb, const SKG_LDS char* sa, const SKG_LDS char* sb,
+                         const TrBase& t, int ks) const {
+    if constexpr (Loader::kTrans)
+      load_frags_tr(fa, fb, t, ks);
     else
       load_frags_ab<Cfg::RB>(fa, fb, sa, sb, ks);
   }
@@ -1103,25 +1143,50 @@ struct Engine {
     }
   }
 
+  // The k-step and the second read are constant offsets from one per-lane
+  // address per fragment and slot (TrBase, formed once per slot and
+  // iteration).  That address is made opaque to the compiler, which
+  // otherwise hoists every (lane offset + constant) of the loop into a
+  // register of its own and re-adds the slot base to each of them on every
+  // iteration (two VALU instructions per read) instead of using the read's
+  // immediate offset.
+  SKG_DEV TrBase tr_bases(const SKG_LDS char* sa, const SKG_LDS char* sb) const {
+    TrBase t;
+    if constexpr (Loader::kTrans) {
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f) {
+        uint32_t x = lds_addr(sa) + tro_a[f];
+        asm volatile("" : "+v"(x));
+        t.a[f] = x;
+      }
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g) {
+        uint32_t x = lds_addr(sb) + tro_b[g];
+        asm volatile("" : "+v"(x));
+        t.b[g] = x;
+      }
+    }
+    return t;
+  }
+
   template <int P>
-  SKG_DEV static Frag tr_frag(const SKG_LDS char* base, uint32_t off, int ks) {
+  SKG_DEV static Frag tr_frag(uint32_t addr, int ks) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef SKG_LDS v4i16 lds_v4i16;
     constexpr int KE = Cfg::Op::KB / 2;  // reduction indices per k-step
-    const SKG_LDS char* p = base + off + ks * KE * P;
+    const SKG_LDS char* p = (const SKG_LDS char*)(uintptr_t)addr + ks * KE * P;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * P));
     const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
     return Frag{l2[0], l2[1], h2[0], h2[1]};
   }
 
-  SKG_DEV void load_frags_tr(FragA& fa, FragB& fb, const SKG_LDS char* sa, const SKG_LDS char* sb,
-                             int ks) const {
+  SKG_DEV void load_frags_tr(FragA& fa, FragB& fb, const TrBase& t, int ks) const {
     if constexpr (Loader::kTrans) {
 #pragma unroll
-      for (int f = 0; f < Cfg::FM; ++f) fa[f] = tr_frag<Loader::PA>(sa, tro_a[f], ks);
+      for (int f = 0; f < Cfg::FM; ++f) fa[f] = tr_frag<Loader::PA>(t.a[f], ks);
 #pragma unroll
-      for (int g = 0; g < Cfg::FN; ++g) fb[g] = tr_frag<Loader::PB>(sb, tro_b[g], ks);
+      for (int g = 0; g < Cfg::FN; ++g) fb[g] = tr_frag<Loader::PB>(t.b[g], ks);
     }
   }
 
@@ -1244,43 +1309,51 @@ struct Engine {
     });
   }
 
-  // Burst variant: at the end of iteration i the two slots it used are
-  // refilled right after the barrier with groups 2i+NSLOT and 2i+NSLOT+1.
-  template <bool LAST>
-  SKG_DEV void grp_iter_burst(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G,
-                              int k0) {
+  // Burst variant (tiles without the rolling schedule).  With two CTAs per
+  // CU, at the end of iteration i the two slots it used are refilled right
+  // after the barrier with groups 2i+NSLOT and 2i+NSLOT+1, and the other
+  // CTA's MFMAs cover the burst.  With one CTA per CU (kDefer) nothing
+  // would: a wave that issues a dozen DMAs in a row stalls until the
+  // address unit takes them, with no MFMA queued.  There the refill of
+  // iteration i-1's slots is issued during iteration i instead, spread
+  // among the MFMAs of its first KSTEPS-1 k-steps (DMA: i >= 1, not the
+  // last iteration, whose pending groups all lie past the segment).  The
+  // awaited groups are the same either way.  Pending groups past the
+  // segment zero-fill slots nobody reads; the main loop waits for them
+  // before the LDS is reused.
+  template <bool LAST, bool DMA>
+  SKG_DEV void grp_iter_burst(FragA (&fa)[2], FragB (&fb)[2], const Loader& ld, int i, int G) {
+    constexpr int ODD = Cfg::NSLOT % 2;  // group 2i+NSLOT is a B group when NSLOT is odd
     const SKG_LDS char* sa = slot(2 * i);
     const SKG_LDS char* sb = slot(2 * i + 1);
-    // wgrad: the im2col offsets of this iteration's refill (groups 2i+NSLOT
-    // and 2i+NSLOT+1, one A and one B group) are computed among the MFMAs of
-    // the first k-steps; after the barrier only the DMAs are left to issue.
-    // (Not with 256 accumulators per lane: the offsets would not fit beside them.)
-    constexpr bool PRE = Loader::kTrans && !LAST && Cfg::KSTEPS >= 2 && Cfg::FM * Cfg::FN * Cfg::NACC <= 128;
-    constexpr int ODD = Cfg::NSLOT % 2;  // group 2i+NSLOT is a B group when NSLOT is odd
-    const int jb = 2 * i + Cfg::NSLOT + (1 - ODD), ja = 2 * i + Cfg::NSLOT + ODD;
-    PreBT pb;
-    PreAT pa;
-#pragma unroll
-    for (int ks = 0; ks + 1 < Cfg::KSTEPS; ++ks) {
-      grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, ks + 1);
-      if constexpr (PRE) {
-        // B in k-step 0, A in k-step 1 (or also 0 when that is the only
-        // k-step before the last): both are ready before the barrier.
-        if (ks == 0) ld.prep_b(iter(jb >> 1), jb < G, pb);
-        if (ks == (Cfg::KSTEPS > 2 ? 1 : 0)) ld.prep_a(iter(ja >> 1), ja < G, pa);
-      }
-      mma(fa[ks & 1], fb[ks & 1], ks);
-      __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
+    typename Loader::Refill rf;
+    if constexpr (kDefer && DMA) {
+      const int jb = 2 * (i - 1) + Cfg::NSLOT + (1 - ODD), ja = 2 * (i - 1) + Cfg::NSLOT + ODD;
+      rf.slot_b = slot(jb);
+      rf.slot_a = slot(ja);
+      rf.it_b = iter(jb >> 1);
+      rf.it_a = iter(ja >> 1);
+      rf.live_b = jb < G;
+      rf.live_a = ja < G;
+      ld.finish_refill(rf);
     }
+    const TrBase tb = tr_bases(sa, sb);
+    static_for<0, Cfg::KSTEPS - 1>([&](auto ks_) {
+      constexpr int ks = decltype(ks_)::value, ND = Loader::UA + Loader::UB, KS = Cfg::KSTEPS - 1;
+      grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, tb, ks + 1);
+      if constexpr (kDefer && DMA)
+        mma_dma<0, Cfg::FM, ks * ND / KS, (ks + 1) * ND / KS>(fa[ks & 1], fb[ks & 1], ld, rf);
+      else
+        mma(fa[ks & 1], fb[ks & 1], ks);
+      __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
+    });
     constexpr int CB = (Cfg::KSTEPS - 1) & 1, KL = Cfg::KSTEPS - 1;
     mma_rows(fa[CB], fb[CB], 0, Cfg::FM / 2, KL);
     if constexpr (!LAST) {
       wait_groups(min(G, 2 * i + Cfg::NSLOT) - (2 * i + 4));
       lds_barrier();
-      if constexpr (PRE) {
-        if (jb < G) ld.issue_b(slot(jb), pb);
-        if (ja < G) ld.issue_a(slot(ja), pa);
-      } else {
+      if constexpr (!kDefer) {
+        const int jb = 2 * i + Cfg::NSLOT + (1 - ODD), ja = 2 * i + Cfg::NSLOT + ODD;
         if (jb < G) ld.issue(jb, iter(jb >> 1), slot(jb));
         if (ja < G) ld.issue(ja, iter(ja >> 1), slot(ja));
       }
@@ -1344,8 +1417,19 @@ struct Engine {
       lds_barrier();
       grp_frags(fa[0], fb[0], slot(0), slot(1), 0);
       read_scales(msa, msb, slot(0), slot(1));
-      for (int i = 0; i + 1 < I; ++i) grp_iter_burst<false>(fa, fb, ld, i, G, k0);
-      grp_iter_burst<true>(fa, fb, ld, I - 1, G, k0);
+      if constexpr (kDefer) {
+        if (I == 1) {
+          grp_iter_burst<true, false>(fa, fb, ld, 0, G);
+        } else {
+          grp_iter_burst<false, false>(fa, fb, ld, 0, G);
+          for (int i = 1; i + 1 < I; ++i) grp_iter_burst<false, true>(fa, fb, ld, i, G);
+          grp_iter_burst<true, false>(fa, fb, ld, I - 1, G);
+        }
+        wait_vm<0>();  // zero-fill loads of groups past the segment
+      } else {
+        for (int i = 0; i + 1 < I; ++i) grp_iter_burst<false, false>(fa, fb, ld, i, G);
+        grp_iter_burst<true, false>(fa, fb, ld, I - 1, G);
+      }
     }
     __syncthreads();  // every wave is done with the ring before LDS is reused
   }
@@ -1431,7 +1515,10 @@ struct Engine {
   // batched loads or allocates the accumulators; each variant tried slowed
   // the hand-off kernels by 15-20 %.
   SKG_DEV void fold_regs(const Fix& fx) {
-    constexpr int FB = PSLOTS < 32 ? PSLOTS : 32;
+    // float4 loads in flight per batch: 128 VGPRs with one wave per SIMD,
+    // 32 with two (half the register file each).
+    constexpr int FBMAX = Cfg::NW > 4 ? 8 : 32;
+    constexpr int FB = PSLOTS < FBMAX ? PSLOTS : FBMAX;
     static_assert(PSLOTS % FB == 0, "fold batches");
     // One round trip reads the flags of the first MAXQ partners (usually
     // all set by now); a partner seen unset is waited for in turn below.
@@ -1777,10 +1864,16 @@ struct Engine {
     // robin (block blk to XCD blk % 8), so give XCD x the contiguous run of
     // CTAs [x*q + min(x, r), ...) of its q or q + 1 blocks: CTAs that share
     // a tile, and neighbouring tiles, then share one L2.
+    // K-major order: the same runs over (slice, tile) pairs taken slice by
+    // slice, so one XCD runs the same k range of several tiles at once.
     int b = blk;
-    if (sk_block && p.sk_order == SK_ORDER_XCD) {
+    if (sk_block && p.sk_order != SK_ORDER_BLOCK) {
       const int q = p.sk_ctas >> 3, r = p.sk_ctas & 7, x = blk & 7;
       b = x * q + min(x, r) + (blk >> 3);
+      if (p.sk_order == SK_ORDER_KMAJOR) {
+        const int s = b / p.sk_tiles;
+        b = (b - s * p.sk_tiles) * p.sk_slices + s;
+      }
     }
     int it = 0, end = 0;
     if (sk_block) {

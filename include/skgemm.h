@@ -153,7 +153,21 @@ enum skg_reduction {
  *                       runs: block b runs CTA x*q + min(x, r) + b/8 with
  *                       x = b mod 8, q = sk_ctas / 8, r = sk_ctas mod 8, so
  *                       that CTAs sharing a tile, and neighbouring tiles,
- *                       share one L2.
+ *                       share one L2;
+ *   SKG_SK_ORDER_KMAJOR for a partition that gives every stream-K CTA one
+ *                       whole slice of one tile (sk_ctas = sk_tiles * S
+ *                       with S = iters_per_tile / iters_per_sk_cta and no
+ *                       extra iterations, as split-K gives): the XCD runs
+ *                       above are taken over the (slice, tile) pairs in
+ *                       slice-major order, so block b runs CTA t*S + s for
+ *                       the pair number c = x*q + min(x, r) + b/8, slice
+ *                       s = c / sk_tiles, tile t = c mod sk_tiles.  The CTAs
+ *                       running one k range of different tiles then share
+ *                       an L2 and read the same rows of the operand that
+ *                       does not depend on the tile's columns (dY for wgrad,
+ *                       A for GEMM) at about the same time.  Any other
+ *                       partition runs in XCD order; the plan reports the
+ *                       order that runs.
  * The chiplet swizzle the pages reject with stream-K (PR #13151,
  * Constraints) remaps tiles; this remaps only whole stream-K ranges.
  * Waits still target higher CTA ids and all stream-K CTAs are co-resident,
@@ -161,7 +175,8 @@ enum skg_reduction {
 enum skg_sk_order {
   SKG_SK_ORDER_AUTO = 0,
   SKG_SK_ORDER_BLOCK = 1,
-  SKG_SK_ORDER_XCD = 2
+  SKG_SK_ORDER_XCD = 2,
+  SKG_SK_ORDER_KMAJOR = 3
 };
 
 /* Compiled tile instances.  TM x TN x TK in elements; each instance exists
@@ -293,7 +308,7 @@ typedef struct skg_plan {
   int64_t workspace_bytes;   /* bytes the caller must pass as ws */
   int32_t requested_mode;    /* the mode asked for; `mode` is what runs */
   int32_t slices;            /* split-K slices per tile (1 unless split-K) */
-  int32_t sk_order;          /* SKG_SK_ORDER_BLOCK or SKG_SK_ORDER_XCD */
+  int32_t sk_order;          /* the order that runs: BLOCK, XCD or KMAJOR */
   int64_t aux_bytes;         /* workspace after the fix-up region that the op
                                 itself uses (dgrad: the transposed filter);
                                 included in workspace_bytes */

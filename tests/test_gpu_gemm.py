@@ -330,3 +330,28 @@ def test_xcd_sk_order_integer_exact(tile, fmt):
                 Y = decode_out(dC, "f32").reshape(M, N)
                 assert np.array_equal(Y, R), "%s %s %s %s ctas=%d xcd order" % (tile, fmt, mode,
                                                                                 red, ctas)
+
+
+@pytest.mark.parametrize("tile,fmt", [("128x128x32", "f16"), ("256x256x64", "bf16")])
+def test_kmajor_sk_order_integer_exact(tile, fmt):
+    # Whole K slices per stream-K CTA, dealt slice by slice: bit-exact in
+    # every mode and fix-up.
+    M, N, K = shape_for(tile, True)
+    A = synth.integer_codes(fmt, M * K, 95, 0.15)
+    B = synth.integer_codes(fmt, N * K, 96, 0.15)
+    R = oracle_gemm(fmt, A, B, M, N, K)
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    p0 = skg.plan_gemm(M=M, N=N, K=K, dtype_ab=fmt, dtype_c="f32", tile=tile, mode="dp_sk",
+                       reduction="tree", ctas=8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    for S in [d for d in (2, 3, 5, ipt) if ipt % d == 0]:
+        for mode in ("dp_sk", "persistent"):
+            for red in REDS:
+                dC = out_buffer("f32", M * N)
+                plan = skg.gemm(dA, dB, dC, None, None, M=M, N=N, K=K, dtype_ab=fmt,
+                                dtype_c="f32", tile=tile, mode=mode, reduction=red, ctas=T * S,
+                                sk_order="kmajor")
+                torch.cuda.synchronize()
+                assert plan["sk_order"] == skg.SK_ORDERS["kmajor"], (T, S)
+                Y = decode_out(dC, "f32").reshape(M, N)
+                assert np.array_equal(Y, R), "%s %s %s %s S=%d kmajor" % (tile, fmt, mode, red, S)

@@ -132,6 +132,32 @@ def test_workload_auto_and_split_k_full_size(mode):
     assert_close(Y, R, wl.dtype, "%s %s" % (wl.name, mode))
 
 
+def divisors(n):
+    return [d for d in range(2, n + 1) if n % d == 0]
+
+
+LONG = (4, 16, 16, 32, 48, 3, 3, (1, 1), (1, 1), 1)  # 16 MAC iterations per tile
+
+
+@pytest.mark.parametrize("tile", ["32x64x64", "256x128x64"])
+@pytest.mark.parametrize("name", ["grouped", "long"])
+def test_kmajor_sk_order_integer_exact(name, tile):
+    # Whole slices dealt slice by slice (pools of tiles x S with S dividing
+    # the iterations per tile): bit-exact in every mode and fix-up.
+    shape = LONG if name == "long" else SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 96)
+    _, p0 = run(x, dy, shape, "bf16", tile, "dp_sk", "workspace", 8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    ds = divisors(ipt)
+    for S in sorted({ds[0], ds[len(ds) // 2], ipt}):
+        for mode in ("dp_sk", "persistent"):
+            for red in REDS:
+                Y, plan = run(x, dy, shape, "bf16", tile, mode, red, T * S, sk_order="kmajor")
+                assert plan["sk_order"] == skg.SK_ORDERS["kmajor"], (T, S, plan)
+                assert np.array_equal(Y, R), "%s %s %s %s S=%d kmajor order" % (name, tile, mode,
+                                                                               red, S)
+
+
 @pytest.mark.parametrize("tile", ["32x64x64", "256x128x64"])
 @pytest.mark.parametrize("name", ["grouped", "wide"])
 def test_block_sk_order_integer_exact(name, tile):

@@ -25,7 +25,7 @@ from oracle import partition as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "skgemm.h")
-TILES = {name: tuple(map(int, name.split("x"))) for name in skg.TILES}
+TILES = {name: tuple(map(int, name.split("w")[0].split("x"))) for name in skg.TILES}
 
 
 def header_functions():
@@ -313,8 +313,52 @@ def test_sk_order_resolution_and_rejection():
     # the order changes no field of the partition
     a, b = skg.plan_gemm(**g), skg.plan_gemm(sk_order="xcd", **g)
     assert all(a[f] == b[f] for f in FIELDS)
-    assert "order" in rejected(skg.plan_gemm, sk_order=3, **g)
+    assert "order" in rejected(skg.plan_gemm, sk_order=4, **g)
     assert "order" in rejected(skg.plan_wgrad, sk_order=-1, **w)
+
+
+def test_kmajor_order_needs_whole_slices():
+    # K-major runs only where every stream-K CTA holds one whole slice of one
+    # tile (split-K, or a pool that divides the iterations so); any other
+    # partition reports the XCD order it falls back to.
+    g = dict(M=512, N=512, K=8192, dtype_ab="bf16", dtype_c="bf16", tile="256x256x64")
+    p = skg.plan_gemm(mode="splitk", reduction="workspace", ctas=16, sk_order="kmajor", **g)  # 16 slices
+    S = p["iters_per_tile"] // p["iters_per_sk_cta"]
+    assert p["extra_iters"] == 0 and p["sk_ctas"] == p["sk_tiles"] * S and S > 1
+    assert p["sk_order"] == _lib.SK_ORDER_KMAJOR
+    q = skg.plan_gemm(mode="dp_sk", reduction="tree", ctas=7, sk_order="kmajor", **g)
+    assert q["extra_iters"] != 0 and q["sk_order"] == _lib.SK_ORDER_XCD
+    w = dict(n=4, h=14, w=14, c=64, k=64, r=3, s=3, stride=(1, 1), pad=(1, 1), groups=1,
+             dtype="f16", tile="128x128x64", mode="dp_sk", reduction="linear")
+    pw = skg.plan_wgrad(ctas=2 * 5, sk_order="kmajor", **w)  # 5 tiles x 2 slices of 6.5 iterations
+    assert pw["sk_order"] == _lib.SK_ORDER_XCD
+    pw = skg.plan_wgrad(ctas=5 * 13, sk_order="kmajor", **w)  # 5 tiles x 13 slices of 1 iteration
+    assert pw["iters_per_tile"] == 13 and pw["sk_order"] == _lib.SK_ORDER_KMAJOR
+
+
+def kmajor_map(sk_ctas, sk_tiles):
+    """The block -> stream-K CTA map documented for SKG_SK_ORDER_KMAJOR."""
+    S = sk_ctas // sk_tiles
+    q, r = sk_ctas // 8, sk_ctas % 8
+    out = []
+    for b in range(sk_ctas):
+        c = (b % 8) * q + min(b % 8, r) + b // 8
+        s, t = c // sk_tiles, c % sk_tiles
+        out.append(t * S + s)
+    return out
+
+
+def test_kmajor_order_is_a_permutation_grouping_slices_by_xcd():
+    # Every CTA runs once, and the CTAs an XCD runs are whole slices (the same
+    # k range) of consecutive tiles: at most ceil(run / tiles) + 1 distinct
+    # slices per XCD.
+    for T, S in [(1, 7), (9, 28), (18, 14), (5, 13), (3, 100), (16, 16), (7, 1)]:
+        m = kmajor_map(T * S, T)
+        assert sorted(m) == list(range(T * S)), (T, S)
+        for x in range(8):
+            cs = [m[b] for b in range(x, T * S, 8)]
+            slices = {c % S for c in cs}
+            assert len(slices) <= -(-len(cs) // T) + 1, (T, S, x)
 
 
 def test_xcd_order_is_a_permutation_into_contiguous_runs():
