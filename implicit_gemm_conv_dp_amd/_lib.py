@@ -14,7 +14,7 @@ SKG_OK, SKG_ERR_HIP, SKG_ERR_UNSUPPORTED = 0, -1, -2
 F16, BF16, F8E4M3, F32, F8E5M2 = 0, 1, 2, 3, 4
 SCALE_ROWCOL, SCALE_TENSOR, SCALE_MX_E8M0 = 0, 1, 2
 MODE_DP, MODE_DP_SK, MODE_PERSISTENT, MODE_SPLITK, MODE_AUTO = 0, 1, 2, 3, 4
-RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO = 0, 1, 2, 3, 4
+RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO, RED_SCATTER = 0, 1, 2, 3, 4, 5
 OP_GEMM, OP_WGRAD, OP_FWD, OP_DGRAD = 0, 1, 2, 3
 TILE_128x128x32, TILE_256x256x64, TILE_256x256x128, TILE_32x64x64, TILE_128x128x64, \
     TILE_256x128x64, TILE_128x128x128 = range(7)
@@ -23,7 +23,7 @@ TILE_COUNT = 7
 MODES = {"dp": MODE_DP, "dp_sk": MODE_DP_SK, "persistent": MODE_PERSISTENT,
          "splitk": MODE_SPLITK, "auto": MODE_AUTO}
 REDUCTIONS = {"linear": RED_LINEAR, "tree": RED_TREE, "atomic": RED_ATOMIC,
-              "workspace": RED_WORKSPACE, "auto": RED_AUTO}
+              "workspace": RED_WORKSPACE, "auto": RED_AUTO, "scatter": RED_SCATTER}
 DTYPES = {"f16": F16, "bf16": BF16, "e4m3": F8E4M3, "f32": F32, "e5m2": F8E5M2}
 SCALE_MODES = {"rowcol": SCALE_ROWCOL, "tensor": SCALE_TENSOR, "mx": SCALE_MX_E8M0}
 SK_ORDER_AUTO, SK_ORDER_BLOCK, SK_ORDER_XCD, SK_ORDER_KMAJOR = 0, 1, 2, 3

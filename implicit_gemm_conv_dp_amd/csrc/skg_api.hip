@@ -119,7 +119,7 @@ KPlan to_kplan(const skg_plan_t& pl, int inject) {
   k.sk_order = pl.sk_order == SKG_SK_ORDER_XCD      ? SK_ORDER_XCD
                : pl.sk_order == SKG_SK_ORDER_KMAJOR ? SK_ORDER_KMAJOR
                                                     : SK_ORDER_BLOCK;
-  k.sk_slices = pl.sk_order == SKG_SK_ORDER_KMAJOR ? (int)(pl.iters_per_tile / pl.iters_per_sk_cta) : 1;
+  k.sk_slices = whole_slices(pl) ? (int)(pl.iters_per_tile / pl.iters_per_sk_cta) : 1;
   k.spin_limit = inject == INJECT_HANDOFF ? kFaultSpin : kSpinLimit;
   k.fault = inject == INJECT_HANDOFF ? FAULT_NO_PUBLISH : FAULT_NONE;
   return k;
@@ -128,7 +128,7 @@ KPlan to_kplan(const skg_plan_t& pl, int inject) {
 Scratch carve(const skg_plan_t& pl, void* ws) {
   Scratch s{nullptr, nullptr, nullptr};
   char* base = static_cast<char*>(ws);
-  if (pl.sk_ctas && (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE)) {
+  if (pl.sk_ctas && handoff_reduction(pl.reduction)) {
     s.flags = reinterpret_cast<uint32_t*>(base);
     s.partials = reinterpret_cast<float*>(base + pl.flags_bytes);  // partials after the flags
   } else if (pl.sk_ctas && pl.reduction == SKG_RED_WORKSPACE) {
@@ -153,8 +153,8 @@ FastDiv make_fastdiv(uint32_t d) {
 int check_run(const skg_plan_t& pl, void* ws, size_t ws_bytes, int cus, int per_cu) {
   if ((size_t)pl.workspace_bytes > ws_bytes) return unsupported("workspace too small for this plan");
   if (pl.workspace_bytes && (!ws || !aligned(ws, 256))) return unsupported("workspace must be 256-byte aligned device memory");
-  if ((pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE) && pl.sk_ctas > (int64_t)cus * per_cu)
-    return unsupported("linear/tree stream-K pool exceeds the resident capacity of the device");
+  if (handoff_reduction(pl.reduction) && pl.sk_ctas > (int64_t)cus * per_cu)
+    return unsupported("linear/tree/scatter stream-K pool exceeds the resident capacity of the device");
   return SKG_OK;
 }
 
@@ -174,7 +174,7 @@ int plan_conv_with(const skg_conv_args_t* a, bool dgrad, const TileDesc& t, int 
 int reset_scratch(const skg_plan_t& pl, void* ws, hipStream_t st) {
   if (!pl.sk_ctas) return SKG_OK;
   hipError_t e = hipSuccess;
-  if (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE)
+  if (handoff_reduction(pl.reduction))
     e = hipMemsetAsync(ws, 0, (size_t)pl.flags_bytes, st);
   else if (pl.reduction == SKG_RED_WORKSPACE)
     e = hipMemsetAsync(ws, 0, (size_t)(pl.workspace_bytes - pl.aux_bytes), st);
@@ -254,7 +254,7 @@ int run_wgrad(const skg_wgrad_args_t* a, void* ws, size_t ws_bytes, hipStream_t 
   if (rc) return rc;
   if (kernel_resets) {
     size_t bytes = 0;
-    if (pl.sk_ctas && (pl.reduction == SKG_RED_LINEAR || pl.reduction == SKG_RED_TREE))
+    if (pl.sk_ctas && handoff_reduction(pl.reduction))
       bytes = (size_t)pl.flags_bytes;
     else if (pl.sk_ctas && pl.reduction == SKG_RED_WORKSPACE)
       bytes = (size_t)(pl.workspace_bytes - pl.aux_bytes);

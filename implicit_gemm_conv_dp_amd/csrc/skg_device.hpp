@@ -23,7 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F8 = 2, DT_F32 = 3, DT_BF8 = 4 };
 enum { MODE_DP = 0, MODE_DP_SK = 1, MODE_PERSISTENT = 2 };
-enum { RED_LINEAR = 0, RED_TREE = 1, RED_ATOMIC = 2, RED_WORKSPACE = 3 };
+enum { RED_LINEAR = 0, RED_TREE = 1, RED_ATOMIC = 2, RED_WORKSPACE = 3, RED_SCATTER = 5 };
 
 // ---------------------------------------------------------------------------
 // Buffer resources.  A load whose byte offset is at or beyond num_records
@@ -157,6 +157,28 @@ SKG_DEV bool flag_wait(const uint32_t* flag, uint32_t limit) {
   }
   asm volatile("" ::: "memory");  // partial loads stay after the poll
   return ok;
+}
+
+// Waits until all n flags at `flags` are set: lane i of the wave polls flags
+// i, i + 64, ...  A lane that gives up stops polling; the wave counts one
+// give-up (as flag_wait does) and returns false.
+SKG_DEV bool flags_wait_all(const uint32_t* flags, int n, uint32_t limit) {
+  bool ok = true;
+  for (int i = threadIdx.x & 63; i < n; i += 64) {
+    uint32_t t = 0;
+    while (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 1u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++t >= limit) {
+        ok = false;
+        break;
+      }
+    }
+  }
+  const bool all = __builtin_amdgcn_ballot_w64(!ok) == 0;
+  if (!all && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_add(&g_skg_wait_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::: "memory");  // partial loads stay after the polls
+  return all;
 }
 
 // ---------------------------------------------------------------------------

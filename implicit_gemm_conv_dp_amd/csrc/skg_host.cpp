@@ -83,8 +83,7 @@ static int resolve_launch(const GemmShape& g, int& mode, int& reduction, int& ct
                           int resident_per_cu, int& slices) {
   slices = 1;
   if (reduction == SKG_RED_AUTO) reduction = SKG_RED_WORKSPACE;
-  if (reduction < SKG_RED_LINEAR || reduction > SKG_RED_WORKSPACE)
-    return unsupported("unknown stream-K reduction");
+  if (!known_reduction(reduction)) return unsupported("unknown stream-K reduction");
   if (ctas == 0 || ctas < -1) return unsupported("streamk ctas must be -1 or positive");
   if (g.tiles_m <= 0 || g.tiles_n <= 0 || g.iters_per_tile <= 0) return unsupported("empty problem");
   const int64_t T = g.tiles_m * g.tiles_n, ipt = g.iters_per_tile;
@@ -147,14 +146,11 @@ int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, 
   out->slices = slices;
   // Slice-major order needs every stream-K CTA to hold one whole slice of
   // one tile; otherwise the XCD runs are taken over the CTAs themselves.
-  if (sk_order == SKG_SK_ORDER_KMAJOR) {
-    const skg_plan_t& p = *out;
-    const bool aligned = p.sk_ctas > 0 && p.extra_iters == 0 &&
-                         p.iters_per_tile % p.iters_per_sk_cta == 0 &&
-                         p.sk_ctas == p.sk_tiles * (p.iters_per_tile / p.iters_per_sk_cta);
-    if (!aligned) sk_order = SKG_SK_ORDER_XCD;
-  }
+  if (sk_order == SKG_SK_ORDER_KMAJOR && !whole_slices(*out)) sk_order = SKG_SK_ORDER_XCD;
   out->sk_order = sk_order;
+  if (reduction == SKG_RED_SCATTER && out->sk_ctas > 0 && !whole_slices(*out))
+    return unsupported("the scatter fix-up needs every stream-K CTA to hold one whole slice of "
+                       "one tile (split-K with the slice count dividing the iterations per tile)");
   return SKG_OK;
 }
 
@@ -162,9 +158,9 @@ int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, 
 // resolved launch the planner plans.
 static int check_launch_knobs(int mode, int reduction, int ctas, bool requested) {
   const int max_mode = requested ? SKG_MODE_AUTO : SKG_MODE_PERSISTENT;
-  const int max_red = requested ? SKG_RED_AUTO : SKG_RED_WORKSPACE;
   if (mode < SKG_MODE_DP || mode > max_mode) return unsupported("unknown launch mode");
-  if (reduction < SKG_RED_LINEAR || reduction > max_red) return unsupported("unknown stream-K reduction");
+  if (!known_reduction(reduction) && !(requested && reduction == SKG_RED_AUTO))
+    return unsupported("unknown stream-K reduction");
   if (ctas == 0 || ctas < -1) return unsupported("streamk ctas must be -1 or positive");
   return SKG_OK;
 }
@@ -254,7 +250,7 @@ int make_plan(const GemmShape& g, const TileDesc& t, int mode, int reduction, in
   // 10. Bytes: flags (one i32 per CTA and wave, 256-byte aligned) then one
   // fp32 partial tile per stream-K CTA; or the fp32 scratch of the workspace
   // reduction (one tile per stream-K tile).
-  if (sk_ctas && (reduction == SKG_RED_LINEAR || reduction == SKG_RED_TREE)) {
+  if (sk_ctas && handoff_reduction(reduction)) {
     p.flags_bytes = ceil_div(4 * sk_ctas * t.n_waves, 256) * 256;
     p.partials_bytes = sk_ctas * int64_t(t.tm) * t.tn * 4;
     p.workspace_bytes = p.flags_bytes + p.partials_bytes;
@@ -422,11 +418,10 @@ int skg_tile_info(int32_t tile_id, skg_tile_info_t* out) {
 }
 
 int skg_default_pool(int32_t reduction, int32_t num_cus, int32_t resident_per_cu, int32_t* out) {
-  if (reduction < SKG_RED_LINEAR || reduction > SKG_RED_WORKSPACE)
-    return unsupported("unknown stream-K reduction");
+  if (!known_reduction(reduction)) return unsupported("unknown stream-K reduction");
   if (num_cus <= 0 || resident_per_cu <= 0) return unsupported("device has no resident capacity");
   if (!out) return unsupported("null output");
-  const int per_cu = (reduction == SKG_RED_LINEAR || reduction == SKG_RED_TREE) ? 1 : 4;
+  const int per_cu = handoff_reduction(reduction) ? 1 : 4;
   *out = num_cus * (per_cu < resident_per_cu ? per_cu : resident_per_cu);
   return SKG_OK;
 }

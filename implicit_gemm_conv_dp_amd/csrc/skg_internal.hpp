@@ -27,6 +27,21 @@ struct TileDesc {
 
 const TileDesc* tile_desc(int tile_id);
 
+// Fix-ups whose CTAs hand partials on through flags (flags + partials in the
+// workspace, every stream-K CTA resident at once).
+inline bool handoff_reduction(int r) {
+  return r == SKG_RED_LINEAR || r == SKG_RED_TREE || r == SKG_RED_SCATTER;
+}
+// A resolved reduction (AUTO excluded).
+inline bool known_reduction(int r) {
+  return (r >= SKG_RED_LINEAR && r <= SKG_RED_WORKSPACE) || r == SKG_RED_SCATTER;
+}
+// Every stream-K CTA holds one whole slice of one tile.
+inline bool whole_slices(const skg_plan_t& p) {
+  return p.sk_ctas > 0 && p.extra_iters == 0 && p.iters_per_tile % p.iters_per_sk_cta == 0 &&
+         p.sk_ctas == p.sk_tiles * (p.iters_per_tile / p.iters_per_sk_cta);
+}
+
 int elem_bytes(int dtype);
 
 // GEMM-shaped view of a problem: what the partitioner needs.

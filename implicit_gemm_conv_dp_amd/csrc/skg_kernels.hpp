@@ -1457,7 +1457,7 @@ struct Engine {
     return wn * Cfg::WTN + g * Cfg::MN + acc_col<Cfg::MN>(4 * q, lane);
   }
 
-  enum { OUT_STORE = 0, OUT_ATOMIC = 1, OUT_WORKSPACE = 2, OUT_PUBLISH = 3 };
+  enum { OUT_STORE = 0, OUT_ATOMIC = 1, OUT_WORKSPACE = 2, OUT_PUBLISH = 3, OUT_SCATTER = 4 };
 
   // How a finished segment leaves the CTA: first add the partials of
   // `nfold` other stream-K CTAs, in a fixed order (partner k is cta + 1 + k
@@ -1555,6 +1555,88 @@ struct Engine {
           for (int u = 0; u < 4; ++u) acc[f][g][e + u] = add_in_agpr(acc[f][g][e + u], t[i][u]);
         });
       });
+    }
+  }
+
+  // OUT_SCATTER (whole-slice partitions): the tile's contributors are the S
+  // consecutive stream-K CTAs c0 .. c0+S-1, each with one slice.  All of
+  // them have published their partials (this one included); contributor
+  // k = cta - c0 sums float4 units [k*U/S, (k+1)*U/S) of the register-order
+  // partial over the S partials, contributor by contributor from c0, and
+  // writes them out as the copy-out would: C = cvt((v * sa[row]) * sb[col]).
+  // A unit is 4 consecutive columns of one row.
+  SKG_DEV void scatter_out(const OutTile& o, int tile, int cta) const {
+    constexpr int U = Cfg::TM * Cfg::TN / 4;
+    const int S = p.sk_slices;
+    const int c0 = (tile - p.dp_tiles) * S, k = cta - c0;
+    flags_wait_all(s.flags + c0 * Cfg::NW, S * Cfg::NW, p.spin_limit);
+    const int u0 = (int)((int64_t)k * U / S), u1 = (int)((int64_t)(k + 1) * U / S);
+    // Batches of SB partials, the smallest of 8 / 16 / 32 that holds all S
+    // (32 only with one CTA per CU: the accumulators are dead here, the
+    // batch takes 4 * SB registers).
+    if (S <= 8)
+      scatter_units<8>(o, c0, S, u0, u1);
+    else if (S <= 16 || Cfg::MIN_CTAS > 1)
+      scatter_units<16>(o, c0, S, u0, u1);
+    else
+      scatter_units<32>(o, c0, S, u0, u1);
+  }
+
+  // Units [u0, u1) of the tile from the S partials of CTAs c0 .. c0+S-1.
+  // Loads go out in batches of SB partials so that one memory round trip
+  // covers a batch.
+  template <int SB>
+  SKG_DEV void scatter_units(const OutTile& o, int c0, int S, int u0, int u1) const {
+    const int dt = Prob::dtype_c(prm);
+    const bool full = o.rows >= Cfg::TM && o.cols >= Cfg::TN;
+    // The tile's S partials are contiguous: one resource, the contributor's
+    // partial c at byte c * PB.
+    constexpr uint32_t PB = Cfg::TM * Cfg::TN * 4;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc_uniform(partial(c0), (uint32_t)S * PB);
+    for (int u = u0 + tid; u < u1; u += Cfg::THREADS) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < S; cb += SB) {
+        // Past the last contributor the batch reloads it (in bounds) and
+        // adds nothing: no load is predicated.
+        f32x4 t[SB];
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          const int c = cb + i < S ? cb + i : S - 1;
+          t[i] = load_dev16_s(r, (uint32_t)u * 16 + (uint32_t)c * PB, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+          if (cb + i < S) v = cb + i == 0 ? t[i] : v + t[i];
+      }
+      // Unit u: lane l of wave w, float4 j = (f * FN + g) * NACC/4 + q.
+      const int w = u / (PSLOTS * 64), j = (u / 64) % PSLOTS, l = u % 64;
+      const int f = j / (Cfg::FN * (Cfg::NACC / 4)), g = (j / (Cfg::NACC / 4)) % Cfg::FN;
+      const int q = j % (Cfg::NACC / 4);
+      const int row = (w / Cfg::WN) * Cfg::WTM + f * Cfg::MN + acc_row<Cfg::MN>(l);
+      const int col = (w % Cfg::WN) * Cfg::WTN + g * Cfg::MN + acc_col<Cfg::MN>(4 * q, l);
+      if (row >= o.rows) continue;
+      const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sb = o.sb && col + e < o.cols ? o.sb[(col + e) * Prob::kScaleInc] : 1.f;
+        x[e] = (v[e] * sa) * sb;
+      }
+      const size_t idx = (size_t)row * o.ld + col;
+      if (full && dt == DT_F32 && ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
+        *(f32x4*)(o.base + idx * 4) = f32x4{x[0], x[1], x[2], x[3]};
+        continue;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= o.cols) break;
+        if (dt == DT_F32)
+          ((float*)o.base)[idx + e] = x[e];
+        else if (dt == DT_F16)
+          ((uint16_t*)o.base)[idx + e] = to_f16_bits(x[e]);
+        else
+          ((uint16_t*)o.base)[idx + e] = to_bf16_bits(x[e]);
+      }
     }
   }
 
@@ -1789,6 +1871,11 @@ struct Engine {
         publish_regs(fx.cta);
         return;
       }
+      if (fx.how == OUT_SCATTER) {
+        publish_regs(fx.cta);
+        scatter_out(o, tile, fx.cta);
+        return;
+      }
     }
     write_out(o, fx, fx.how == OUT_WORKSPACE ? s.ws + (size_t)(tile - p.dp_tiles) * Cfg::TM * Cfg::TN
                                              : nullptr);
@@ -1813,6 +1900,10 @@ struct Engine {
       return fx;
     }
     if (started && ended) return fx;  // a whole tile inside one range
+    if (p.reduction == RED_SCATTER) {
+      fx.how = OUT_SCATTER;
+      return fx;
+    }
     const int sk_tile = tile - p.dp_tiles;
     const int first = cta_of(sk_tile * p.ipt);
     const int last = cta_of(sk_tile * p.ipt + p.ipt - 1);

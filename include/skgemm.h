@@ -132,14 +132,27 @@ enum skg_mode {
  *   ATOMIC     fp32 atomics into the output, which must be fp32 (the call
  *              zeroes it first);
  *   WORKSPACE  fp32 atomics into scratch, then a second-stage kernel applies
- *              the epilogue and writes the output. */
+ *              the epilogue and writes the output;
+ *   SCATTER    deterministic reduce-scatter, not one of the page's four: for
+ *              partitions that give every stream-K CTA one whole slice of
+ *              one tile (sk_ctas = sk_tiles * S, S = iters_per_tile /
+ *              iters_per_sk_cta, no extra iterations: split-K with S
+ *              dividing the iterations, or any pool that divides them so).
+ *              Every contributor publishes its fp32 partial; contributor k
+ *              of a tile's S then sums the k-th of S equal parts of the tile
+ *              over all S partials, in contributor order, and writes that
+ *              part of the output.  One round of hand-offs where linear
+ *              takes S - 1 and tree ceil(log2 S); same workspace and the
+ *              same residency rule as linear/tree.  Other partitions: -2.
+ *              Never chosen by AUTO. */
 enum skg_reduction {
   SKG_RED_LINEAR = 0,
   SKG_RED_TREE = 1,
   SKG_RED_ATOMIC = 2,
   SKG_RED_WORKSPACE = 3,
-  SKG_RED_AUTO = 4  /* resolves to WORKSPACE: it never waits, so it takes the
+  SKG_RED_AUTO = 4, /* resolves to WORKSPACE: it never waits, so it takes the
                        occupancy-sized pool (same commit as SKG_MODE_AUTO) */
+  SKG_RED_SCATTER = 5
 };
 
 /* Which stream-K CTA each block runs (the dispatch order of the partition's

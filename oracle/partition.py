@@ -31,7 +31,13 @@ pool.  Readings where the page leaves a step open:
 from dataclasses import dataclass
 
 MODES = ("dp", "dp_sk", "persistent")
-REDUCTIONS = ("linear", "tree", "atomic", "workspace")
+# "scatter" is not one of the page's four fix-ups: a one-round deterministic
+# reduce-scatter for partitions whose stream-K CTAs each hold one whole slice
+# of one tile (every contributor publishes its partial; contributor k of the
+# tile's S sums the k-th of S equal parts over all S partials in contributor
+# order).  It waits on other CTAs like linear / tree and uses their workspace.
+REDUCTIONS = ("linear", "tree", "atomic", "workspace", "scatter")
+HANDOFF = ("linear", "tree", "scatter")
 
 
 def ceil_div(a, b):
@@ -40,13 +46,13 @@ def ceil_div(a, b):
 
 def default_pool(reduction, num_cus, resident_per_cu):
     """Pool used for ``ctas = -1``: one CTA per CU for the reductions that wait
-    on other CTAs (linear, tree), four per CU for those that never wait
+    on other CTAs (linear, tree, scatter), four per CU for those that never wait
     (atomic, workspace); never more than the device keeps resident."""
     if reduction not in REDUCTIONS:
         raise ValueError("unknown reduction")
     if num_cus <= 0 or resident_per_cu <= 0:
         raise ValueError("device has no resident capacity")
-    per_cu = 1 if reduction in ("linear", "tree") else 4
+    per_cu = 1 if reduction in HANDOFF else 4
     return num_cus * min(per_cu, resident_per_cu)
 
 
@@ -73,6 +79,21 @@ class Plan:
     flags_bytes: int
     partials_bytes: int
     workspace_bytes: int       # total bytes the caller must supply
+
+    def whole_slices(self):
+        """Every stream-K CTA runs exactly one slice of one tile: the tile's
+        iterations split into S = ipt / ipc equal slices, one CTA each."""
+        ipc, ipt = self.iters_per_sk_cta, self.iters_per_tile
+        return (self.sk_ctas > 0 and self.extra_iters == 0 and ipt % ipc == 0
+                and self.sk_ctas == self.sk_tiles * (ipt // ipc))
+
+    def scatter_part(self, b, units):
+        """Units ``[lo, hi)`` of a tile's ``units`` that stream-K CTA b sums
+        and writes under the scatter fix-up, with the contributors it sums in
+        order: the k-th of S equal parts for contributor k = b mod S."""
+        S = self.iters_per_tile // self.iters_per_sk_cta
+        c0, k = (b // S) * S, b % S
+        return k * units // S, (k + 1) * units // S, list(range(c0, c0 + S))
 
     # -- the per-CTA view --------------------------------------------------
     def sk_range(self, b):
@@ -178,15 +199,18 @@ def plan(tiles_m, tiles_n, iters_per_tile, tm, tn, n_waves,
         tree_rounds += 1
     # 10. Bytes.
     flags = partials = ws = 0
-    if sk_ctas and reduction in ("linear", "tree"):
+    if sk_ctas and reduction in HANDOFF:
         flags = ceil_div(4 * sk_ctas * n_waves, 256) * 256
         partials = sk_ctas * tm * tn * 4
         ws = flags + partials
     elif sk_ctas and reduction == "workspace":
         ws = sk_tiles * tm * tn * 4
-    return Plan(tiles_m, tiles_n, T, ipt, P, mode, reduction, dp_tiles,
-                sk_tiles, sk_ctas, sk_iters, ipc, extra, grid, max_contrib,
-                max_contrib - 1, tree_rounds, n_waves, flags, partials, ws)
+    out = Plan(tiles_m, tiles_n, T, ipt, P, mode, reduction, dp_tiles,
+               sk_tiles, sk_ctas, sk_iters, ipc, extra, grid, max_contrib,
+               max_contrib - 1, tree_rounds, n_waves, flags, partials, ws)
+    if reduction == "scatter" and sk_ctas and not out.whole_slices():
+        raise ValueError("scatter needs every stream-K CTA to hold one whole slice of one tile")
+    return out
 
 
 def gemm_tiles(M, N, K, tm, tn, tk):

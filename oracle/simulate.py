@@ -19,6 +19,12 @@ Fix-up semantics modelled (tile contributors ``c_0 < c_1 < ... < c_{n-1}``,
   ``r = 0, 1, ...``: if ``p % (2s) == 0`` and ``p + s < n`` wait on
   ``c_{p+s}``; if ``p % (2s) == s`` publish and drop out.
 
+* scatter (whole-slice partitions only; not one of the page's fix-ups) --
+  every contributor publishes its partial, then waits on every other
+  contributor of the tile, lower and higher alike: the tile's contributors
+  must all be resident together, so forward progress rests on residency of
+  the whole group, not on the order of the waits.
+
 atomic and workspace have no events (nobody waits).
 """
 
@@ -29,7 +35,7 @@ def events(p: Plan, block):
     """Ordered ``("pub", cta)`` / ``("wait", cta)`` events of grid block
     ``block`` (stream-K CTAs are blocks ``[0, sk_ctas)`` in both modes)."""
     ev = []
-    if block >= p.sk_ctas or p.reduction not in ("linear", "tree"):
+    if block >= p.sk_ctas or p.reduction not in ("linear", "tree", "scatter"):
         return ev
     for (t, k0, k1, started, ended) in p.segments(block):
         if started and ended:
@@ -37,7 +43,10 @@ def events(p: Plan, block):
         contrib = p.contributors(t - p.dp_tiles)
         n = len(contrib)
         pos = contrib.index(block)
-        if p.reduction == "linear":
+        if p.reduction == "scatter":
+            ev.append(("pub", block))
+            ev += [("wait", c) for c in contrib if c != block]
+        elif p.reduction == "linear":
             if pos == 0:
                 ev += [("wait", c) for c in contrib[1:]]
             else:

@@ -88,3 +88,20 @@ def test_wgrad_repeat(index, mode, reduction):
     assert plan["sk_ctas"] > 0 and plan["max_contrib"] >= 2
     ws = skg.workspace_for(plan, "cuda")
     repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)
+
+
+@pytest.mark.parametrize("index,tile", [(3, "256x128x64"), (3, "256x256x64"), (4, "32x64x64")])
+def test_wgrad_scatter_repeat(index, tile):
+    # Split-K over the default pool with the reduce-scatter fix-up, k-major
+    # order: every launch bit-identical on random data.
+    wl = synth.WORKLOADS[index]
+    inp = wl.inputs()
+    dx, ddy = to_dev(inp["x"], wl.dtype), to_dev(inp["dy"], wl.dtype)
+    dw = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device="cuda")
+    kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
+              pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile=tile, mode="splitk",
+              reduction="scatter", ctas=-1, sk_order="kmajor")
+    plan = skg.plan_wgrad(**kw)
+    assert plan["slices"] > 1 and plan["sk_ctas"] == plan["tiles"] * plan["slices"]
+    ws = skg.workspace_for(plan, "cuda")
+    repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)

@@ -107,3 +107,30 @@ def test_forced_handoff_give_up_is_counted_and_poisons(mode, reduction):
     skg.gemm(dA, dB, C, **kw)
     torch.cuda.synchronize()
     assert np.array_equal(decode_out(C, "f32").reshape(M, N), R)
+
+
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent"])
+def test_forced_handoff_give_up_is_counted_scatter(mode):
+    # Scatter: every contributor publishes (no flag raised under the switch)
+    # and each of its waves then polls all of the tile's flags, gives up and
+    # counts once; tiles held by a single CTA stay exact.
+    A, B, R = operands()
+    dA, dB = to_dev(A, "f16"), to_dev(B, "f16")
+    C = out_buffer("f32", M * N)
+    tm, tn, tk = 128, 128, 32
+    tiles_m, tiles_n, ipt = P.gemm_tiles(M, N, K, tm, tn, tk)
+    T = tiles_m * tiles_n
+    S = next(d for d in (2, 3, 4, 5) if ipt % d == 0)
+    kw = dict(M=M, N=N, K=K, dtype_ab="f16", dtype_c="f32", tile=TILE, mode=mode,
+              reduction="scatter", ctas=T * S)
+    plan = skg.plan_gemm(**kw)
+    assert plan["sk_ctas"] == T * S and plan["sk_tiles"] == T
+    skg.skg_fixup_timeouts(reset=True)
+    with fault("handoff"):
+        skg.gemm(dA, dB, C, **kw)
+    torch.cuda.synchronize()
+    got = skg.skg_fixup_timeouts(reset=True)
+    assert got == 4 * T * S, (got, 4 * T * S)
+    skg.gemm(dA, dB, C, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_out(C, "f32").reshape(M, N), R)

@@ -355,3 +355,48 @@ def test_kmajor_sk_order_integer_exact(tile, fmt):
                 assert plan["sk_order"] == skg.SK_ORDERS["kmajor"], (T, S)
                 Y = decode_out(dC, "f32").reshape(M, N)
                 assert np.array_equal(Y, R), "%s %s %s %s S=%d kmajor" % (tile, fmt, mode, red, S)
+
+
+@pytest.mark.parametrize("tile,fmt", [("128x128x32", "f16"), ("256x256x64", "bf16"),
+                                      ("256x128x64", "f16"), ("256x256x128", "e4m3")])
+def test_scatter_fixup_integer_exact(tile, fmt):
+    # The reduce-scatter fix-up on whole-slice pools with per-row / per-column
+    # power-of-two scales applied by the contributors that write each part,
+    # ragged edge tiles included: bit-exact in both launch modes.
+    M, N, K = shape_for(tile)
+    A = synth.integer_codes(fmt, M * K, 101, 0.15)
+    B = synth.integer_codes(fmt, N * K, 102, 0.15)
+    sa, sb = synth.pow2_scales(M, 103), synth.pow2_scales(N, 104)
+    R = oracle_gemm(fmt, A, B, M, N, K, scale_a=sa, scale_b=sb)
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    p0 = skg.plan_gemm(M=M, N=N, K=K, dtype_ab=fmt, dtype_c="f32", tile=tile, mode="dp_sk",
+                       reduction="tree", ctas=8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    for S in [d for d in (2, 3, 4, 8, ipt) if ipt % d == 0]:
+        for mode in ("dp_sk", "persistent"):
+            dC = out_buffer("f32", M * N)
+            plan = skg.gemm(dA, dB, dC, to_dev_f32(sa), to_dev_f32(sb), M=M, N=N, K=K,
+                            dtype_ab=fmt, dtype_c="f32", tile=tile, mode=mode, reduction="scatter",
+                            ctas=T * S)
+            torch.cuda.synchronize()
+            assert plan["reduction"] == skg.REDUCTIONS["scatter"]
+            Y = decode_out(dC, "f32").reshape(M, N)
+            assert np.array_equal(Y, R), "%s %s %s S=%d scatter" % (tile, fmt, mode, S)
+
+
+@pytest.mark.parametrize("fmt_c", ["f16", "bf16"])
+def test_scatter_fixup_16bit_output(fmt_c):
+    # Random data, 16-bit output: the part a contributor writes goes through
+    # the same rounding as the copy-out (within the tolerance of the format).
+    tile, fmt = "128x128x64", "bf16"
+    M, N, K = shape_for(tile)
+    A = synth.to_codes(synth.draw("uniform", M * K, 1), fmt)
+    B = synth.to_codes(synth.draw("uniform", N * K, 2), fmt)
+    R = oracle_gemm(fmt, A, B, M, N, K)
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    for S in (2, 3, 8):
+        dC = out_buffer(fmt_c, M * N)
+        skg.gemm(dA, dB, dC, None, None, M=M, N=N, K=K, dtype_ab=fmt, dtype_c=fmt_c, tile=tile,
+                 mode="dp_sk", reduction="scatter", ctas=6 * S)
+        torch.cuda.synchronize()
+        assert_close(decode_out(dC, fmt_c).reshape(M, N), R, fmt, "scatter S=%d %s" % (S, fmt_c))

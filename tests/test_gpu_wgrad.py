@@ -158,6 +158,41 @@ def test_kmajor_sk_order_integer_exact(name, tile):
                                                                                red, S)
 
 
+@pytest.mark.parametrize("tile", ["32x64x64", "128x128x64", "256x128x64", "256x256x64"])
+@pytest.mark.parametrize("name", ["grouped", "long"])
+def test_scatter_fixup_integer_exact(name, tile):
+    # The reduce-scatter fix-up on whole-slice pools (tiles x S, S dividing
+    # the iterations per tile), both launch modes, both CTA orders that
+    # apply: bit-exact.
+    shape = LONG if name == "long" else SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 97)
+    _, p0 = run(x, dy, shape, "bf16", tile, "dp_sk", "workspace", 8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    ds = divisors(ipt)
+    for S in sorted({ds[0], ds[len(ds) // 2], ipt}):
+        for mode in ("dp_sk", "persistent"):
+            for order in ("xcd", "kmajor"):
+                Y, plan = run(x, dy, shape, "bf16", tile, mode, "scatter", T * S, sk_order=order)
+                assert plan["reduction"] == skg.REDUCTIONS["scatter"] and plan["sk_ctas"] == T * S
+                assert np.array_equal(Y, R), "%s %s %s S=%d %s scatter" % (name, tile, mode, S,
+                                                                          order)
+
+
+def test_scatter_fixup_full_layer():
+    # The 56x56 layer, split-K over the default pool with the scatter fix-up
+    # in k-major order, element by element against the oracle.
+    wl = synth.WORKLOADS[3]
+    inp = wl.inputs()
+    shape = (wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s, wl.stride, wl.pad, wl.groups)
+    R = oracle_wgrad(wl.dtype, inp["x"], inp["dy"], wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s,
+                     wl.stride[0], wl.stride[1], wl.pad[0], wl.pad[1], wl.groups).reshape(wl.k, -1)
+    for tile in ("256x128x64", "256x256x64"):
+        Y, plan = run(inp["x"], inp["dy"], shape, wl.dtype, tile, "splitk", "scatter", -1,
+                      sk_order="kmajor")
+        assert plan["slices"] > 1 and plan["sk_order"] == skg.SK_ORDERS["kmajor"]
+        assert_close(Y.reshape(wl.k, -1), R, wl.dtype, "%s %s scatter" % (wl.name, tile))
+
+
 @pytest.mark.parametrize("tile", ["32x64x64", "256x128x64"])
 @pytest.mark.parametrize("name", ["grouped", "wide"])
 def test_block_sk_order_integer_exact(name, tile):

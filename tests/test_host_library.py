@@ -372,3 +372,26 @@ def test_xcd_order_is_a_permutation_into_contiguous_runs():
         for x in range(8):
             run = [m[b] for b in range(x, S, 8)]
             assert run == list(range(run[0], run[0] + len(run))) if run else True, (S, x)
+
+
+def test_scatter_plan_matches_oracle_and_rejects_partial_slices():
+    # The reduce-scatter fix-up: accepted on whole-slice partitions with the
+    # oracle's plan (linear / tree workspace), -2 before any launch otherwise.
+    g = dict(M=512, N=384, K=64 * 24, dtype_ab="bf16", dtype_c="f32", tile="128x128x64")
+    for S in (2, 3, 4, 6, 8, 12, 24):
+        c = skg.plan_gemm(mode="dp_sk", reduction="scatter", ctas=12 * S, **g)
+        o = P.plan(4, 3, 24, 128, 128, 4, "dp_sk", "scatter", 12 * S)
+        assert all(c[f] == getattr(o, f) for f in FIELDS), S
+        assert c["reduction"] == _lib.RED_SCATTER
+        t = skg.plan_gemm(mode="dp_sk", reduction="tree", ctas=12 * S, **g)
+        assert c["workspace_bytes"] == t["workspace_bytes"] > 0
+        sp = skg.plan_gemm(mode="splitk", reduction="scatter", ctas=S, **g)
+        assert sp["slices"] == S and sp["sk_ctas"] == 12 * S
+    for ctas in (5, 13, 12 * 5, 12 * 7):   # ranges straddling tiles / uneven slices
+        msg = rejected(skg.plan_gemm, mode="dp_sk", reduction="scatter", ctas=ctas, **g)
+        assert "whole slice" in msg, ctas
+    assert "whole slice" in rejected(skg.plan_gemm, mode="splitk", reduction="scatter", ctas=5, **g)
+    # nothing to reduce: accepted
+    assert skg.plan_gemm(mode="dp", reduction="scatter", ctas=12, **g)["sk_ctas"] == 0
+    assert skg.skg_default_pool(_lib.RED_SCATTER, 304, 8) == 304
+    assert "reduction" in rejected(skg.plan_gemm, mode="dp_sk", reduction=6, ctas=24, **g)

@@ -221,3 +221,61 @@ def test_persistent_early_segments_only_wait_on_earlier_running_segments(reducti
                         n += 1
     if reduction == "tree":
         assert n > 100
+
+
+def test_scatter_plan_needs_whole_slices():
+    # 3 tiles x 12 iterations over 3 x 4 CTAs: 4 slices of 3 iterations each.
+    p = P.plan(1, 3, 12, 32, 32, 4, "dp_sk", "scatter", 12)
+    assert p.whole_slices() and p.iters_per_sk_cta == 3
+    # same workspace as linear / tree
+    t = P.plan(1, 3, 12, 32, 32, 4, "dp_sk", "tree", 12)
+    assert (p.flags_bytes, p.partials_bytes, p.workspace_bytes) == \
+        (t.flags_bytes, t.partials_bytes, t.workspace_bytes)
+    for pool in (5, 7, 8, 11):   # ranges that straddle tiles or split unevenly
+        assert not P.plan(1, 3, 12, 32, 32, 4, "dp_sk", "tree", pool).whole_slices()
+        with pytest.raises(ValueError):
+            P.plan(1, 3, 12, 32, 32, 4, "dp_sk", "scatter", pool)
+    # all-DP plans have nothing to reduce and are accepted
+    assert P.plan(1, 3, 12, 32, 32, 4, "dp", "scatter", 3).sk_ctas == 0
+    assert P.default_pool("scatter", 256, 2) == 256
+
+
+def test_scatter_parts_partition_every_tile():
+    # Under the scatter fix-up each tile's units are cut into the S parts its
+    # contributors write: together they cover the tile once, in contributor
+    # order, and each part sums exactly the tile's contributors (as the
+    # partitioner's own inverse map finds them).
+    n = 0
+    for T in (1, 2, 3, 5, 9, 18):
+        for ipt in (2, 6, 12, 28, 1568):
+            for S in range(2, 29):
+                if ipt % S:
+                    continue
+                p = P.plan(1, T, ipt, 32, 32, 4, "dp_sk", "scatter", T * S)
+                assert p.whole_slices()
+                for units in (256, 4096, 16384, 1000):
+                    for t in range(T):
+                        contrib = p.contributors(t)
+                        assert len(contrib) == S
+                        cover = []
+                        for b in contrib:
+                            lo, hi, who = p.scatter_part(b, units)
+                            assert who == contrib
+                            cover += list(range(lo, hi))
+                        assert cover == list(range(units)), (T, ipt, S, units, t)
+                n += 1
+    assert n > 100
+
+
+def test_scatter_needs_the_whole_group_resident():
+    # Every contributor waits on all the others, lower ids included: the
+    # group of n must be resident at once, and is enough in block order.
+    for T, ipt, n in [(1, 8, 4), (3, 12, 4), (2, 28, 7), (5, 6, 3)]:
+        p = P.plan(1, T, ipt, 32, 32, 4, "dp_sk", "scatter", T * n)
+        assert not S.waits_target_higher(p)
+        assert S.min_capacity(p) == n
+        assert not S.completes(p, n - 1)
+        assert S.completes(p, T * n)
+        assert S.events(p, 1)[0] == ("pub", 1)
+        assert sorted(c for k, c in S.events(p, 1) if k == "wait") == \
+            [c for c in range(n) if c != 1]
