@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--ctas", type=int, default=None)
     ap.add_argument("--tile", default=None)
     ap.add_argument("--sk-order", default="auto", choices=["auto", "block", "xcd", "kmajor"],
-                    help="stream-K CTA order (auto: xcd for wgrad, block for GEMM)")
+                    help="stream-K CTA order (auto: kmajor for wgrad, block for GEMM)")
     ap.add_argument("--dtype", default=None, choices=["e4m3", "e5m2"],
                     help="fp8 operand format of the fp8 GEMM workload (default e4m3)")
     ap.add_argument("--scale-mode", default=None, choices=["rowcol", "tensor"],
@@ -380,6 +380,19 @@ def table(args, dev, headline_runner):
         for key in ("pool_cap", "frac_of_pool_cap", "traffic"):
             if key in roof:
                 row[key] = roof[key]
+        extra = []
+        for (tile, mode, red, ctas) in synth.EXTRA_LAUNCHES.get(i, []):
+            r.set_launch(tile, mode, red, ctas, "auto")
+            ek, es = r.timed(TABLE_WARMUP // 5, TABLE_REPEAT // 5)
+            e = stats_us(ek)
+            eroof = roofline_of(wl, e["median"] * 1e-3, r.dtype, tile, mode, red, ctas,
+                                args.traffic, pool=r.plan["pool"] if r.plan["sk_ctas"] else None)
+            extra.append({"tile": tile, "mode": mode, "reduction": red, "ctas": ctas,
+                          "kernel_us": e, "step_us": stats_us(es), "achieved": eroof["achieved"],
+                          "unit": eroof["unit"], "frac": eroof["frac"]})
+        if extra:
+            row["extra_launches"] = extra
+            r.set_launch(wl.tile, wl.modes[0], wl.reductions[0], wl.ctas, "auto")
         if wl.op != "gemm":
             # The same kernel with every tile data-parallel (grid = tiles).
             r.set_launch(wl.tile, "dp", "linear", wl.ctas, "auto")

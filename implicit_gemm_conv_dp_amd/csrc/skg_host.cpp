@@ -131,7 +131,7 @@ static int resolve_launch(const GemmShape& g, int& mode, int& reduction, int& ct
 
 int resolve_sk_order(int requested, bool wgrad) {
   if (requested != SKG_SK_ORDER_AUTO) return requested;
-  return wgrad ? SKG_SK_ORDER_XCD : SKG_SK_ORDER_BLOCK;
+  return wgrad ? SKG_SK_ORDER_KMAJOR : SKG_SK_ORDER_BLOCK;
 }
 
 int plan_launch(const GemmShape& g, const TileDesc& t, int mode, int reduction, int ctas,

@@ -207,15 +207,18 @@ class ConvWorkload:
 # The five workloads.  Tiles for 1, 2 and 4 are the ones the workloads name;
 # 3 and 5 use the tiles measured fastest for them.  Workload 4 runs its pool
 # at the resident capacity of the 32x64x64 tile (two CTAs per CU), which
-# keeps twice the loads in flight on this latency-bound shape.
+# keeps twice the loads in flight on this latency-bound shape.  Workload 3
+# runs 256x256 tiles (9 output tiles) over a pool of 252 = 9 x 28 CTAs: every
+# stream-K CTA then holds 56 whole iterations of one tile, which the k-major
+# CTA order turns into 28 k ranges read by all 9 tiles at about the same time.
 WORKLOADS = {
     1: GemmWorkload(1, "gemm_f16_256x256x4096_pool6_linear", 256, 256, 4096, "f16", "f16",
                     "uniform", "128x128x32", ("dp_sk",), ("linear",), 6),
     2: GemmWorkload(2, "gemm_bf16_4864x4096x4096_tree", 4864, 4096, 4096, "bf16", "bf16",
                     "normal01", "256x256x64", ("persistent", "dp_sk"), ("tree",), 256),
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
-                     (1, 1), (1, 1), 1, "f16", "uniform", "256x128x64",
-                     ("dp_sk", "persistent"), ("workspace", "linear", "tree", "atomic"), 256),
+                     (1, 1), (1, 1), 1, "f16", "uniform", "256x256x64",
+                     ("persistent", "dp_sk"), ("tree", "linear", "atomic", "workspace"), 252),
     4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
                      (2, 2), (1, 1), 32, "bf16", "uniform", "32x64x64", ("dp_sk",), ("linear",),
                      512),
@@ -247,6 +250,10 @@ NEXT_WORKLOADS = {
                      "normal", "128x128x128", ("persistent",), ("workspace",), 512, scales=True,
                      scale_mode="mx"),
 }
+
+# Further launches of a workload reported beside its own: the dense wgrad
+# layer with the reduce-scatter fix-up (not one of the page's four).
+EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "scatter", 252)]}
 
 # Earlier name of the first four of them.
 LAYER_WORKLOADS = {i: w for i, w in NEXT_WORKLOADS.items() if i in (6, 7, 8, 9)}

@@ -158,9 +158,10 @@ enum skg_reduction {
 /* Which stream-K CTA each block runs (the dispatch order of the partition's
  * CTAs; the partition itself is the same).  Workgroups go to the 8 XCDs of
  * gfx950 round robin, block i to XCD i mod 8, and each XCD has its own L2.
- *   SKG_SK_ORDER_AUTO   XCD for wgrad, BLOCK for GEMM (measured: wgrad's
- *                       neighbouring stream-K CTAs read the same operand
- *                       lines, GEMM's do not);
+ *   SKG_SK_ORDER_AUTO   KMAJOR for wgrad (so XCD where the slices are not
+ *                       whole), BLOCK for GEMM (measured: wgrad's stream-K
+ *                       CTAs share the dY and X rows of a k range, GEMM's
+ *                       neighbouring CTAs do not share lines);
  *   SKG_SK_ORDER_BLOCK  block b runs stream-K CTA b;
  *   SKG_SK_ORDER_XCD    the stream-K CTAs are dealt to the XCDs in contiguous
  *                       runs: block b runs CTA x*q + min(x, r) + b/8 with
