@@ -359,5 +359,17 @@ SKG_DEV uint16_t to_f16_bits(float v) {
 SKG_DEV uint16_t to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
+// Two values rounded to nearest even and packed (a in the low half): one
+// v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950.
+SKG_DEV uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+}
+SKG_DEV uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
 
 }  // namespace skg

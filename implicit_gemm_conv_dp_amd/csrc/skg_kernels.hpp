@@ -1663,12 +1663,14 @@ struct Engine {
     return Row{*(const SKG_LDS f32x4*)p, *(const SKG_LDS f32x4*)(p + 16)};
   }
 
-  template <int HOW, int DTC>
+  // SCALED: apply the row / column scales; without scales the products
+  // would be v * 1 * 1, skipped (bit-identical).
+  template <int HOW, int DTC, bool SCALED>
   SKG_DEV void emit_full(const Row& r, const OutTile& o, const Fix& fx, float* wsp, int row, int col,
                          int tofs, float sa, const f32x4& sb0, const f32x4& sb1) const {
     {
       static_assert(HOW == OUT_STORE, "atomic fix-ups copy out through atomic_full");
-      const f32x4 w0 = (r.v0 * sa) * sb0, w1 = (r.v1 * sa) * sb1;
+      const f32x4 w0 = SCALED ? (r.v0 * sa) * sb0 : r.v0, w1 = SCALED ? (r.v1 * sa) * sb1 : r.v1;
       const size_t idx = (size_t)row * o.ld + col;
       if constexpr (DTC == DT_F32) {
         // C is written once and not read back here: non-temporal stores.
@@ -1679,13 +1681,12 @@ struct Engine {
         i32x4 h;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float a0 = w0[2 * e], a1 = w0[2 * e + 1], b0 = w1[2 * e], b1 = w1[2 * e + 1];
           if constexpr (DTC == DT_F16) {
-            h[e] = (int)(to_f16_bits(a0) | ((uint32_t)to_f16_bits(a1) << 16));
-            h[e + 2] = (int)(to_f16_bits(b0) | ((uint32_t)to_f16_bits(b1) << 16));
+            h[e] = (int)pack_f16x2(w0[2 * e], w0[2 * e + 1]);
+            h[e + 2] = (int)pack_f16x2(w1[2 * e], w1[2 * e + 1]);
           } else {
-            h[e] = (int)(to_bf16_bits(a0) | ((uint32_t)to_bf16_bits(a1) << 16));
-            h[e + 2] = (int)(to_bf16_bits(b0) | ((uint32_t)to_bf16_bits(b1) << 16));
+            h[e] = (int)pack_bf16x2(w0[2 * e], w0[2 * e + 1]);
+            h[e + 2] = (int)pack_bf16x2(w1[2 * e], w1[2 * e + 1]);
           }
         }
         __builtin_nontemporal_store(h, (i32x4*)((uint16_t*)o.base + idx));
@@ -1707,7 +1708,7 @@ struct Engine {
   }
 
   // Copy-out of one pass of a full tile: no bounds checks.
-  template <int HOW, int DTC>
+  template <int HOW, int DTC, bool SCALED>
   SKG_DEV void copy_full(const OutTile& o, const Fix& fx, float* wsp, int pass, int col,
                          const f32x4& sb0, const f32x4& sb1, const float (&sav)[NR]) const {
     const int lr0 = tid / CPRO;
@@ -1716,9 +1717,16 @@ struct Engine {
     for (int i = 0; i < NR; ++i) {
       const int lr = lr0 + i * RSTEP, row = pass * Cfg::WTM + lr;
       Row r = staged(lr, col);
-      const int tofs = row * Cfg::TN + col;
-      emit_full<HOW, DTC>(r, o, fx, wsp, row, col, tofs, sav[i], sb0, sb1);
+      emit_full<HOW, DTC, SCALED>(r, o, fx, wsp, row, col, row * Cfg::TN + col, sav[i], sb0, sb1);
     }
+  }
+  template <int DTC>
+  SKG_DEV void copy_full_store(const OutTile& o, const Fix& fx, float* wsp, int pass, int col,
+                               const f32x4& sb0, const f32x4& sb1, const float (&sav)[NR]) const {
+    if (o.sa || o.sb)
+      copy_full<OUT_STORE, DTC, true>(o, fx, wsp, pass, col, sb0, sb1, sav);
+    else
+      copy_full<OUT_STORE, DTC, false>(o, fx, wsp, pass, col, sb0, sb1, sav);
   }
 
   // Atomic copy-out of one pass of a full tile (atomic and workspace
@@ -1842,11 +1850,11 @@ struct Engine {
       } else if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC) {
         atomic_full<OUT_ATOMIC>(o, wsp, pass);
       } else if (dt == DT_F32) {
-        copy_full<OUT_STORE, DT_F32>(o, fx, wsp, pass, col, sb0, sb1, sav);
+        copy_full_store<DT_F32>(o, fx, wsp, pass, col, sb0, sb1, sav);
       } else if (dt == DT_F16) {
-        copy_full<OUT_STORE, DT_F16>(o, fx, wsp, pass, col, sb0, sb1, sav);
+        copy_full_store<DT_F16>(o, fx, wsp, pass, col, sb0, sb1, sav);
       } else {
-        copy_full<OUT_STORE, DT_BF16>(o, fx, wsp, pass, col, sb0, sb1, sav);
+        copy_full_store<DT_BF16>(o, fx, wsp, pass, col, sb0, sb1, sav);
       }
       __syncthreads();
     }
