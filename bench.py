@@ -47,8 +47,12 @@ SCRUB_BYTES = 512 << 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # A step of the headline workload takes ~0.16 ms: 200 untimed steps
+    # (~30 ms) bring the GPU to its steady state (with 10, the kernel ran
+    # 168 instead of 150 us per launch on the same box), 400 timed ones
+    # take ~60 ms.
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=2, choices=list(range(1, 11)),
                     help="headline workload (value, roofline, cpu_baseline); 6-9 are the "
                          "forward and dgrad convolutions of the two wgrad layers, 10 the fp8 "
