@@ -303,7 +303,8 @@ int validate_gemm(const skg_gemm_args_t* a) {
   if (a->scale_mode == SKG_SCALE_MX_E8M0) {
     if (a->dtype_ab != SKG_F8E4M3 && a->dtype_ab != SKG_F8E5M2)
       return unsupported("MX block scales need fp8 or bf8 inputs");
-    if (a->tile_id != SKG_TILE_128x128x128) return unsupported("MX block scales need the 128x128x128 tile");
+    if (a->tile_id != SKG_TILE_128x128x128 && a->tile_id != SKG_TILE_256x256x128)
+      return unsupported("MX block scales need the 128x128x128 or 256x256x128 tile");
     if (a->K % 128) return unsupported("MX block scales need K to be a multiple of 128");
   }
   if (a->sk_order < SKG_SK_ORDER_AUTO || a->sk_order > SKG_SK_ORDER_KMAJOR)

@@ -8,7 +8,10 @@ template <int DT>
 GemmInst f8_by_tile(int tile_id, int scale_mode) {
   const bool tensor = scale_mode == SKG_SCALE_TENSOR;
   if (tile_id == SKG_TILE_256x256x128) {
-    if (scale_mode == SKG_SCALE_MX_E8M0) return {nullptr, nullptr};
+    if (scale_mode == SKG_SCALE_MX_E8M0) {
+      typedef TileCfg<DT, 256, 256, 128, 2, 2, 32, 128, true> Cfg;
+      return {&launch_instance<Cfg, GemmMxProblem<Cfg>>, &occupancy_instance<Cfg, GemmMxProblem<Cfg>>};
+    }
     return gemm_inst::make<TileCfg<DT, 256, 256, 128, 2, 2, 32, 128>>(tensor);
   }
   if (tile_id == SKG_TILE_128x128x128) {

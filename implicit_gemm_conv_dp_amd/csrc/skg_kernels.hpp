@@ -382,6 +382,20 @@ struct MxGrpLoader : GemmGrpLoader<Cfg> {
       scales_b(it, slot, live);
   }
   SKG_DEV void issue(int j, int it, SKG_LDS char* slot) const { issue_live(j, it, slot, true); }
+
+  // DMA instruction N of a refill spread among the MFMAs, in the order of
+  // issue_live: the B group's rows, its scale word, then the A group's.
+  template <int N>
+  SKG_DEV void refill(const typename Base::Refill& r) const {
+    if constexpr (N < Rows::UB)
+      Base::template refill<N>(r);
+    else if constexpr (N == Rows::UB)
+      scales_b(r.it_b, r.slot_b, r.live_b);
+    else if constexpr (N < UB + Rows::UA)
+      Base::template refill<Rows::UB + (N - UB)>(r);
+    else
+      scales_a(r.it_a, r.slot_a, r.live_a);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -828,8 +842,8 @@ struct Engine {
   // byte 2 that of k-step 1.
   static constexpr bool kMx = LoaderMx<Loader>::value;
   // One CTA per CU: the burst schedule spreads its refills among the MFMAs
-  // (grp_iter_burst).  Not with MX scales (mma_dma issues plain MFMAs).
-  static constexpr bool kDefer = Cfg::MIN_CTAS == 1 && !kMx;
+  // (grp_iter_burst).
+  static constexpr bool kDefer = Cfg::MIN_CTAS == 1;
   uint32_t msa[Cfg::FM], msb[Cfg::FN], nsa[Cfg::FM], nsb[Cfg::FN];
 
   SKG_DEV Engine(const Params& prm_, const KPlan& p_, const Scratch& s_, SKG_LDS char* lds_)
@@ -1193,13 +1207,13 @@ struct Engine {
   // The MFMAs of rows [F0, F1) of one k-step with DMA instructions
   // [D0, D1) of a refill spread among them in program order, so that the
   // wave issues each DMA while an MFMA runs instead of in one burst.
-  template <int F0, int F1, int D0, int D1, class Refill>
+  template <int F0, int F1, int D0, int D1, int KS = 0, class Refill>
   SKG_DEV void mma_dma(const FragA& fa, const FragB& fb, const Loader& ld, const Refill& rf) {
     constexpr int NM = (F1 - F0) * Cfg::FN, ND = D1 - D0;
     static_for<0, NM>([&](auto m_) {
       constexpr int m = decltype(m_)::value;
       constexpr int f = F0 + m / Cfg::FN, g = m % Cfg::FN;
-      Cfg::Op::run(acc[f][g], fb[g], fa[f]);  // transposed block
+      mfma(f, g, fa[f], fb[g], KS);  // transposed block (k-step KS's scales under MX)
       if constexpr (ND > 0) {
         // DMA d follows MFMA (d * NM) / ND
         static_for<0, ND>([&](auto d_) {
@@ -1273,7 +1287,7 @@ struct Engine {
           wait_vm<Loader::UA>();
           lds_barrier();
         }
-        mma_dma<f, f + 1, D0, D0 + RD>(fa, fb[CB], ld, rf);
+        mma_dma<f, f + 1, D0, D0 + RD, ks>(fa, fb[CB], ld, rf);
         if constexpr (f == 0) {
           fa[FM - 1] = one_frag<true>(sa, FM - 1, ks);
         }
@@ -1342,7 +1356,7 @@ struct Engine {
       constexpr int ks = decltype(ks_)::value, ND = Loader::UA + Loader::UB, KS = Cfg::KSTEPS - 1;
       grp_frags(fa[(ks + 1) & 1], fb[(ks + 1) & 1], sa, sb, tb, ks + 1);
       if constexpr (kDefer && DMA)
-        mma_dma<0, Cfg::FM, ks * ND / KS, (ks + 1) * ND / KS>(fa[ks & 1], fb[ks & 1], ld, rf);
+        mma_dma<0, Cfg::FM, ks * ND / KS, (ks + 1) * ND / KS, ks>(fa[ks & 1], fb[ks & 1], ld, rf);
       else
         mma(fa[ks & 1], fb[ks & 1], ks);
       __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region

@@ -232,7 +232,8 @@ WORKLOADS = {
 # the launches measured fastest (256x256x64 tiles, persistent, tree fix-up
 # for the dense layer; 128x128x64 tiles for the grouped one, 16 channels per
 # group, where every plan is all-DP), and the fp8 GEMM of workload 5 with OCP
-# MX (E8M0) block scales instead of row/column scales.
+# MX (E8M0) block scales instead of row/column scales (256x256x128 tiles:
+# 4 ring slots once the scale bytes ride along, refilled among the MFMAs).
 NEXT_WORKLOADS = {
     6: ConvWorkload(6, "fwd_f16_n32_56x56_c256_k256_3x3", "fwd", 32, 56, 56, 256, 256, 3, 3,
                     (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
@@ -247,7 +248,7 @@ NEXT_WORKLOADS = {
                     3, 3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
                     ("tree",), 256),
     10: GemmWorkload(10, "gemm_e4m3_8192x8192x8192_mx_e8m0", 8192, 8192, 8192, "e4m3", "bf16",
-                     "normal", "128x128x128", ("persistent",), ("workspace",), 512, scales=True,
+                     "normal", "256x256x128", ("persistent",), ("workspace",), 256, scales=True,
                      scale_mode="mx"),
 }
 

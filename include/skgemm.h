@@ -87,8 +87,9 @@ enum skg_scale_mode {
    *                    consecutive K elements of a row of A or a column of B:
    *                    C[m][n] = round(sum_b 2^(sa[m][b]-127) 2^(sb[n][b]-127)
    *                    sum_{k in b} a(m,k) b(k,n)).  fp8 / bf8 inputs, the
-   *                    128x128x128 tile, K a multiple of 128, both pointers
-   *                    non-NULL and 16-byte aligned; no further scale. */
+   *                    128x128x128 or 256x256x128 tile, K a multiple of 128,
+   *                    both pointers non-NULL and 16-byte aligned; no
+   *                    further scale. */
   SKG_SCALE_MX_E8M0 = 2
 };
 
@@ -198,7 +199,7 @@ enum skg_sk_order {
 enum skg_tile {
   SKG_TILE_128x128x32 = 0,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_256x256x64 = 1,   /* f16/bf16 GEMM and wgrad, 4 waves */
-  SKG_TILE_256x256x128 = 2,  /* fp8 GEMM, 4 waves */
+  SKG_TILE_256x256x128 = 2,  /* fp8 GEMM (also with MX block scales), 4 waves */
   SKG_TILE_32x64x64 = 3,     /* f16/bf16 wgrad (small per-group M), 4 waves */
   SKG_TILE_128x128x64 = 4,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_256x128x64 = 5,   /* f16/bf16 GEMM and wgrad, 4 waves */

@@ -27,25 +27,28 @@ pytestmark = pytest.mark.gpu
 MODES = ["dp", "dp_sk", "persistent"]
 REDS = ["linear", "tree", "atomic", "workspace"]
 TILE = "128x128x128"
+TILES = ["128x128x128", "256x256x128"]
 
 
 def e8m0(n, seed, lo, hi):
     return (127 + synth.rng(seed).integers(lo, hi + 1, n)).astype(np.uint8)
 
 
-def run(A, B, SA, SB, M, N, K, fmt, fmt_c, mode, red, ctas):
+def run(A, B, SA, SB, M, N, K, fmt, fmt_c, mode, red, ctas, tile=TILE):
     dC = out_buffer(fmt_c, M * N)
     plan = skg.gemm(to_dev(A, fmt), to_dev(B, fmt), dC,
                     torch.from_numpy(SA).to("cuda"), torch.from_numpy(SB).to("cuda"),
-                    M=M, N=N, K=K, dtype_ab=fmt, dtype_c=fmt_c, tile=TILE, mode=mode,
+                    M=M, N=N, K=K, dtype_ab=fmt, dtype_c=fmt_c, tile=tile, mode=mode,
                     reduction=red, ctas=ctas, scale_mode="mx")
     torch.cuda.synchronize()
     return decode_out(dC, fmt_c).reshape(M, N), plan
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-def test_integer_exact_all_modes_and_fixups(fmt):
-    M, N, K = 2 * 128 + 40, 128 + 72, 18 * 128
+def test_integer_exact_all_modes_and_fixups(fmt, tile):
+    tm = int(tile.split("x")[0])
+    M, N, K = 2 * tm + 40, tm + 72, 18 * 128
     A = synth.integer_codes(fmt, M * K, 51, 0.2)
     B = synth.integer_codes(fmt, N * K, 52, 0.2)
     SA, SB = e8m0(M * K // 32, 53, -4, 4), e8m0(N * K // 32, 54, -4, 4)
@@ -56,13 +59,14 @@ def test_integer_exact_all_modes_and_fixups(fmt):
             if mode == "dp" and red != "linear":
                 continue
             for ctas in (5, 13):
-                Y, plan = run(A, B, SA, SB, M, N, K, fmt, "f32", mode, red, ctas)
-                assert np.array_equal(Y, R), "%s %s %s ctas=%d: not bit-exact (max diff %g)" % (
-                    fmt, mode, red, ctas, np.nanmax(np.abs(Y - R)))
+                Y, plan = run(A, B, SA, SB, M, N, K, fmt, "f32", mode, red, ctas, tile)
+                assert np.array_equal(Y, R), "%s %s %s %s ctas=%d: not bit-exact (max diff %g)" % (
+                    tile, fmt, mode, red, ctas, np.nanmax(np.abs(Y - R)))
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-def test_random_within_tolerance(fmt):
+def test_random_within_tolerance(fmt, tile):
     M, N, K = 3 * 128 + 8, 2 * 128 + 16, 20 * 128
     A = synth.to_codes(synth.draw("normal", M * K, 61), fmt)
     B = synth.to_codes(synth.draw("normal", N * K, 62), fmt)
@@ -70,17 +74,18 @@ def test_random_within_tolerance(fmt):
     R = gemm_mx(fmt, A, B, SA, SB, M, N, K)
     for mode, red, fmt_c in (("dp", "linear", "bf16"), ("dp_sk", "tree", "bf16"),
                              ("persistent", "workspace", "f32"), ("dp_sk", "atomic", "f32")):
-        Y, plan = run(A, B, SA, SB, M, N, K, fmt, fmt_c, mode, red, 11)
-        assert_close(Y, R, fmt, "mx %s %s %s" % (fmt, mode, red))
+        Y, plan = run(A, B, SA, SB, M, N, K, fmt, fmt_c, mode, red, 11, tile)
+        assert_close(Y, R, fmt, "mx %s %s %s %s" % (tile, fmt, mode, red))
 
 
-def test_full_size_sampled():
+@pytest.mark.parametrize("tile,ctas", [("128x128x128", 512), ("256x256x128", 256)])
+def test_full_size_sampled(tile, ctas):
     M = N = K = 8192
     g = synth.rng(71)
     A = synth.to_codes(synth.draw("normal", M * K, 72), "e4m3")
     B = synth.to_codes(synth.draw("normal", N * K, 73), "e4m3")
     SA, SB = e8m0(M * K // 32, 74, -3, 3), e8m0(N * K // 32, 75, -3, 3)
-    Y, plan = run(A, B, SA, SB, M, N, K, "e4m3", "bf16", "persistent", "workspace", 512)
+    Y, plan = run(A, B, SA, SB, M, N, K, "e4m3", "bf16", "persistent", "workspace", ctas, tile)
     assert not np.isnan(Y).any(), "unwritten outputs"
     idx = [(int(g.integers(M)), int(g.integers(N))) for _ in range(400)]
     ref = np.array([gemm_mx_entry("e4m3", A, B, SA, SB, m, n, K) for m, n in idx])
@@ -93,7 +98,7 @@ def test_mx_rejections():
     M, N, K = 128, 128, 256
     base = dict(M=M, N=N, K=K, dtype_ab="e4m3", dtype_c="bf16", tile=TILE, mode="dp_sk",
                 reduction="linear", ctas=4, scale_mode="mx")
-    for bad in (dict(tile="256x256x128"), dict(K=192), dict(dtype_ab="bf16", tile="128x128x64")):
+    for bad in (dict(tile="256x256x64"), dict(K=192), dict(dtype_ab="bf16", tile="128x128x64")):
         with pytest.raises(skg.SkgError) as ei:
             skg.plan_gemm(**dict(base, **bad))
         assert ei.value.status == -2
