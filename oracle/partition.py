@@ -219,15 +219,26 @@ def gemm_tiles(M, N, K, tm, tn, tk):
 
 
 def wgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups,
-                tm, tn, tk):
+                tm, tn, tk, group_block=0):
     """Implicit-GEMM view of a wgrad: GEMM-M = output channels, folded per
     group (the tile count is per group, so a partial last M tile stays inside
-    its group), GEMM-N = Cpg*R*S, reduction = N*Ho*Wo."""
+    its group), GEMM-N = Cpg*R*S, reduction = N*Ho*Wo.
+
+    group_block > 0: block-diagonal tiles, each holding group_block whole
+    consecutive groups (tm = group_block * Kpg output channels; the columns
+    of every row are its own group's Cpg*R*S filter entries), so GEMM-M is
+    tiled over all K output channels at once and only the last M tile can
+    hold fewer groups."""
     ho = (H + 2 * pad_h - R) // stride_h + 1
     wo = (W + 2 * pad_w - S) // stride_w + 1
     kpg, cpg = K // groups, C // groups
-    return (groups * ceil_div(kpg, tm), ceil_div(cpg * R * S, tn),
-            ceil_div(N * ho * wo, tk))
+    if group_block:
+        if tm != group_block * kpg:
+            raise ValueError("a block-diagonal tile holds group_block whole groups")
+        tiles_m = ceil_div(groups, group_block)
+    else:
+        tiles_m = groups * ceil_div(kpg, tm)
+    return (tiles_m, ceil_div(cpg * R * S, tn), ceil_div(N * ho * wo, tk))
 
 
 def fwd_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk):

@@ -95,6 +95,47 @@ def test_wgrad_tiles_fold_groups():
     assert P.wgrad_tiles(32, 56, 56, 256, 256, 3, 3, 1, 1, 1, 1, 1, 128, 128, 32) == (2, 18, 3136)
 
 
+def bd_tiles_by_brute_force(K, groups, cpg_rs, tm, tn, gb):
+    """Tiles of a block-diagonal wgrad found by walking every dW element:
+    output channel k belongs to group k // Kpg, and the tile holding it is
+    the one holding its group among consecutive runs of gb groups."""
+    kpg = K // groups
+    tiles = set()
+    for k in range(K):
+        for n in range(cpg_rs):
+            tiles.add(((k // kpg) // gb, n // tn))
+    rows = {}
+    for (i, _) in tiles:
+        rows[i] = [k for k in range(K) if (k // kpg) // gb == i]
+    for i, ks in rows.items():
+        # a tile's rows are whole groups, at most tm of them, contiguous
+        assert len(ks) <= tm and ks == list(range(ks[0], ks[0] + len(ks)))
+        assert len(ks) % kpg == 0
+    tm_count = len({i for (i, _) in tiles})
+    tn_count = len({j for (_, j) in tiles})
+    assert len(tiles) == tm_count * tn_count
+    return tm_count, tn_count
+
+
+def test_wgrad_tiles_block_diagonal():
+    # 32 groups of 16: four groups per 64-row tile -> 8 M tiles; the 144
+    # columns (3x3 taps of 16 channels) in one 144-wide N tile; reduction
+    # 64*14*14 in steps of 32.
+    assert P.wgrad_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 64, 144, 32,
+                         group_block=4) == (8, 1, 392)
+    for groups in (1, 3, 4, 5, 6, 9, 32):
+        for r, s in ((1, 1), (3, 3), (5, 5)):
+            K = C = 16 * groups
+            t = P.wgrad_tiles(2, 9, 9, C, K, r, s, 1, 1, r // 2, s // 2, groups, 64, 144, 32,
+                              group_block=4)
+            assert t[:2] == bd_tiles_by_brute_force(K, groups, 16 * r * s, 64, 144, 4)
+    # one group per tile and tm = Kpg is the per-group count
+    assert P.wgrad_tiles(4, 8, 8, 64, 64, 3, 3, 1, 1, 1, 1, 4, 16, 144, 32, group_block=1) == \
+        P.wgrad_tiles(4, 8, 8, 64, 64, 3, 3, 1, 1, 1, 1, 4, 16, 144, 32)
+    with pytest.raises(ValueError):
+        P.wgrad_tiles(4, 8, 8, 64, 64, 3, 3, 1, 1, 1, 1, 4, 32, 144, 32, group_block=4)
+
+
 def test_all_dp_plan_has_safe_divisor():
     p = P.plan(4, 4, 10, 64, 64, 4, "dp_sk", "linear", 16)
     assert p.sk_ctas == 0 and p.iters_per_sk_cta == 1 and p.workspace_bytes == 0
