@@ -31,6 +31,7 @@ const TileDesc kTiles[SKG_TILE_COUNT] = {
     /* 128x128x64  */ {128, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
     /* 256x128x64  */ {256, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
     /* 128x128x128 */ {128, 128, 128, 4, M_F8, 0, 0},
+    /* 64x144x32   */ {64, 144, 32, 4, 0, M_F16 | M_BF16, 0, 4},
 };
 
 // Offsets inside one buffer are 32-bit on the device (buffer resources).
@@ -269,9 +270,11 @@ GemmShape wgrad_shape(const skg_wgrad_args_t* a, const TileDesc& t) {
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   const int64_t kpg = a->k / a->groups, cpg = a->c / a->groups;
-  // Groups fold into GEMM-M with the tile count defined per group.
-  return {int64_t(a->groups) * ceil_div(kpg, t.tm), ceil_div(cpg * a->r * a->s, t.tn),
-          ceil_div(int64_t(a->n) * ho * wo, t.tk)};
+  // Groups fold into GEMM-M: dense tiles are counted per group, a
+  // block-diagonal tile holds group_block whole groups.
+  const int64_t tiles_m = t.group_block ? ceil_div(a->groups, t.group_block)
+                                        : int64_t(a->groups) * ceil_div(kpg, t.tm);
+  return {tiles_m, ceil_div(cpg * a->r * a->s, t.tn), ceil_div(int64_t(a->n) * ho * wo, t.tk)};
 }
 
 GemmShape conv_shape(const skg_conv_args_t* a, const TileDesc& t, bool dgrad) {
@@ -346,6 +349,8 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
     return unsupported("groups must divide C and K");
   const int64_t cpg = a->c / a->groups, kpg = a->k / a->groups;
   if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
+  if (t->group_block && (cpg != 16 || kpg != 16))
+    return unsupported("the block-diagonal wgrad tile needs 16 input and 16 output channels per group");
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)
@@ -381,6 +386,8 @@ int validate_conv(const skg_conv_args_t* a, bool dgrad) {
     return unsupported("groups must divide C and K");
   const int64_t cpg = a->c / a->groups, kpg = a->k / a->groups;
   if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
+  if (t->group_block && (cpg != 16 || kpg != 16))
+    return unsupported("the block-diagonal wgrad tile needs 16 input and 16 output channels per group");
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)
@@ -415,6 +422,7 @@ int skg_tile_info(int32_t tile_id, skg_tile_info_t* out) {
   out->gemm_dtypes = t->gemm_mask;
   out->wgrad_dtypes = t->wgrad_mask;
   out->conv_dtypes = t->conv_mask;
+  out->group_block = t->group_block;
   return SKG_OK;
 }
 

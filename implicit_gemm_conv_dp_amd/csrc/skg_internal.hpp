@@ -23,6 +23,7 @@ struct TileDesc {
   int gemm_mask;   // 1 << skg_dtype accepted as GEMM A/B
   int wgrad_mask;  // 1 << skg_dtype accepted as wgrad X/dY
   int conv_mask;   // 1 << skg_dtype accepted for forward conv / dgrad
+  int group_block; // block-diagonal wgrad tile: whole 16-channel groups per tile (0: dense)
 };
 
 const TileDesc* tile_desc(int tile_id);

@@ -88,7 +88,10 @@ struct WgradParams {
 // ---------------------------------------------------------------------------
 // MX_: the operand slots also hold each row's E8M0 block scales of the
 // iteration (4 bytes per row after the row data).
-template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64, bool MX_ = false>
+// BDG_ > 0: block-diagonal grouped wgrad tile holding BDG_ whole groups of
+// 16 channels (WgradBdLoader).
+template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64, bool MX_ = false,
+          int BDG_ = 0>
 struct TileCfg {
   static constexpr int DT = DT_, TM = TM_, TN = TN_, TK = TK_, WM = WM_, WN = WN_, MN = MN_;
   static constexpr bool MX = MX_;
@@ -142,13 +145,26 @@ struct TileCfg {
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
   static constexpr bool SPREAD = TM == 256 && TN == 256 && !MX_;
+  // Block-diagonal tile: a MAC iteration is the A tile (TK rows of the
+  // tile's TM output channels) followed by one plane per filter tap (TK
+  // rows of the same TM input channels at that tap's pixel), BD_ITER bytes;
+  // a ring of BD_D iterations takes the whole LDS.
+  static constexpr int BDG = BDG_;
+  static constexpr int BD_TAPS = TN / 16;
+  static constexpr int BD_PLANE = TK * TM * 2;
+  static constexpr int BD_ITER = BD_PLANE * (1 + BD_TAPS);
+  static constexpr int BD_D = BDG_ ? 160 * 1024 / BD_ITER : 0;
+  static constexpr int LDS_BD = BD_D * BD_ITER;
   // Resident CTAs per CU the register allocation must allow: tiles of up
-  // to 128x128 keep two (their LDS fits twice), larger ones take the CU.
-  static constexpr int MIN_CTAS = TM * TN <= 128 * 128 ? 2 : 1;
+  // to 128x128 keep two (their LDS fits twice), larger ones and the
+  // block-diagonal tile take the CU.
+  static constexpr int MIN_CTAS = BDG_ ? 1 : TM * TN <= 128 * 128 ? 2 : 1;
   static_assert(RB == 64 || RB == 128, "LDS row layout");
   static_assert(FM >= 1 && FN >= 1 && WTM % MN == 0 && WTN % MN == 0, "wave tile");
   static_assert(KSTEPS >= 1 && RB % Op::KB == 0, "k steps");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(BDG_ == 0 || (TM == 16 * BDG_ && MN == 16 && WM == BDG_ && WN == 1 && BD_D >= 2),
+                "block-diagonal tile: one wave per group");
 };
 
 // ---------------------------------------------------------------------------
@@ -805,6 +821,162 @@ struct WgradProblem {
 };
 
 // ---------------------------------------------------------------------------
+// Block-diagonal grouped wgrad (16 input and 16 output channels per group):
+// the tile's TM output channels are BDG whole groups, and their input
+// channels are the same index range [k0, k0 + TM).  Row k of the tile only
+// meets its own group's input channels, so the tile is not a dense GEMM
+// tile: wave w owns group w, i.e. rows [16w, 16w + 16), and all TN = 16 *
+// taps columns, whose B fragments come from the same 16 channels of each
+// tap's plane.  MAC iteration `it` covers reduction rows q0 + d, d < TK:
+// the A tile holds dY[q][k0 .. k0+TM) per row, plane t holds X at pixel q
+// shifted by filter tap tap0 + t, channels [k0, k0+TM); every row of either
+// is one contiguous run of TM * 2 bytes (a whole 128-byte line for TM =
+// 64).  Each thread moves the same (row, chunk) of the A tile and of every
+// plane: it splits its row's reduction index once per iteration, and the
+// taps only add wave-uniform offsets.  Padding, taps past R*S, rows past the
+// reduction and channels past C come back as zero (out-of-range buffer
+// offsets).
+template <class Cfg>
+struct WgradBdLoader {
+  static constexpr bool kDma = true, kGrouped = false, kTrans = true;
+  static_assert(Cfg::ESZ == 2 && Cfg::BDG > 0, "block-diagonal tile");
+  static constexpr int PA = Cfg::TM * 2, PB = PA;  // bytes per q row
+  static constexpr int TAPS = Cfg::BD_TAPS, PLANE = Cfg::BD_PLANE;
+  static constexpr int CPR = PA / 16;
+  static_assert(Cfg::THREADS == Cfg::TK * CPR, "one 16-byte chunk per thread, tile and plane");
+  static constexpr int UA = 1, UB = TAPS;  // DMA instructions per thread and iteration
+
+  __amdgpu_buffer_rsrc_t rx, rdy;
+  int wave, row;
+  uint32_t coff;          // the thread's channel bytes
+  bool chan_ok;           // its chunk lies inside C
+  uint32_t lwo, lho;      // digits (radix Wo, then Ho) of its row
+  uint32_t loff;          // X offset of those digits (image folded in)
+  int tr[TAPS], ts[TAPS];  // r - ph and s - pw of each plane's tap (past R*S: never in range)
+  uint32_t toff[TAPS];    // ((r - ph) * W + (s - pw)) * C * 2
+  uint32_t k2, hwc2, shwc2, swc2, cw1, cw2, howo;
+  int kred, H, W, Ho, Wo, sh, sw;
+  FastDiv div_howo, div_wo;
+
+  SKG_DEV void init(const WgradParams& w, int k0, int tap0, int tid) {
+    rx = make_rsrc(w.X, w.x_bytes);
+    rdy = make_rsrc(w.dY, w.dy_bytes);
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    k2 = (uint32_t)w.K * 2;
+    const uint32_t c2 = (uint32_t)w.C * 2;
+    kred = w.kred;
+    H = w.H;
+    W = w.W;
+    Ho = w.Ho;
+    Wo = w.Wo;
+    sh = w.sh;
+    sw = w.sw;
+    howo = (uint32_t)(w.Ho * w.Wo);
+    hwc2 = (uint32_t)(w.H * w.W) * c2;
+    shwc2 = (uint32_t)(w.sh * w.W) * c2;
+    swc2 = (uint32_t)w.sw * c2;
+    cw1 = shwc2 - (uint32_t)w.Wo * swc2;  // wo wrapped: wo - Wo, ho + 1
+    cw2 = hwc2 - (uint32_t)w.Ho * shwc2;  // ho wrapped: ho - Ho, img + 1
+    div_howo = w.div_howo;
+    div_wo = w.div_wo;
+    row = tid / CPR;
+    const int chunk = (tid % CPR) ^ tr_swz<PA, Cfg::MN>(row);
+    const int ch = k0 + chunk * 8;
+    chan_ok = ch < w.C;  // C == K: 16 channels in and out per group
+    coff = (uint32_t)ch * 2;
+    const uint32_t t = fdiv((uint32_t)row, div_wo);
+    const uint32_t img = fdiv(t, w.div_ho);
+    lwo = (uint32_t)row - t * (uint32_t)Wo;
+    lho = t - img * (uint32_t)Ho;
+    loff = img * hwc2 + lho * shwc2 + lwo * swc2;
+    const int rs = w.R * w.S;
+#pragma unroll
+    for (int j = 0; j < TAPS; ++j) {
+      const int tap = tap0 + j;
+      const int r = (int)fdiv((uint32_t)tap, w.div_s);
+      const int sx = tap - r * w.S;
+      tr[j] = tap < rs ? r - w.ph : (1 << 30);
+      ts[j] = sx - w.pw;
+      toff[j] = (uint32_t)(r - w.ph) * ((uint32_t)w.W * c2) + (uint32_t)(sx - w.pw) * c2;
+    }
+  }
+
+  // The scalar split of iteration it's first row, and the thread's row.
+  struct QBase {
+    uint32_t wo, ho, pix;  // the thread's output position and its X offset (no tap)
+    uint32_t aoff;         // dY offset of the thread's row and chunk
+    bool ok;               // row inside the reduction and chunk inside C
+  };
+  SKG_DEV QBase qbase(int it) const {
+    const uint32_t q0 = __builtin_amdgcn_readfirstlane((uint32_t)it * Cfg::TK);
+    const uint32_t img = fdiv(q0, div_howo);
+    const uint32_t rem = q0 - img * howo;
+    const uint32_t ho0 = fdiv(rem, div_wo);
+    const uint32_t wo0 = rem - ho0 * (uint32_t)Wo;
+    const uint32_t base = img * hwc2 + ho0 * shwc2 + wo0 * swc2;
+    QBase b;
+    uint32_t wo = wo0 + lwo;
+    const bool c1 = wo >= (uint32_t)Wo;
+    wo = c1 ? wo - (uint32_t)Wo : wo;
+    uint32_t ho = ho0 + lho + (c1 ? 1u : 0u);
+    const bool c2 = ho >= (uint32_t)Ho;
+    ho = c2 ? ho - (uint32_t)Ho : ho;
+    b.wo = wo;
+    b.ho = ho;
+    b.pix = base + loff + (c1 ? cw1 : 0u) + (c2 ? cw2 : 0u) + coff;
+    b.aoff = (q0 + (uint32_t)row) * k2 + coff;
+    b.ok = chan_ok & ((int)q0 + row < kred);
+    return b;
+  }
+
+  SKG_DEV uint32_t a_off(const QBase& b) const { return b.ok ? b.aoff : kOOB; }
+  SKG_DEV uint32_t b_off(const QBase& b, int j) const {
+    const int hi = __mul24((int)b.ho, sh) + tr[j];
+    const int wi = __mul24((int)b.wo, sw) + ts[j];
+    const bool ok = b.ok & ((uint32_t)hi < (uint32_t)H) & ((uint32_t)wi < (uint32_t)W);
+    return ok ? b.pix + toff[j] : kOOB;
+  }
+
+  // MAC iteration `it` into the ring entry at `e`: the A tile, then the
+  // tap planes.
+  SKG_DEV void issue_iter(int it, SKG_LDS char* e) const {
+    const QBase b = qbase(it);
+    dma16(rdy, lds_addr(e + wave * 1024), a_off(b));
+#pragma unroll
+    for (int j = 0; j < TAPS; ++j) dma16(rx, lds_addr(e + (1 + j) * PLANE + wave * 1024), b_off(b, j));
+  }
+};
+
+template <class Cfg>
+struct WgradBdProblem {
+  static constexpr int kScaleInc = 1;  // no scales
+  typedef WgradParams Params;
+  typedef WgradBdLoader<Cfg> Loader;
+
+  SKG_DEV static void setup(const Params& w, const KPlan& p, int tile, Loader& ld, OutTile& out,
+                               int tid) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    ld.init(w, tm * Cfg::TM, tn * Cfg::BD_TAPS, tid);
+    out = out_tile(w, p, tile);
+  }
+  SKG_DEV static OutTile out_tile(const Params& w, const KPlan& p, int tile) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int k0 = tm * Cfg::TM, n0 = tn * Cfg::TN;
+    OutTile o;
+    // dW is K x (R*S*16) row-major; the tile's rows are output channels
+    // k0.., its columns (tap, channel) entries n0.. of each row's own group.
+    o.base = (char*)(w.dW + (size_t)k0 * w.gemm_n + n0);
+    o.sa = nullptr;
+    o.sb = nullptr;
+    o.ld = w.gemm_n;
+    o.rows = w.K - k0;
+    o.cols = w.gemm_n - n0;
+    return o;
+  }
+  SKG_DEV static int dtype_c(const Params&) { return DT_F32; }
+};
+
+// ---------------------------------------------------------------------------
 // Fix-up families: each kernel instance carries the code of one, so the
 // epilogue of the other does not take part in its register allocation.
 //   FIX_HANDOFF: linear and tree (partials handed on through flags);
@@ -844,6 +1016,7 @@ struct Engine {
   // One CTA per CU: the burst schedule spreads its refills among the MFMAs
   // (grp_iter_burst).
   static constexpr bool kDefer = Cfg::MIN_CTAS == 1;
+  static constexpr bool kBd = Cfg::BDG > 0;  // block-diagonal grouped wgrad tile
   uint32_t msa[Cfg::FM], msb[Cfg::FN], nsa[Cfg::FM], nsb[Cfg::FN];
 
   SKG_DEV Engine(const Params& prm_, const KPlan& p_, const Scratch& s_, SKG_LDS char* lds_)
@@ -954,7 +1127,9 @@ struct Engine {
 
   // MAC iterations [k0, k1) of one tile into acc.
   SKG_DEV void mainloop(Loader& ld, int k0, int k1) {
-    if constexpr (Loader::kGrouped)
+    if constexpr (kBd)
+      mainloop_bd(ld, k0, k1);
+    else if constexpr (Loader::kGrouped)
       mainloop_grp(ld, k0, k1);
     else if constexpr (Loader::kDma)
       mainloop_dma(ld, k0, k1);
@@ -1149,7 +1324,14 @@ struct Engine {
   }
 
   SKG_DEV void tr_init() {
-    if constexpr (Loader::kTrans) {
+    if constexpr (kBd) {
+      // Wave wm's group: its 16 output channels in the A tile, its 16 input
+      // channels in every tap plane (plane g follows the A tile).
+#pragma unroll
+      for (int f = 0; f < Cfg::FM; ++f) tro_a[f] = tr_offset<Loader::PA>(wm * Cfg::WTM + f * Cfg::MN);
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g) tro_b[g] = g * Loader::PLANE + tr_offset<Loader::PB>(wm * Cfg::WTM);
+    } else if constexpr (Loader::kTrans) {
 #pragma unroll
       for (int f = 0; f < Cfg::FM; ++f) tro_a[f] = tr_offset<Loader::PA>(wm * Cfg::WTM + f * Cfg::MN);
 #pragma unroll
@@ -1445,6 +1627,58 @@ struct Engine {
         grp_iter_burst<true, false>(fa, fb, ld, I - 1, G);
       }
     }
+    __syncthreads();  // every wave is done with the ring before LDS is reused
+  }
+
+  // Block-diagonal pipeline: a ring of BD_D iterations, iteration i in
+  // entry i % BD_D (the A tile, then the tap planes).  Before iteration i a
+  // wave waits for its own loads of i and meets the other waves at the
+  // barrier, after which iteration i is complete in LDS and nobody reads
+  // iteration i-1's entry any more; it refills that entry with iteration
+  // i-1+BD_D, reads one A fragment (its group's output channels) and one B
+  // fragment per tap (its group's input channels in that plane), and runs
+  // one MFMA per tap.  Iterations past the segment are never issued.
+  SKG_DEV SKG_LDS char* bd_entry(int i) const { return lds + (i % Cfg::BD_D) * Cfg::BD_ITER; }
+
+  // Wait until at most n iterations younger than the awaited one are in
+  // flight.
+  SKG_DEV static void wait_iters(int n) {
+    constexpr int L = Loader::UA + Loader::UB, D = Cfg::BD_D;
+    static_assert(D <= 6 && 5 * L < 64, "wait table");
+    switch (n <= 0 ? 0 : n < D - 1 ? n : D - 1) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<L>(); break;
+      case 2: wait_vm<2 * L>(); break;
+      case 3: wait_vm<3 * L>(); break;
+      case 4: wait_vm<4 * L>(); break;
+      default: wait_vm<5 * L>(); break;
+    }
+  }
+
+  SKG_DEV void mainloop_bd(const Loader& ld, int k0, int k1) {
+    constexpr int D = Cfg::BD_D;
+    __builtin_amdgcn_s_waitcnt(0);  // see mainloop_dma
+    zero_acc();
+    tr_init();
+    const int I = k1 - k0;  // >= 1
+    gk0 = k0;
+    gL = I;
+    grot = (I - k0 % I) % I;
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < I) ld.issue_iter(iter(j), bd_entry(j));
+    for (int i = 0; i < I; ++i) {
+      // Issued so far: iterations up to D-1 (i <= 1) or i-2+D.
+      wait_iters(i == 0 ? min(I - 1, D - 1) : min(I - 1 - i, D - 2));
+      lds_barrier();
+      if (i >= 1 && i - 1 + D < I) ld.issue_iter(iter(i - 1 + D), bd_entry(i - 1));
+      const SKG_LDS char* e = bd_entry(i);
+      FragA fa;
+      FragB fb;
+      load_frags_tr(fa, fb, tr_bases(e, e + Loader::PLANE), 0);
+      mma(fa, fb, 0);
+    }
+    wait_vm<0>();
     __syncthreads();  // every wave is done with the ring before LDS is reused
   }
 
@@ -1809,7 +2043,60 @@ struct Engine {
     }
   }
 
+  // Copy-out straight from the accumulators (block-diagonal tiles, whose
+  // 144-column rows do not fit the staged copy-out's thread mapping): lane
+  // l of a fragment holds four consecutive columns of one row.
+  SKG_DEV void write_direct(const OutTile& o, const Fix& fx, float* wsp) const {
+    const int dt = Prob::dtype_c(prm);
+#pragma unroll
+    for (int f = 0; f < Cfg::FM; ++f) {
+      const int row = row_of(f);
+      if (row >= o.rows) continue;
+      const float sa = o.sa ? o.sa[row * Prob::kScaleInc] : 1.f;
+#pragma unroll
+      for (int g = 0; g < Cfg::FN; ++g)
+#pragma unroll
+        for (int q = 0; q < Cfg::NACC / 4; ++q) {
+          const int col = col_of(g, q);
+          const f32x4 v = {acc[f][g][4 * q], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                           acc[f][g][4 * q + 3]};
+          if (FIX == FIX_ATOMIC && fx.how == OUT_WORKSPACE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(wsp + row * Cfg::TN + col + e, v[e]);
+            continue;
+          }
+          const size_t idx = (size_t)row * o.ld + col;
+          if (fx.how == OUT_STORE && !o.sa && !o.sb && dt == DT_F32 && col + 4 <= o.cols &&
+              ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
+            __builtin_nontemporal_store(v, (f32x4*)((float*)o.base + idx));
+            continue;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= o.cols) break;
+            const float w = (v[e] * sa) * (o.sb ? o.sb[(col + e) * Prob::kScaleInc] : 1.f);
+            if (FIX == FIX_ATOMIC && fx.how == OUT_ATOMIC)
+              unsafeAtomicAdd((float*)o.base + idx + e, w);
+            else if (dt == DT_F32)
+              ((float*)o.base)[idx + e] = w;
+            else if (dt == DT_F16)
+              ((uint16_t*)o.base)[idx + e] = to_f16_bits(w);
+            else
+              ((uint16_t*)o.base)[idx + e] = to_bf16_bits(w);
+          }
+        }
+    }
+  }
+
   SKG_DEV void write_out(const OutTile& o, const Fix& fx, float* wsp) {
+    if constexpr (kBd) {
+      write_direct(o, fx, wsp);
+    } else {
+      write_staged(o, fx, wsp);
+    }
+  }
+
+  SKG_DEV void write_staged(const OutTile& o, const Fix& fx, float* wsp) {
     static_assert(Cfg::TN % VC == 0 && Cfg::THREADS % CPRO == 0 && 64 % CPRO == 0 &&
                       (Cfg::WTM % RSTEP == 0 || RSTEP % Cfg::WTM == 0),
                   "copy-out mapping");
@@ -2045,9 +2332,10 @@ struct Engine {
 template <class Cfg, class Prob, int FIX>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_CTAS) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
-  constexpr int kLds = Prob::Loader::kGrouped ? Cfg::LDS_GRP
-                       : Prob::Loader::kDma   ? Cfg::LDS_DMA
-                                              : Cfg::LDS;
+  constexpr int kLds = Cfg::BDG > 0             ? Cfg::LDS_BD
+                       : Prob::Loader::kGrouped ? Cfg::LDS_GRP
+                       : Prob::Loader::kDma     ? Cfg::LDS_DMA
+                                                : Cfg::LDS;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   Engine<Cfg, Prob, FIX> e(prm, p, s, (SKG_LDS char*)lds);
   e.run();

@@ -219,9 +219,13 @@ WORKLOADS = {
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
                      (1, 1), (1, 1), 1, "f16", "uniform", "256x256x64",
                      ("persistent", "dp_sk"), ("tree", "linear", "atomic", "workspace"), 252),
+    # 16 channels per group: the block-diagonal tile (four whole groups per
+    # 64-row tile, whole 128-byte lines) over 224 CTAs, i.e. 28 whole slices
+    # of 14 iterations per tile, with the reduce-scatter fix-up; the
+    # per-group 32x64x64 tile and the linear fix-up are reported beside it.
     4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
-                     (2, 2), (1, 1), 32, "bf16", "uniform", "32x64x64", ("dp_sk",), ("linear",),
-                     512),
+                     (2, 2), (1, 1), 32, "bf16", "uniform", "64x144x32", ("dp_sk",), ("scatter",),
+                     224),
     5: GemmWorkload(5, "gemm_e4m3_8192x8192x8192_rowcol_scales", 8192, 8192, 8192, "e4m3",
                     "bf16", "normal", "256x256x128", ("persistent",), ("workspace",), 256,
                     scales=True),
@@ -253,8 +257,13 @@ NEXT_WORKLOADS = {
 }
 
 # Further launches of a workload reported beside its own: the dense wgrad
-# layer with the reduce-scatter fix-up (not one of the page's four).
-EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "scatter", 252)]}
+# layer with the reduce-scatter fix-up (not one of the page's four); the
+# grouped layer with the linear and tree fix-ups on the block-diagonal tile
+# and with the per-group tile (partial 32-row M tiles, groups folded into
+# GEMM-M one per tile).
+EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "scatter", 252)],
+                  4: [("64x144x32", "dp_sk", "tree", 224), ("64x144x32", "dp_sk", "linear", 128),
+                      ("32x64x64", "dp_sk", "linear", 512)]}
 
 # Earlier name of the first four of them.
 LAYER_WORKLOADS = {i: w for i, w in NEXT_WORKLOADS.items() if i in (6, 7, 8, 9)}

@@ -204,7 +204,11 @@ enum skg_tile {
   SKG_TILE_128x128x64 = 4,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_256x128x64 = 5,   /* f16/bf16 GEMM and wgrad, 4 waves */
   SKG_TILE_128x128x128 = 6,  /* fp8 GEMM (also with MX block scales), 4 waves */
-  SKG_TILE_COUNT = 7
+  SKG_TILE_64x144x32 = 7,    /* f16/bf16 grouped wgrad, block-diagonal: four whole
+                                groups of 16 input and 16 output channels per
+                                tile (GEMM-M = 64 output channels, GEMM-N = 9
+                                filter taps x 16 channels), 4 waves */
+  SKG_TILE_COUNT = 8
 };
 
 enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1, SKG_OP_FWD = 2, SKG_OP_DGRAD = 3 };
@@ -215,6 +219,9 @@ typedef struct skg_tile_info {
   int32_t gemm_dtypes;     /* bit mask of 1 << skg_dtype accepted for GEMM A/B */
   int32_t wgrad_dtypes;    /* bit mask accepted for wgrad X/dY (0: no wgrad) */
   int32_t conv_dtypes;     /* bit mask accepted for forward conv and dgrad (0: none) */
+  int32_t group_block;     /* block-diagonal wgrad tile: whole groups per tile
+                              (each of 16 input and 16 output channels); 0:
+                              dense tile, counted per group */
 } skg_tile_info_t;
 
 /* GEMM problem.  A is M x K row-major with leading dimension lda (elements),
@@ -255,7 +262,14 @@ typedef struct skg_gemm_args {
  * filter gradient, fp32, K x R x S x (C/groups) row-major.  Group g maps input
  * channels [g*C/groups, (g+1)*C/groups) to output channels
  * [g*K/groups, (g+1)*K/groups).  C/groups must be a multiple of 8 and
- * K/groups a multiple of 8; X, dY, dW 16-byte aligned. */
+ * K/groups a multiple of 8; X, dY, dW 16-byte aligned.
+ * Groups fold into GEMM-M (PR #13151, the wgrad port commit: GEMM-M = K).
+ * Dense tiles are counted per group (groups * ceil(Kpg/TM) M tiles, so a
+ * tile never spans two groups).  The block-diagonal tile SKG_TILE_64x144x32
+ * needs C/groups == K/groups == 16; it holds four consecutive groups
+ * (ceil(groups/4) M tiles, the last one possibly with fewer groups), and
+ * each row's 144 columns are its own group's (tap, channel) entries, i.e.
+ * ceil(R*S/9) N tiles of nine taps. */
 typedef struct skg_wgrad_args {
   int32_t n, h, w, c, k, r, s;
   int32_t stride_h, stride_w, pad_h, pad_w, groups;

@@ -90,6 +90,24 @@ def test_wgrad_repeat(index, mode, reduction):
     repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)
 
 
+@pytest.mark.parametrize("reduction", ["linear", "tree"])
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent"])
+def test_wgrad_per_group_tile_repeat(mode, reduction):
+    # The grouped layer on the per-group 32x64x64 tile (one partial 32-row M
+    # tile per group): 96 tiles of 196 iterations over 512 CTAs.
+    wl = synth.WORKLOADS[4]
+    inp = wl.inputs()
+    dx, ddy = to_dev(inp["x"], wl.dtype), to_dev(inp["dy"], wl.dtype)
+    dw = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device="cuda")
+    kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
+              pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile="32x64x64", mode=mode,
+              reduction=reduction, ctas=512)
+    plan = skg.plan_wgrad(**kw)
+    assert plan["sk_ctas"] == 512 and plan["max_contrib"] >= 2
+    ws = skg.workspace_for(plan, "cuda")
+    repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)
+
+
 @pytest.mark.parametrize("index,tile", [(3, "256x128x64"), (3, "256x256x64"), (4, "32x64x64")])
 def test_wgrad_scatter_repeat(index, tile):
     # Split-K over the default pool with the reduce-scatter fix-up, k-major

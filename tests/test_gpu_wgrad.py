@@ -205,3 +205,82 @@ def test_block_sk_order_integer_exact(name, tile):
                 Y, plan = run(x, dy, shape, "bf16", tile, mode, red, ctas, sk_order="block")
                 assert plan["sk_order"] == skg.SK_ORDERS["block"]
                 assert np.array_equal(Y, R), "%s %s %s %s block order" % (name, tile, mode, red)
+
+
+# Block-diagonal grouped tile (16 input and 16 output channels per group,
+# four groups per 64-row tile; nine filter taps per 144-column tile).
+BD_TILE = "64x144x32"
+BD_SHAPES = {
+    # 2 M tiles, 32 iterations each (the ring wraps), stride 1
+    "bd_two_tiles": (4, 16, 16, 128, 128, 3, 3, (1, 1), (1, 1), 8),
+    # 4 + 2 groups (ragged last M tile), reduction 243 = 7 iterations + a tail
+    "bd_ragged": (3, 9, 9, 96, 96, 3, 3, (1, 1), (1, 1), 6),
+    # stride 2 with padding, like the workload's layer
+    "bd_strided": (8, 14, 14, 64, 64, 3, 3, (2, 2), (1, 1), 4),
+    # one group, uneven padding
+    "bd_one_group": (3, 7, 5, 16, 16, 3, 3, (1, 1), (0, 1), 1),
+    # 1x1: one tap used, eight taps past R*S
+    "bd_1x1": (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
+    # 5x5: 25 taps in three N tiles (the last holds 7), strides 2 x 1
+    "bd_5x5": (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+}
+
+
+@pytest.mark.parametrize("name", list(BD_SHAPES))
+def test_block_diagonal_integer_exact_all_modes_and_fixups(name):
+    shape = BD_SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 131)
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            for ctas in (3, 7, 16):
+                Y, plan = run(x, dy, shape, "bf16", BD_TILE, mode, red, ctas)
+                assert np.array_equal(Y, R), "%s %s %s ctas=%d not bit-exact" % (name, mode, red,
+                                                                                 ctas)
+                if mode == "dp":
+                    break
+
+
+@pytest.mark.parametrize("name", list(BD_SHAPES))
+def test_block_diagonal_random(name):
+    shape = BD_SHAPES[name]
+    for fmt in ("f16", "bf16"):
+        x, dy, R = inputs(shape, fmt, False, 137)
+        for mode, red, ctas in [("dp", "linear", 1), ("dp_sk", "tree", 5),
+                                ("persistent", "linear", 11), ("dp_sk", "atomic", 6),
+                                ("persistent", "workspace", 9)]:
+            Y, plan = run(x, dy, shape, fmt, BD_TILE, mode, red, ctas)
+            assert_close(Y, R, fmt, "%s %s %s %s" % (name, fmt, mode, red))
+
+
+@pytest.mark.parametrize("name", ["bd_two_tiles", "bd_ragged", "bd_5x5"])
+def test_block_diagonal_split_k_scatter_and_orders(name):
+    shape = BD_SHAPES[name]
+    x, dy, R = inputs(shape, "bf16", True, 139)
+    for mode, red, ctas, order in [("splitk", "scatter", 2, "kmajor"),
+                                   ("splitk", "scatter", 4, "auto"),
+                                   ("splitk", "tree", 5, "xcd"),
+                                   ("splitk", "workspace", 2, "block"),
+                                   ("dp_sk", "linear", 9, "block"),
+                                   ("persistent", "tree", 13, "xcd"),
+                                   ("auto", "auto", -1, "auto")]:
+        Y, plan = run(x, dy, shape, "bf16", BD_TILE, mode, red, ctas, sk_order=order)
+        assert np.array_equal(Y, R), "%s %s %s %d %s not bit-exact" % (name, mode, red, ctas,
+                                                                       order)
+
+
+def test_block_diagonal_full_layer():
+    # The grouped 28x28 layer (N=64, 32 groups, stride 2) on the
+    # block-diagonal tile, element by element against the oracle, in the
+    # hand-off fix-ups at the full pool and with split-K scatter.
+    wl = synth.WORKLOADS[4]
+    inp = wl.inputs()
+    shape = (wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s, wl.stride, wl.pad, wl.groups)
+    R = oracle_wgrad(wl.dtype, inp["x"], inp["dy"], wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s,
+                     wl.stride[0], wl.stride[1], wl.pad[0], wl.pad[1], wl.groups).reshape(wl.k, -1)
+    for mode, red, ctas in [("dp_sk", "linear", 256), ("persistent", "tree", 256),
+                            ("dp_sk", "atomic", 256), ("splitk", "scatter", 28)]:
+        Y, plan = run(inp["x"], inp["dy"], shape, wl.dtype, BD_TILE, mode, red, ctas)
+        assert (plan["tiles_m"], plan["tiles_n"]) == (8, 1)
+        assert_close(Y, R, wl.dtype, "%s %s %s %s" % (wl.name, BD_TILE, mode, red))

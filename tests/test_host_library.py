@@ -48,6 +48,7 @@ def test_tile_table():
         info = skg.skg_tile_info(tid)
         assert (info.tm, info.tn, info.tk) == TILES[name]
         assert info.n_waves == 4
+        assert info.group_block == (4 if name == "64x144x32" else 0)
     with pytest.raises(skg.SkgError) as ei:
         skg.skg_tile_info(99)
     assert ei.value.status == -2
@@ -139,6 +140,55 @@ def test_wgrad_plan_equals_oracle(tile):
                     tiles = P.wgrad_tiles(n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g,
                                           tm, tn, tk)
                     same_plan(cp, P.plan(*tiles, tm, tn, 4, mode, red, ctas))
+
+
+# Grouped shapes with 16 input and 16 output channels per group: the
+# workload's layer, a ragged last M tile (6 groups: 4 + 2), one group, 1x1
+# and 5x5 filters (1 and 3 N tiles of nine taps), stride 1 and 2.
+BD_SHAPES = [
+    (64, 28, 28, 512, 512, 3, 3, (2, 2), (1, 1), 32),
+    (2, 9, 9, 96, 96, 3, 3, (1, 1), (1, 1), 6),
+    (3, 7, 5, 16, 16, 3, 3, (1, 1), (0, 1), 1),
+    (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
+    (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+]
+
+
+def test_block_diagonal_wgrad_plan_equals_oracle():
+    tm, tn, tk = TILES["64x144x32"]
+    for (n, h, w, c, k, r, s, st, pd, g) in BD_SHAPES:
+        for mode in ("dp", "dp_sk", "persistent", "splitk"):
+            for red in ("linear", "tree", "atomic", "workspace", "scatter"):
+                for ctas in (3, 7, 8, 16, 224, 256):
+                    tiles = P.wgrad_tiles(n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g,
+                                          tm, tn, tk, group_block=4)
+                    T = tiles[0] * tiles[1]
+                    rm, rr, rc, S = P.resolve_launch(T, tiles[2], mode, red, ctas)
+                    try:
+                        o = P.plan(*tiles, tm, tn, 4, rm, rr, rc)
+                    except ValueError:
+                        rejected(skg.plan_wgrad, n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st,
+                                 pad=pd, groups=g, dtype="bf16", tile="64x144x32", mode=mode,
+                                 reduction=red, ctas=ctas)
+                        continue
+                    cp = skg.plan_wgrad(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st, pad=pd,
+                                        groups=g, dtype="bf16", tile="64x144x32", mode=mode,
+                                        reduction=red, ctas=ctas)
+                    same_plan(cp, o)
+    # the workload's layer: 8 tiles of 392 iterations
+    cp = skg.plan_wgrad(n=64, h=28, w=28, c=512, k=512, r=3, s=3, stride=(2, 2), pad=(1, 1),
+                        groups=32, dtype="bf16", tile="64x144x32", mode="dp_sk",
+                        reduction="linear", ctas=256)
+    assert (cp["tiles_m"], cp["tiles_n"], cp["iters_per_tile"]) == (8, 1, 392)
+
+
+def test_block_diagonal_wgrad_needs_16_channels_per_group():
+    kw = dict(n=2, h=8, w=8, r=3, s=3, stride=(1, 1), pad=(1, 1), dtype="f16",
+              tile="64x144x32", mode="dp_sk", reduction="tree", ctas=4)
+    for c, k, g in ((64, 64, 2), (64, 128, 4), (128, 64, 4), (256, 256, 8)):
+        msg = rejected(skg.plan_wgrad, c=c, k=k, groups=g, **kw)
+        assert "16 input and 16 output channels" in msg
+    assert skg.plan_wgrad(c=64, k=64, groups=4, **kw)["tiles_m"] == 1
 
 
 def rejected(fn, **kw):
