@@ -17,8 +17,8 @@ MODE_DP, MODE_DP_SK, MODE_PERSISTENT, MODE_SPLITK, MODE_AUTO = 0, 1, 2, 3, 4
 RED_LINEAR, RED_TREE, RED_ATOMIC, RED_WORKSPACE, RED_AUTO, RED_SCATTER = 0, 1, 2, 3, 4, 5
 OP_GEMM, OP_WGRAD, OP_FWD, OP_DGRAD = 0, 1, 2, 3
 TILE_128x128x32, TILE_256x256x64, TILE_256x256x128, TILE_32x64x64, TILE_128x128x64, \
-    TILE_256x128x64, TILE_128x128x128, TILE_64x144x32 = range(8)
-TILE_COUNT = 8
+    TILE_256x128x64, TILE_128x128x128, TILE_64x144x32, TILE_128x64x32 = range(9)
+TILE_COUNT = 9
 
 MODES = {"dp": MODE_DP, "dp_sk": MODE_DP_SK, "persistent": MODE_PERSISTENT,
          "splitk": MODE_SPLITK, "auto": MODE_AUTO}
@@ -32,7 +32,8 @@ SK_ORDERS = {"auto": SK_ORDER_AUTO, "block": SK_ORDER_BLOCK, "xcd": SK_ORDER_XCD
 TILES = {"128x128x32": TILE_128x128x32, "256x256x64": TILE_256x256x64,
          "256x256x128": TILE_256x256x128, "32x64x64": TILE_32x64x64,
          "128x128x64": TILE_128x128x64, "256x128x64": TILE_256x128x64,
-         "128x128x128": TILE_128x128x128, "64x144x32": TILE_64x144x32}
+         "128x128x128": TILE_128x128x128, "64x144x32": TILE_64x144x32,
+         "128x64x32": TILE_128x64x32}
 
 
 class skg_tile_info_t(ctypes.Structure):

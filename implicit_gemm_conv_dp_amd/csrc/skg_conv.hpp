@@ -232,4 +232,153 @@ struct ConvProblem {
   SKG_DEV static int dtype_c(const Params& c) { return c.dtype_out; }
 };
 
+// Block-diagonal grouped tile for 16 input and 16 output channels per group
+// (so C == K): the tile's TN = 16 * BDG channels are BDG whole groups, one
+// wave per group, over TM pixels.  A MAC iteration covers TK / 16 filter
+// taps of every group's 16 channels: the A side is one plane per tap, TM
+// pixel rows of the tile's TN channels gathered at that tap (a whole
+// 128-byte line per row for TN = 64), the B side TN filter rows (W for the
+// forward pass, the per-group transposed Wt for dgrad) of TK reduction
+// elements; the filter rows of consecutive groups are consecutive, so B is
+// one dense slab.  Wave w multiplies its group's 32-byte slice of every A
+// row by its group's 16 filter rows.  Two CTAs share a CU (two ring entries
+// each): the loads of a CU are bound by the requests its waves keep in
+// flight, and the short per-tile reduction leaves little to pipeline.
+template <class Cfg, bool DGRAD>
+struct ConvBdLoader {
+  static constexpr bool kDma = true, kGrouped = false, kTrans = false;
+  static_assert(Cfg::ESZ == 2 && Cfg::BDG > 0 && Cfg::TN == 64, "block-diagonal conv tile");
+  static constexpr int PA = Cfg::TN * 2;        // bytes per A row (pixel at one tap)
+  static constexpr int RBB = Cfg::TK * 2;       // bytes per B row and iteration
+  static constexpr int NPL = Cfg::TK / 16;      // taps (A planes) per iteration
+  static constexpr int PLANE = Cfg::TM * PA;
+  static constexpr int B_OFF = NPL * PLANE;
+  static constexpr int ENTRY = B_OFF + Cfg::TN * RBB;
+  static constexpr int D = Cfg::BD_LDS / ENTRY > 6 ? 6 : Cfg::BD_LDS / ENTRY;
+  static_assert(D >= 2 && PA == 128 && (RBB == 64 || RBB == 128), "ring entries");
+  static constexpr int STEP = Cfg::THREADS / (PA / 16);  // A rows per DMA instruction
+  static constexpr int UPL = Cfg::TM / STEP;              // DMA instructions per plane
+  static constexpr int UA = NPL * UPL, UB = Cfg::TN * RBB / (Cfg::THREADS * 16);
+  static_assert(UPL * STEP == Cfg::TM && UB * Cfg::THREADS * 16 == Cfg::TN * RBB && UB >= 1,
+                "DMA mapping");
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int wave;
+  uint32_t cofs;               // A: byte offset of this thread's channels within a pixel
+  bool chan_ok;                // its channels lie inside the activation
+  int pn[UPL];                 // n * act_h, or -1 for a row past GEMM-M
+  int py[UPL], px[UPL];        // forward: ho*sh - ph, wo*sw - pw; dgrad: h + ph, w + pw
+  uint32_t offb[UB], limb[UB]; // B: this thread's chunk, and the bytes left in its row
+  int act_h, act_w, S, RS, sh, sw;
+  uint32_t act_c2;
+  FastDiv div_s, div_sh, div_sw;
+
+  SKG_DEV void init(const ConvParams& c, int m0, int k0, int tid) {
+    ra = make_rsrc(c.act, c.act_bytes);
+    rb = make_rsrc(c.filt, c.filt_bytes);
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    act_h = c.act_h;
+    act_w = c.act_w;
+    S = c.S;
+    RS = c.kred / 16;
+    sh = c.sh;
+    sw = c.sw;
+    act_c2 = (uint32_t)c.act_c * 2;
+    div_s = c.div_s;
+    div_sh = c.div_sh;
+    div_sw = c.div_sw;
+    int row, chunk;
+    lds_slot<PA>(tid, row, chunk);
+    const int ch = k0 + chunk * 8;
+    chan_ok = ch < c.act_c;
+    cofs = (uint32_t)ch * 2;
+    const int pix_w = c.pix_w;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+      const int m = m0 + row + u * STEP;
+      const uint32_t n = fdiv((uint32_t)m, c.div_pix_hw);
+      const int rem = m - (int)n * (int)c.div_pix_hw.d;
+      const int y = (int)fdiv((uint32_t)rem, c.div_pix_w);
+      const int x = rem - y * pix_w;
+      pn[u] = m < c.gm ? (int)n * act_h : -1;
+      py[u] = DGRAD ? y + c.ph : y * c.sh - c.ph;
+      px[u] = DGRAD ? x + c.pw : x * c.sw - c.pw;
+    }
+    const uint32_t rowb = (uint32_t)c.kred * 2;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      int br, bc;
+      lds_slot<RBB>(tid + u * Cfg::THREADS, br, bc);
+      const int frow = k0 + br;
+      offb[u] = (uint32_t)frow * rowb + bc * 16;
+      limb[u] = frow < c.out_c ? rowb - bc * 16 : 0u;
+    }
+  }
+
+  // Activation row u of this thread at filter tap `tap`, or kOOB.
+  SKG_DEV uint32_t a_off(int u, int tap, int r, int s) const {
+    int hi, wi;
+    bool ok = chan_ok & (tap < RS) & (pn[u] >= 0);
+    if constexpr (!DGRAD) {
+      hi = py[u] + r;
+      wi = px[u] + s;
+    } else {
+      const int t = py[u] - r, v = px[u] - s;
+      hi = (int)fdiv((uint32_t)t, div_sh);
+      wi = (int)fdiv((uint32_t)v, div_sw);
+      ok = ok & (t >= 0) & (v >= 0) & (hi * sh == t) & (wi * sw == v);
+    }
+    ok = ok & ((uint32_t)hi < (uint32_t)act_h) & ((uint32_t)wi < (uint32_t)act_w);
+    const uint32_t off = (uint32_t)((pn[u] + hi) * act_w + wi) * act_c2 + cofs;
+    return ok ? off : kOOB;
+  }
+
+  // MAC iteration `it` into the ring entry at `e`: the A planes, then the
+  // B slab.
+  SKG_DEV void issue_iter(int it, SKG_LDS char* e) const {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int tap = it * NPL + j;
+      const int r = (int)fdiv((uint32_t)tap, div_s);
+      const int s = tap - r * S;
+#pragma unroll
+      for (int u = 0; u < UPL; ++u)
+        dma16(ra, lds_addr(e + j * PLANE + u * Cfg::THREADS * 16 + wave * 1024), a_off(u, tap, r, s));
+    }
+    const uint32_t kb = (uint32_t)it * RBB;
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      dma16(rb, lds_addr(e + B_OFF + u * Cfg::THREADS * 16 + wave * 1024),
+            kb < limb[u] ? offb[u] + kb : kOOB);
+  }
+};
+
+template <class Cfg, bool DGRAD>
+struct ConvBdProblem {
+  typedef ConvParams Params;
+  static constexpr int kScaleInc = 1;  // no scales
+  typedef ConvBdLoader<Cfg, DGRAD> Loader;
+
+  SKG_DEV static void setup(const Params& c, const KPlan& p, int tile, Loader& ld, OutTile& out, int tid) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    ld.init(c, tm * Cfg::TM, tn * Cfg::TN, tid);
+    out = out_tile(c, p, tile);
+  }
+  SKG_DEV static OutTile out_tile(const Params& c, const KPlan& p, int tile) {
+    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int m0 = tm * Cfg::TM, k0 = tn * Cfg::TN;
+    const int esz = c.dtype_out == DT_F32 ? 4 : 2;
+    OutTile o;
+    // Pixel rows of out_c channels; the tile's channels start at k0.
+    o.base = c.out + ((size_t)m0 * c.out_c + k0) * esz;
+    o.sa = nullptr;
+    o.sb = nullptr;
+    o.ld = c.out_c;
+    o.rows = c.gm - m0;
+    o.cols = c.out_c - k0;
+    return o;
+  }
+  SKG_DEV static int dtype_c(const Params& c) { return c.dtype_out; }
+};
+
 }  // namespace skg

@@ -32,6 +32,7 @@ const TileDesc kTiles[SKG_TILE_COUNT] = {
     /* 256x128x64  */ {256, 128, 64, 4, M_F16 | M_BF16, M_F16 | M_BF16, M_F16 | M_BF16},
     /* 128x128x128 */ {128, 128, 128, 4, M_F8, 0, 0},
     /* 64x144x32   */ {64, 144, 32, 4, 0, M_F16 | M_BF16, 0, 4},
+    /* 128x64x32   */ {128, 64, 32, 4, 0, 0, M_F16 | M_BF16, 4},
 };
 
 // Offsets inside one buffer are 32-bit on the device (buffer resources).
@@ -281,6 +282,12 @@ GemmShape conv_shape(const skg_conv_args_t* a, const TileDesc& t, bool dgrad) {
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   const int64_t kpg = a->k / a->groups, cpg = a->c / a->groups;
+  if (t.group_block) {
+    // Block-diagonal: group_block whole groups per N tile, the reduction
+    // per group (16 channels at every tap).
+    const int64_t gm = dgrad ? int64_t(a->n) * a->h * a->w : int64_t(a->n) * ho * wo;
+    return {ceil_div(gm, t.tm), ceil_div(a->groups, t.group_block), ceil_div(a->r * a->s * 16, t.tk)};
+  }
   // Groups fold into GEMM-N with the tile count per group.
   if (!dgrad)
     return {ceil_div(int64_t(a->n) * ho * wo, t.tm), int64_t(a->groups) * ceil_div(kpg, t.tn),
@@ -350,7 +357,7 @@ int validate_wgrad(const skg_wgrad_args_t* a) {
   const int64_t cpg = a->c / a->groups, kpg = a->k / a->groups;
   if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
   if (t->group_block && (cpg != 16 || kpg != 16))
-    return unsupported("the block-diagonal wgrad tile needs 16 input and 16 output channels per group");
+    return unsupported("the block-diagonal tile needs 16 input and 16 output channels per group");
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)
@@ -387,7 +394,7 @@ int validate_conv(const skg_conv_args_t* a, bool dgrad) {
   const int64_t cpg = a->c / a->groups, kpg = a->k / a->groups;
   if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
   if (t->group_block && (cpg != 16 || kpg != 16))
-    return unsupported("the block-diagonal wgrad tile needs 16 input and 16 output channels per group");
+    return unsupported("the block-diagonal tile needs 16 input and 16 output channels per group");
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)

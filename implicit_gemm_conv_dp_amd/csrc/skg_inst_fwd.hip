@@ -11,9 +11,15 @@ ConvInst make() {
   typedef ConvProblem<Cfg, false> Prob;
   return {&launch_instance<Cfg, Prob>, &occupancy_instance<Cfg, Prob>};
 }
+template <class Cfg>
+ConvInst make_bd() {
+  typedef ConvBdProblem<Cfg, false> Prob;
+  return {&launch_instance<Cfg, Prob>, &occupancy_instance<Cfg, Prob>};
+}
 template <int DT>
 ConvInst by_tile(int tile_id) {
   switch (tile_id) {
+    case SKG_TILE_128x64x32: return make_bd<TileCfg<DT, 128, 64, 32, 1, 4, 16, 64, false, 4, 2>>();
     case SKG_TILE_256x256x64: return make<TileCfg<DT, 256, 256, 64, 2, 2, 32>>();
     case SKG_TILE_128x128x64: return make<TileCfg<DT, 128, 128, 64, 2, 2, 32>>();
     case SKG_TILE_256x128x64: return make<TileCfg<DT, 256, 128, 64, 2, 2, 32>>();

@@ -88,10 +88,12 @@ struct WgradParams {
 // ---------------------------------------------------------------------------
 // MX_: the operand slots also hold each row's E8M0 block scales of the
 // iteration (4 bytes per row after the row data).
-// BDG_ > 0: block-diagonal grouped wgrad tile holding BDG_ whole groups of
-// 16 channels (WgradBdLoader).
+// BDG_ > 0: block-diagonal grouped tile holding BDG_ whole groups of 16
+// channels, one wave per group: along M for the wgrad (WgradBdLoader),
+// along N for the forward convolution and dgrad (ConvBdLoader); BDC_ of
+// them share a CU (each with its share of the LDS).
 template <int DT_, int TM_, int TN_, int TK_, int WM_, int WN_, int MN_, int RBS_ = 64, bool MX_ = false,
-          int BDG_ = 0>
+          int BDG_ = 0, int BDC_ = 1>
 struct TileCfg {
   static constexpr int DT = DT_, TM = TM_, TN = TN_, TK = TK_, WM = WM_, WN = WN_, MN = MN_;
   static constexpr bool MX = MX_;
@@ -145,25 +147,20 @@ struct TileCfg {
   // CTA per CU); otherwise issue them in one burst after the barrier, which
   // keeps them further ahead (two CTAs per CU hide the burst).
   static constexpr bool SPREAD = TM == 256 && TN == 256 && !MX_;
-  // Block-diagonal tile: a MAC iteration is the A tile (TK rows of the
-  // tile's TM output channels) followed by one plane per filter tap (TK
-  // rows of the same TM input channels at that tap's pixel), BD_ITER bytes;
-  // a ring of BD_D iterations takes the whole LDS.
+  // Block-diagonal tile: its loader lays out one ring entry per MAC
+  // iteration (Loader::ENTRY bytes, Loader::D entries in BD_LDS bytes).
   static constexpr int BDG = BDG_;
-  static constexpr int BD_TAPS = TN / 16;
-  static constexpr int BD_PLANE = TK * TM * 2;
-  static constexpr int BD_ITER = BD_PLANE * (1 + BD_TAPS);
-  static constexpr int BD_D = BDG_ ? 160 * 1024 / BD_ITER : 0;
-  static constexpr int LDS_BD = BD_D * BD_ITER;
+  static constexpr int BD_LDS = 160 * 1024 / BDC_;
   // Resident CTAs per CU the register allocation must allow: tiles of up
-  // to 128x128 keep two (their LDS fits twice), larger ones and the
-  // block-diagonal tile take the CU.
-  static constexpr int MIN_CTAS = BDG_ ? 1 : TM * TN <= 128 * 128 ? 2 : 1;
+  // to 128x128 keep two (their LDS fits twice), larger ones take the CU,
+  // block-diagonal ones BDC_ each.
+  static constexpr int MIN_CTAS = BDG_ ? BDC_ : TM * TN <= 128 * 128 ? 2 : 1;
   static_assert(RB == 64 || RB == 128, "LDS row layout");
   static_assert(FM >= 1 && FN >= 1 && WTM % MN == 0 && WTN % MN == 0, "wave tile");
   static_assert(KSTEPS >= 1 && RB % Op::KB == 0, "k steps");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(BDG_ == 0 || (TM == 16 * BDG_ && MN == 16 && WM == BDG_ && WN == 1 && BD_D >= 2),
+  static_assert(BDG_ == 0 || (MN == 16 && ((TM == 16 * BDG_ && WM == BDG_ && WN == 1) ||
+                                            (TN == 16 * BDG_ && WN == BDG_ && WM == 1))),
                 "block-diagonal tile: one wave per group");
 };
 
@@ -841,7 +838,12 @@ struct WgradBdLoader {
   static constexpr bool kDma = true, kGrouped = false, kTrans = true;
   static_assert(Cfg::ESZ == 2 && Cfg::BDG > 0, "block-diagonal tile");
   static constexpr int PA = Cfg::TM * 2, PB = PA;  // bytes per q row
-  static constexpr int TAPS = Cfg::BD_TAPS, PLANE = Cfg::BD_PLANE;
+  // One MAC iteration: the A tile, then one plane per filter tap, in a
+  // ring of D entries filling the LDS.
+  static constexpr int TAPS = Cfg::TN / 16, PLANE = Cfg::TK * PA;
+  static constexpr int ENTRY = PLANE * (1 + TAPS);
+  static constexpr int D = Cfg::BD_LDS / ENTRY > 6 ? 6 : Cfg::BD_LDS / ENTRY;
+  static_assert(D >= 2, "two ring entries at least");
   static constexpr int CPR = PA / 16;
   static_assert(Cfg::THREADS == Cfg::TK * CPR, "one 16-byte chunk per thread, tile and plane");
   static constexpr int UA = 1, UB = TAPS;  // DMA instructions per thread and iteration
@@ -956,7 +958,7 @@ struct WgradBdProblem {
   SKG_DEV static void setup(const Params& w, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
     const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-    ld.init(w, tm * Cfg::TM, tn * Cfg::BD_TAPS, tid);
+    ld.init(w, tm * Cfg::TM, tn * Loader::TAPS, tid);
     out = out_tile(w, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& w, const KPlan& p, int tile) {
@@ -992,6 +994,16 @@ struct LoaderMx {
 template <class L>
 struct LoaderMx<L, std::void_t<decltype(L::kMx)>> {
   static constexpr bool value = L::kMx;
+};
+
+// Block-diagonal loaders declare their ring: D entries of ENTRY bytes.
+template <class L, class = void>
+struct LoaderRing {
+  static constexpr int bytes = 0;
+};
+template <class L>
+struct LoaderRing<L, std::void_t<decltype(L::ENTRY)>> {
+  static constexpr int bytes = L::D * L::ENTRY;
 };
 
 template <class Cfg, class Prob, int FIX>
@@ -1324,14 +1336,14 @@ struct Engine {
   }
 
   SKG_DEV void tr_init() {
-    if constexpr (kBd) {
+    if constexpr (kBd && Loader::kTrans) {
       // Wave wm's group: its 16 output channels in the A tile, its 16 input
       // channels in every tap plane (plane g follows the A tile).
 #pragma unroll
       for (int f = 0; f < Cfg::FM; ++f) tro_a[f] = tr_offset<Loader::PA>(wm * Cfg::WTM + f * Cfg::MN);
 #pragma unroll
       for (int g = 0; g < Cfg::FN; ++g) tro_b[g] = g * Loader::PLANE + tr_offset<Loader::PB>(wm * Cfg::WTM);
-    } else if constexpr (Loader::kTrans) {
+    } else if constexpr (Loader::kTrans && !kBd) {
 #pragma unroll
       for (int f = 0; f < Cfg::FM; ++f) tro_a[f] = tr_offset<Loader::PA>(wm * Cfg::WTM + f * Cfg::MN);
 #pragma unroll
@@ -1630,20 +1642,18 @@ struct Engine {
     __syncthreads();  // every wave is done with the ring before LDS is reused
   }
 
-  // Block-diagonal pipeline: a ring of BD_D iterations, iteration i in
-  // entry i % BD_D (the A tile, then the tap planes).  Before iteration i a
-  // wave waits for its own loads of i and meets the other waves at the
-  // barrier, after which iteration i is complete in LDS and nobody reads
-  // iteration i-1's entry any more; it refills that entry with iteration
-  // i-1+BD_D, reads one A fragment (its group's output channels) and one B
-  // fragment per tap (its group's input channels in that plane), and runs
-  // one MFMA per tap.  Iterations past the segment are never issued.
-  SKG_DEV SKG_LDS char* bd_entry(int i) const { return lds + (i % Cfg::BD_D) * Cfg::BD_ITER; }
+  // Block-diagonal pipeline: a ring of D iterations, iteration i in entry
+  // i % D.  Before iteration i a wave waits for its own loads of i and
+  // meets the other waves at the barrier, after which iteration i is
+  // complete in LDS and nobody reads iteration i-1's entry any more; it
+  // refills that entry with iteration i-1+D, reads its group's fragments
+  // and runs its MFMAs.  Iterations past the segment are never issued.
+  SKG_DEV SKG_LDS char* bd_entry(int i) const { return lds + (i % Loader::D) * Loader::ENTRY; }
 
   // Wait until at most n iterations younger than the awaited one are in
   // flight.
   SKG_DEV static void wait_iters(int n) {
-    constexpr int L = Loader::UA + Loader::UB, D = Cfg::BD_D;
+    constexpr int L = Loader::UA + Loader::UB, D = Loader::D;
     static_assert(D <= 6 && 5 * L < 64, "wait table");
     switch (n <= 0 ? 0 : n < D - 1 ? n : D - 1) {
       case 0: wait_vm<0>(); break;
@@ -1655,8 +1665,26 @@ struct Engine {
     }
   }
 
+  // Fragments of k-step ks of a forward / dgrad entry (ConvBdLoader): the
+  // A planes hold TM pixel rows of the tile's channels at one tap each, the
+  // B tile TN filter rows of the iteration's reduction.  Lane l's eight
+  // reduction indices 8 * (l / 16) .. +7 of the k-step are tap 2 ks + l / 32,
+  // channels 8 * ((l / 16) & 1) .. +7 of its group: 16 contiguous bytes.
+  SKG_DEV void bd_conv_frags(FragA& fa, FragB& fb, const SKG_LDS char* e, int ks) const {
+    const int lrow = lane % 16, half = (lane / 16) & 1;
+    const SKG_LDS char* pa = e + (2 * ks + lane / 32) * Loader::PLANE;
+#pragma unroll
+    for (int f = 0; f < Cfg::FM; ++f)
+      fa[f] = *(const SKG_LDS Frag*)(pa + lds_off<Loader::PA>(f * Cfg::MN + lrow, 2 * wn + half));
+    const SKG_LDS char* pb = e + Loader::B_OFF;
+#pragma unroll
+    for (int g = 0; g < Cfg::FN; ++g)
+      fb[g] = *(const SKG_LDS Frag*)(pb + lds_off<Loader::RBB>(wn * Cfg::WTN + g * Cfg::MN + lrow,
+                                                                4 * ks + lane / 16));
+  }
+
   SKG_DEV void mainloop_bd(const Loader& ld, int k0, int k1) {
-    constexpr int D = Cfg::BD_D;
+    constexpr int D = Loader::D;
     __builtin_amdgcn_s_waitcnt(0);  // see mainloop_dma
     zero_acc();
     tr_init();
@@ -1675,8 +1703,17 @@ struct Engine {
       const SKG_LDS char* e = bd_entry(i);
       FragA fa;
       FragB fb;
-      load_frags_tr(fa, fb, tr_bases(e, e + Loader::PLANE), 0);
-      mma(fa, fb, 0);
+      if constexpr (Loader::kTrans) {
+        static_assert(Cfg::KSTEPS == 1, "one k-step per wgrad iteration");
+        load_frags_tr(fa, fb, tr_bases(e, e + Loader::PLANE), 0);
+        mma(fa, fb, 0);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
+          bd_conv_frags(fa, fb, e, ks);
+          mma(fa, fb, 0);
+        }
+      }
     }
     wait_vm<0>();
     __syncthreads();  // every wave is done with the ring before LDS is reused
@@ -2066,10 +2103,17 @@ struct Engine {
             continue;
           }
           const size_t idx = (size_t)row * o.ld + col;
-          if (fx.how == OUT_STORE && !o.sa && !o.sb && dt == DT_F32 && col + 4 <= o.cols &&
-              ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
-            __builtin_nontemporal_store(v, (f32x4*)((float*)o.base + idx));
-            continue;
+          if (fx.how == OUT_STORE && !o.sa && !o.sb && col + 4 <= o.cols) {
+            if (dt == DT_F32 && ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
+              __builtin_nontemporal_store(v, (f32x4*)((float*)o.base + idx));
+              continue;
+            }
+            if (dt != DT_F32 && ((uintptr_t)(o.base + idx * 2) & 7) == 0) {
+              const i32x2 h = dt == DT_F16 ? i32x2{(int)pack_f16x2(v[0], v[1]), (int)pack_f16x2(v[2], v[3])}
+                                           : i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+              __builtin_nontemporal_store(h, (i32x2*)((uint16_t*)o.base + idx));
+              continue;
+            }
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -2305,34 +2349,136 @@ struct Engine {
       split = it;
       if (it < end && it % p.ipt != 0) split = min(end, (it / p.ipt + 1) * p.ipt);
     }
-    while (true) {
-      int tile, k0, k1, cta;
-      if (it < split || (it < end && dp_tile >= p.dp_tiles)) {
-        const int t = it / p.ipt;
-        const int seg_end = min(end, (t + 1) * p.ipt);
-        tile = p.dp_tiles + t;
-        k0 = it - t * p.ipt;
-        k1 = seg_end - t * p.ipt;
-        cta = b;
-        it = seg_end;  // strictly increases
-      } else if (dp_tile < p.dp_tiles) {
-        tile = dp_order(dp_tile);
-        k0 = 0;
-        k1 = p.ipt;
-        cta = -1;
-        dp_tile += dp_step;  // strictly increases
-      } else {
-        break;
-      }
-      process(tile, k0, k1, cta);
+    Walk w = {it, end, split, dp_tile, dp_step, b};
+    if constexpr (kStream) {
+      run_stream(w);
+    } else {
+      Seg sg;
+      while (next_segment(w, sg)) process(sg.tile, sg.k0, sg.k1, sg.cta);
     }
+  }
+
+  // The CTA's work list: stream-K iterations [it, split), then its DP tiles,
+  // then the rest of its stream-K range.
+  struct Walk {
+    int it, end, split, dp_tile, dp_step, b;
+  };
+  struct Seg {
+    int tile, k0, k1, cta;
+  };
+  SKG_DEV bool next_segment(Walk& w, Seg& sg) const {
+    if (w.it < w.split || (w.it < w.end && w.dp_tile >= p.dp_tiles)) {
+      const int t = w.it / p.ipt;
+      const int seg_end = min(w.end, (t + 1) * p.ipt);
+      sg.tile = p.dp_tiles + t;
+      sg.k0 = w.it - t * p.ipt;
+      sg.k1 = seg_end - t * p.ipt;
+      sg.cta = w.b;
+      w.it = seg_end;  // strictly increases
+      return true;
+    }
+    if (w.dp_tile < p.dp_tiles) {
+      sg.tile = dp_order(w.dp_tile);
+      sg.k0 = 0;
+      sg.k1 = p.ipt;
+      sg.cta = -1;
+      w.dp_tile += w.dp_step;  // strictly increases
+      return true;
+    }
+    return false;
+  }
+
+  // Hands a finished segment on (fix-up and copy-out; no LDS involved on
+  // the block-diagonal tiles).
+  SKG_DEV void finish(const Seg& sg, const OutTile& o) {
+    const Fix fx = fixup(sg.tile, sg.k0, sg.k1, sg.cta);
+    if constexpr (FIX == FIX_HANDOFF) {
+      if (fx.nfold > 0) fold_regs(fx);
+      if (fx.how == OUT_PUBLISH) {
+        publish_regs(fx.cta);
+        return;
+      }
+      if (fx.how == OUT_SCATTER) {
+        publish_regs(fx.cta);
+        scatter_out(o, sg.tile, fx.cta);
+        return;
+      }
+    }
+    write_out(o, fx, fx.how == OUT_WORKSPACE ? s.ws + (size_t)(sg.tile - p.dp_tiles) * Cfg::TM * Cfg::TN
+                                             : nullptr);
+  }
+
+  // Block-diagonal forward / dgrad tiles have a short reduction (a few MAC
+  // iterations per tile), so the ring runs across the CTA's segments: the
+  // iterations of the current segment and of the next one form one stream,
+  // position q in ring entry q % D, and the refill after each barrier
+  // continues into the next segment while the current one is multiplied,
+  // handed on and written out (none of which touches the LDS).
+  static constexpr bool kStream = kBd && !Loader::kTrans;
+
+  SKG_DEV void run_stream(Walk& w) {
+    constexpr int D = Loader::D;
+    Seg cur, nxt;
+    if (!next_segment(w, cur)) return;
+    Loader lc, ln;
+    OutTile oc, on;
+    Prob::setup(prm, p, cur.tile, lc, oc, tid);
+    bool has_nxt = next_segment(w, nxt);
+    if (has_nxt) Prob::setup(prm, p, nxt.tile, ln, on, tid);
+    int base = 0;    // stream position of cur's first iteration
+    int issued = 0;  // positions [0, issued) are issued
+    // Issues position q (q == issued) if it lies in cur or nxt.
+    auto issue_next = [&]() -> bool {
+      const int ic = cur.k1 - cur.k0;
+      const int q = issued;
+      if (q < base + ic) {
+        lc.issue_iter(cur.k0 + (q - base), bd_entry(q));
+      } else if (has_nxt && q < base + ic + (nxt.k1 - nxt.k0)) {
+        ln.issue_iter(nxt.k0 + (q - base - ic), bd_entry(q));
+      } else {
+        return false;
+      }
+      ++issued;
+      return true;
+    };
+    while (issued < D && issue_next()) {
+    }
+    while (true) {
+      zero_acc();
+      const int ic = cur.k1 - cur.k0;
+      for (int i = 0; i < ic; ++i) {
+        const int q = base + i;
+        wait_iters(issued - 1 - q);
+        lds_barrier();
+        // The entry of position q-1 is free: keep the ring D positions ahead.
+        while (issued < q + D && issue_next()) {
+        }
+        const SKG_LDS char* e = bd_entry(q);
+        FragA fa;
+        FragB fb;
+#pragma unroll
+        for (int ks = 0; ks < Cfg::KSTEPS; ++ks) {
+          bd_conv_frags(fa, fb, e, ks);
+          mma(fa, fb, 0);
+        }
+      }
+      finish(cur, oc);
+      if (!has_nxt) break;
+      base += ic;
+      cur = nxt;
+      lc = ln;
+      oc = on;
+      has_nxt = next_segment(w, nxt);
+      if (has_nxt) Prob::setup(prm, p, nxt.tile, ln, on, tid);
+    }
+    wait_vm<0>();
   }
 };
 
 template <class Cfg, class Prob, int FIX>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::MIN_CTAS) void sk_kernel(typename Prob::Params prm, KPlan p,
                                                             Scratch s) {
-  constexpr int kLds = Cfg::BDG > 0             ? Cfg::LDS_BD
+  constexpr int kLds = Cfg::BDG > 0             ? LoaderRing<typename Prob::Loader>::bytes
                        : Prob::Loader::kGrouped ? Cfg::LDS_GRP
                        : Prob::Loader::kDma     ? Cfg::LDS_DMA
                                                 : Cfg::LDS;

@@ -234,10 +234,12 @@ WORKLOADS = {
 # Workloads of the rows built after the five: the other two convolutions of
 # the two wgrad layers (forward and input gradient), on the same engine, in
 # the launches measured fastest (256x256x64 tiles, persistent, tree fix-up
-# for the dense layer; 128x128x64 tiles for the grouped one, 16 channels per
-# group, where every plan is all-DP), and the fp8 GEMM of workload 5 with OCP
-# MX (E8M0) block scales instead of row/column scales (256x256x128 tiles:
-# 4 ring slots once the scale bytes ride along, refilled among the MFMAs).
+# for the dense layer; the block-diagonal 128x64x32 tile for the grouped
+# one, 16 channels per group, two CTAs per CU, where a tile's reduction is
+# 5 MAC iterations and the data-parallel launch is the fastest), and the
+# fp8 GEMM of workload 5 with OCP MX (E8M0) block scales instead of
+# row/column scales (256x256x128 tiles: 4 ring slots once the scale bytes
+# ride along, refilled among the MFMAs).
 NEXT_WORKLOADS = {
     6: ConvWorkload(6, "fwd_f16_n32_56x56_c256_k256_3x3", "fwd", 32, 56, 56, 256, 256, 3, 3,
                     (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
@@ -246,11 +248,11 @@ NEXT_WORKLOADS = {
                     (1, 1), (1, 1), 1, "f16", "f16", "uniform", "256x256x64", ("persistent",),
                     ("tree",), 256),
     8: ConvWorkload(8, "fwd_bf16_n64_28x28_c512_k512_g32_3x3_s2", "fwd", 64, 28, 28, 512, 512, 3,
-                    3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
-                    ("tree",), 256),
+                    3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x64x32", ("dp",),
+                    ("tree",), 512),
     9: ConvWorkload(9, "dgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", "dgrad", 64, 28, 28, 512, 512,
-                    3, 3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x128x64", ("dp_sk",),
-                    ("tree",), 256),
+                    3, 3, (2, 2), (1, 1), 32, "bf16", "bf16", "uniform", "128x64x32", ("persistent",),
+                    ("tree",), 512),
     10: GemmWorkload(10, "gemm_e4m3_8192x8192x8192_mx_e8m0", 8192, 8192, 8192, "e4m3", "bf16",
                      "normal", "256x256x128", ("persistent",), ("workspace",), 256, scales=True,
                      scale_mode="mx"),
@@ -260,10 +262,13 @@ NEXT_WORKLOADS = {
 # layer with the reduce-scatter fix-up (not one of the page's four); the
 # grouped layer with the linear and tree fix-ups on the block-diagonal tile
 # and with the per-group tile (partial 32-row M tiles, groups folded into
-# GEMM-M one per tile).
+# GEMM-M one per tile); the grouped forward and dgrad on the dense
+# per-group 128x128x64 tile (16 of its 128 columns used).
 EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "scatter", 252)],
                   4: [("64x144x32", "dp_sk", "tree", 224), ("64x144x32", "dp_sk", "linear", 128),
-                      ("32x64x64", "dp_sk", "linear", 512)]}
+                      ("32x64x64", "dp_sk", "linear", 512)],
+                  8: [("128x64x32", "persistent", "tree", 512), ("128x128x64", "dp_sk", "tree", 256)],
+                  9: [("128x128x64", "dp_sk", "tree", 256)]}
 
 # Earlier name of the first four of them.
 LAYER_WORKLOADS = {i: w for i, w in NEXT_WORKLOADS.items() if i in (6, 7, 8, 9)}

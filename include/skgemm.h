@@ -208,7 +208,12 @@ enum skg_tile {
                                 groups of 16 input and 16 output channels per
                                 tile (GEMM-M = 64 output channels, GEMM-N = 9
                                 filter taps x 16 channels), 4 waves */
-  SKG_TILE_COUNT = 8
+  SKG_TILE_128x64x32 = 8,    /* f16/bf16 grouped forward conv and dgrad,
+                                block-diagonal: 128 pixels x four whole groups
+                                of 16 input and 16 output channels (GEMM-N =
+                                64 channels), two filter taps per MAC
+                                iteration, 4 waves */
+  SKG_TILE_COUNT = 9
 };
 
 enum skg_op { SKG_OP_GEMM = 0, SKG_OP_WGRAD = 1, SKG_OP_FWD = 2, SKG_OP_DGRAD = 3 };
@@ -302,7 +307,11 @@ typedef struct skg_wgrad_args {
  * act and filt have type dtype (f16 or bf16); out has dtype_out (f16, bf16,
  * or f32, which the atomic reduction needs).  Channels per group (C/groups
  * and K/groups) must be multiples of 8; act, filt, out 16-byte aligned.  The
- * tiles are those whose skg_tile_info.conv_dtypes is non-zero. */
+ * tiles are those whose skg_tile_info.conv_dtypes is non-zero.  Dense tiles
+ * are counted per group along GEMM-N (groups * ceil(N per group / TN)); the
+ * block-diagonal tile SKG_TILE_128x64x32 needs C/groups == K/groups == 16
+ * and holds four consecutive groups (ceil(groups/4) N tiles), with a
+ * reduction of R*S*16 per group (ceil(R*S/2) MAC iterations of two taps). */
 typedef struct skg_conv_args {
   int32_t n, h, w, c, k, r, s;
   int32_t stride_h, stride_w, pad_h, pad_w, groups;

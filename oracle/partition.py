@@ -241,21 +241,38 @@ def wgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups,
     return (tiles_m, ceil_div(cpg * R * S, tn), ceil_div(N * ho * wo, tk))
 
 
-def fwd_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk):
+def _n_tiles(groups, npg, tn, group_block):
+    """GEMM-N tiles of a convolution whose N index runs over channels folded
+    per group: per group (dense tiles), or group_block whole consecutive
+    groups per tile (block-diagonal tiles, tn = group_block * npg)."""
+    if group_block:
+        if tn != group_block * npg:
+            raise ValueError("a block-diagonal tile holds group_block whole groups")
+        return ceil_div(groups, group_block)
+    return groups * ceil_div(npg, tn)
+
+
+def fwd_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk,
+              group_block=0):
     """Implicit-GEMM view of a forward convolution: GEMM-M = output pixels
     N*Ho*Wo, GEMM-N = output channels folded per group (the tile count is
-    per group, so an N tile never crosses a group), reduction = R*S*Cpg."""
+    per group, so an N tile never crosses a group; or group_block whole
+    groups per block-diagonal tile), reduction = R*S*Cpg per group."""
     ho = (H + 2 * pad_h - R) // stride_h + 1
     wo = (W + 2 * pad_w - S) // stride_w + 1
     kpg, cpg = K // groups, C // groups
-    return (ceil_div(N * ho * wo, tm), groups * ceil_div(kpg, tn), ceil_div(R * S * cpg, tk))
+    return (ceil_div(N * ho * wo, tm), _n_tiles(groups, kpg, tn, group_block),
+            ceil_div(R * S * cpg, tk))
 
 
-def dgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk):
+def dgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk,
+                group_block=0):
     """Implicit-GEMM view of the input gradient: GEMM-M = input pixels
-    N*H*W, GEMM-N = input channels folded per group, reduction = R*S*Kpg."""
+    N*H*W, GEMM-N = input channels folded per group (or group_block whole
+    groups per block-diagonal tile), reduction = R*S*Kpg per group."""
     kpg, cpg = K // groups, C // groups
-    return (ceil_div(N * H * W, tm), groups * ceil_div(cpg, tn), ceil_div(R * S * kpg, tk))
+    return (ceil_div(N * H * W, tm), _n_tiles(groups, cpg, tn, group_block),
+            ceil_div(R * S * kpg, tk))
 
 
 def check_plan(p):

@@ -50,6 +50,37 @@ def test_conv_plans_equal_oracle(op):
     assert n_checked > 500
 
 
+BD_SHAPES = [
+    (64, 28, 28, 512, 512, 3, 3, (2, 2), (1, 1), 32),
+    (2, 9, 9, 96, 96, 3, 3, (1, 1), (1, 1), 6),
+    (3, 7, 5, 16, 16, 3, 3, (1, 1), (0, 1), 1),
+    (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
+    (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+]
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_block_diagonal_conv_plans_equal_oracle(op):
+    tm, tn, tk = TILES["128x64x32"]
+    tiles_of = P.fwd_tiles if op == "fwd" else P.dgrad_tiles
+    for shape in BD_SHAPES:
+        n, h, w, c, k, r, s, st, pd, g = shape
+        t = tiles_of(n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g, tm, tn, tk,
+                     group_block=4)
+        for mode in ("dp", "dp_sk", "persistent"):
+            for red in ("linear", "tree", "atomic", "workspace"):
+                for ctas in (7, 256):
+                    kw = kw_of(shape, "128x64x32", mode, red, ctas)
+                    c_plan = (skg.plan_fwd if op == "fwd" else skg.plan_dgrad)(**kw)
+                    o = P.plan(*t, tm, tn, 4, mode, red, ctas)
+                    aux = 0 if op == "fwd" else -(-k * r * s * (c // g) * 2 // 256) * 256
+                    for f in FIELDS:
+                        v = c_plan[f] - (aux if f == "workspace_bytes" else 0)
+                        assert v == getattr(o, f), (op, shape, mode, red, ctas, f)
+    kw = kw_of((2, 8, 8, 64, 128, 3, 3, (1, 1), (1, 1), 4), "128x64x32", "dp_sk", "tree", 8)
+    assert "16 input and 16 output channels" in rejected(op, **kw)
+
+
 def rejected(op, **kw):
     with pytest.raises(skg.SkgError) as ei:
         (skg.plan_fwd if op == "fwd" else skg.plan_dgrad)(**kw)

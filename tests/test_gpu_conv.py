@@ -141,3 +141,77 @@ def test_layer_full_size(op, layer):
     for mode, red in (("dp_sk", "tree"), ("persistent", "workspace")):
         Y, plan = run(op, act, filt, shape, fmt, "f32", tile, mode, red, 256)
         assert_close(Y, R, fmt, "%s %s %s %s" % (op, layer, mode, red))
+
+
+# Block-diagonal grouped tile (16 input and 16 output channels per group,
+# four groups per 64-channel N tile, two filter taps per MAC iteration).
+BD_TILE = "128x64x32"
+BD_SHAPES = {
+    # 2 N tiles, stride 1, 128-pixel M tiles with a ragged tail (4*10*10)
+    "bd_two_tiles": (4, 10, 10, 128, 128, 3, 3, (1, 1), (1, 1), 8),
+    # 4 + 2 groups (ragged last N tile)
+    "bd_ragged": (3, 9, 9, 96, 96, 3, 3, (1, 1), (1, 1), 6),
+    # stride 2 with padding, like the grouped layer (dgrad: taps that reach
+    # no output pixel)
+    "bd_strided": (4, 14, 14, 64, 64, 3, 3, (2, 2), (1, 1), 4),
+    # one group, uneven padding
+    "bd_one_group": (3, 7, 5, 16, 16, 3, 3, (1, 1), (0, 1), 1),
+    # 1x1: one tap, the second tap of the only iteration past R*S
+    "bd_1x1": (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
+    # 5x5 over 13 iterations, strides 2 x 1
+    "bd_5x5": (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+}
+
+
+@pytest.mark.parametrize("name", list(BD_SHAPES))
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_block_diagonal_integer_exact_all_modes_and_fixups(op, name):
+    shape = BD_SHAPES[name]
+    act, filt, R = inputs(op, shape, "bf16", True, 151)
+    for mode in MODES:
+        for red in REDS:
+            if mode == "dp" and red != "linear":
+                continue
+            for ctas in (3, 7, 16):
+                Y, plan = run(op, act, filt, shape, "bf16", "f32", BD_TILE, mode, red, ctas)
+                assert np.array_equal(Y, R), "%s %s %s %s ctas=%d not bit-exact" % (op, name, mode,
+                                                                                    red, ctas)
+                if mode == "dp":
+                    break
+
+
+@pytest.mark.parametrize("name", list(BD_SHAPES))
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_block_diagonal_random_16bit_outputs(op, name):
+    shape = BD_SHAPES[name]
+    for fmt in ("f16", "bf16"):
+        act, filt, R = inputs(op, shape, fmt, False, 157)
+        for mode, red, ctas, fmt_out in [("dp", "linear", 1, fmt), ("dp_sk", "tree", 5, "bf16"),
+                                         ("persistent", "linear", 11, "f16"),
+                                         ("persistent", "workspace", 9, fmt),
+                                         ("dp_sk", "atomic", 6, "f32")]:
+            Y, plan = run(op, act, filt, shape, fmt, fmt_out, BD_TILE, mode, red, ctas)
+            assert_close(Y, R, fmt, "%s %s %s %s %s -> %s" % (op, name, fmt, mode, red, fmt_out))
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_block_diagonal_grouped_layer_full_size(op):
+    # The grouped 28x28 layer (N=64, 32 groups, stride 2) on the
+    # block-diagonal tile, element by element against the oracle.
+    *shape, fmt = LAYERS["n64_28x28_c512_k512_g32_3x3_s2"]
+    shape = tuple(shape)
+    n, h, w, c, k, r, s, st, pd, g = shape
+    ho, wo = out_size(h, w, r, s, st[0], st[1], pd[0], pd[1])
+    na = n * h * w * c if op == "fwd" else n * ho * wo * k
+    act = synth.to_codes(synth.draw("uniform", na, 91), fmt)
+    filt = synth.to_codes(synth.draw("uniform", k * r * s * (c // g), 92), fmt)
+    if op == "fwd":
+        R = oracle_forward(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    else:
+        R = oracle_dgrad(fmt, act, filt, n, h, w, c, k, r, s, st[0], st[1], pd[0], pd[1], g)
+    R = R.reshape(-1, R.shape[-1])
+    for mode, red, fmt_out in (("persistent", "tree", "bf16"), ("dp_sk", "linear", "f32"),
+                               ("dp", "linear", "bf16")):
+        Y, plan = run(op, act, filt, shape, fmt, fmt_out, BD_TILE, mode, red, 256)
+        assert plan["tiles_n"] == 8
+        assert_close(Y, R, fmt, "%s %s %s %s -> %s" % (op, BD_TILE, mode, red, fmt_out))

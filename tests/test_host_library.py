@@ -48,7 +48,7 @@ def test_tile_table():
         info = skg.skg_tile_info(tid)
         assert (info.tm, info.tn, info.tk) == TILES[name]
         assert info.n_waves == 4
-        assert info.group_block == (4 if name == "64x144x32" else 0)
+        assert info.group_block == (4 if name in ("64x144x32", "128x64x32") else 0)
     with pytest.raises(skg.SkgError) as ei:
         skg.skg_tile_info(99)
     assert ei.value.status == -2

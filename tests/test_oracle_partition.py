@@ -136,6 +136,27 @@ def test_wgrad_tiles_block_diagonal():
         P.wgrad_tiles(4, 8, 8, 64, 64, 3, 3, 1, 1, 1, 1, 4, 32, 144, 32, group_block=4)
 
 
+def test_conv_tiles_block_diagonal():
+    # Forward / dgrad: GEMM-N runs over channels; a block-diagonal tile of
+    # 64 columns holds four whole 16-channel groups.  Brute force over every
+    # output channel, as for the wgrad rows.
+    for groups in (1, 3, 4, 5, 32):
+        C = K = 16 * groups
+        seen = {(ch // 16) // 4 for ch in range(K)}
+        for tiles_of in (P.fwd_tiles, P.dgrad_tiles):
+            t = tiles_of(2, 9, 9, C, K, 3, 3, 2, 2, 1, 1, groups, 128, 64, 32, group_block=4)
+            assert t[1] == len(seen)
+            assert t[2] == 5  # 3*3*16 = 144 reduction elements per group, 32 per iteration
+    # the workload's layers: 64 x 14 x 14 output pixels (forward), 64 x 28 x 28
+    # input pixels (dgrad), 32 groups
+    assert P.fwd_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 128, 64, 32,
+                       group_block=4) == (98, 8, 5)
+    assert P.dgrad_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 128, 64, 32,
+                         group_block=4) == (392, 8, 5)
+    with pytest.raises(ValueError):
+        P.fwd_tiles(2, 9, 9, 64, 64, 3, 3, 1, 1, 1, 1, 4, 128, 128, 32, group_block=4)
+
+
 def test_all_dp_plan_has_safe_divisor():
     p = P.plan(4, 4, 10, 64, 64, 4, "dp_sk", "linear", 16)
     assert p.sk_ctas == 0 and p.iters_per_sk_cta == 1 and p.workspace_bytes == 0
