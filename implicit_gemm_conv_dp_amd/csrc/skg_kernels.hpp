@@ -2349,12 +2349,33 @@ struct Engine {
       split = it;
       if (it < end && it % p.ipt != 0) split = min(end, (it / p.ipt + 1) * p.ipt);
     }
-    Walk w = {it, end, split, dp_tile, dp_step, b};
     if constexpr (kStream) {
+      Walk w = {it, end, split, dp_tile, dp_step, b};
       run_stream(w);
     } else {
-      Seg sg;
-      while (next_segment(w, sg)) process(sg.tile, sg.k0, sg.k1, sg.cta);
+      // (The same walk as next_segment, written out: as a call it changes
+      // the register allocation of the spilling fp8 instances.)
+      while (true) {
+        int tile, k0, k1, cta;
+        if (it < split || (it < end && dp_tile >= p.dp_tiles)) {
+          const int t = it / p.ipt;
+          const int seg_end = min(end, (t + 1) * p.ipt);
+          tile = p.dp_tiles + t;
+          k0 = it - t * p.ipt;
+          k1 = seg_end - t * p.ipt;
+          cta = b;
+          it = seg_end;  // strictly increases
+        } else if (dp_tile < p.dp_tiles) {
+          tile = dp_order(dp_tile);
+          k0 = 0;
+          k1 = p.ipt;
+          cta = -1;
+          dp_tile += dp_step;  // strictly increases
+        } else {
+          break;
+        }
+        process(tile, k0, k1, cta);
+      }
     }
   }
 
