@@ -265,12 +265,44 @@ def fwd_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm,
             ceil_div(R * S * cpg, tk))
 
 
+def dgrad_phases(H, W, R, S, stride_h, stride_w, pad_h, pad_w):
+    """Stride phases of the input gradient.  Input row h receives filter row
+    r only when h + pad_h - r is a multiple of stride_h, i.e. when r and
+    h + pad_h agree modulo stride_h; likewise for columns.  Phase (a, b)
+    holds the pixels with (h + pad_h) mod stride_h == a and (w + pad_w) mod
+    stride_w == b: rows h0, h0 + stride_h, ... (hc of them), columns w0,
+    w0 + stride_w, ... (wc), and its taps are r = a, a + stride_h, ... (rc)
+    times s = b, b + stride_w, ... (sc).  Returns one tuple
+    (a, b, h0, w0, hc, wc, rc, sc) per phase, row phase major."""
+    out = []
+    for a in range(stride_h):
+        h0 = (a - pad_h) % stride_h
+        hc = max(0, ceil_div(H - h0, stride_h))
+        rc = max(0, ceil_div(R - a, stride_h))
+        for b in range(stride_w):
+            w0 = (b - pad_w) % stride_w
+            wc = max(0, ceil_div(W - w0, stride_w))
+            sc = max(0, ceil_div(S - b, stride_w))
+            out.append((a, b, h0, w0, hc, wc, rc, sc))
+    return out
+
+
 def dgrad_tiles(N, H, W, C, K, R, S, stride_h, stride_w, pad_h, pad_w, groups, tm, tn, tk,
                 group_block=0):
     """Implicit-GEMM view of the input gradient: GEMM-M = input pixels
     N*H*W, GEMM-N = input channels folded per group (or group_block whole
-    groups per block-diagonal tile), reduction = R*S*Kpg per group."""
+    groups per block-diagonal tile), reduction = R*S*Kpg per group.
+
+    Block-diagonal tiles order GEMM-M by stride phase (dgrad_phases): a tile
+    holds pixels of one phase only and reduces over that phase's taps, so
+    the M tiles are counted per phase and the iterations per tile are those
+    of the phase with the most taps."""
     kpg, cpg = K // groups, C // groups
+    if group_block:
+        ph = dgrad_phases(H, W, R, S, stride_h, stride_w, pad_h, pad_w)
+        tiles_m = sum(ceil_div(N * hc * wc, tm) for (_, _, _, _, hc, wc, _, _) in ph)
+        taps = max(rc * sc for (_, _, _, _, _, _, rc, sc) in ph)
+        return (tiles_m, _n_tiles(groups, cpg, tn, group_block), max(1, ceil_div(taps * kpg, tk)))
     return (ceil_div(N * H * W, tm), _n_tiles(groups, cpg, tn, group_block),
             ceil_div(R * S * kpg, tk))
 

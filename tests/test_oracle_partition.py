@@ -143,16 +143,20 @@ def test_conv_tiles_block_diagonal():
     for groups in (1, 3, 4, 5, 32):
         C = K = 16 * groups
         seen = {(ch // 16) // 4 for ch in range(K)}
-        for tiles_of in (P.fwd_tiles, P.dgrad_tiles):
-            t = tiles_of(2, 9, 9, C, K, 3, 3, 2, 2, 1, 1, groups, 128, 64, 32, group_block=4)
-            assert t[1] == len(seen)
-            assert t[2] == 5  # 3*3*16 = 144 reduction elements per group, 32 per iteration
+        t = P.fwd_tiles(2, 9, 9, C, K, 3, 3, 2, 2, 1, 1, groups, 128, 64, 32, group_block=4)
+        assert t[1] == len(seen)
+        assert t[2] == 5  # 3*3*16 = 144 reduction elements per group, 32 per iteration
+        t = P.dgrad_tiles(2, 9, 9, C, K, 3, 3, 2, 2, 1, 1, groups, 128, 64, 32, group_block=4)
+        assert t[1] == len(seen) and t[2] == 2  # at most 2 x 2 taps of one stride phase
     # the workload's layers: 64 x 14 x 14 output pixels (forward), 64 x 28 x 28
     # input pixels (dgrad), 32 groups
     assert P.fwd_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 128, 64, 32,
                        group_block=4) == (98, 8, 5)
+    # dgrad: four stride phases of 14 x 14 pixels per image (12544 pixels
+    # each over 64 images, 98 tiles of 128), at most 2 x 2 taps -> 64
+    # reduction elements per group
     assert P.dgrad_tiles(64, 28, 28, 512, 512, 3, 3, 2, 2, 1, 1, 32, 128, 64, 32,
-                         group_block=4) == (392, 8, 5)
+                         group_block=4) == (4 * 98, 8, 2)
     with pytest.raises(ValueError):
         P.fwd_tiles(2, 9, 9, 64, 64, 3, 3, 1, 1, 1, 1, 4, 128, 128, 32, group_block=4)
 
@@ -341,3 +345,33 @@ def test_scatter_needs_the_whole_group_resident():
         assert S.events(p, 1)[0] == ("pub", 1)
         assert sorted(c for k, c in S.events(p, 1) if k == "wait") == \
             [c for c in range(n) if c != 1]
+
+
+def test_dgrad_phases_by_brute_force():
+    # Every input pixel lies in exactly one phase; a phase's taps are
+    # exactly the taps whose shifted position is a multiple of the stride,
+    # which include every tap that reaches an output pixel of that pixel.
+    for (H, W, R, S, sh, sw, ph, pw) in [(9, 9, 3, 3, 2, 2, 1, 1), (28, 28, 3, 3, 2, 2, 1, 1),
+                                         (11, 7, 5, 5, 2, 1, 2, 2), (10, 13, 3, 2, 3, 2, 0, 1),
+                                         (5, 6, 1, 1, 2, 2, 0, 0), (8, 8, 3, 3, 1, 1, 1, 1),
+                                         (3, 4, 4, 4, 4, 3, 1, 2)]:
+        ho = (H + 2 * ph - R) // sh + 1
+        wo = (W + 2 * pw - S) // sw + 1
+        phases = P.dgrad_phases(H, W, R, S, sh, sw, ph, pw)
+        assert len(phases) == sh * sw
+        owner = {}
+        for (a, b, h0, w0, hc, wc, rc, sc) in phases:
+            taps = {(a + sh * i, b + sw * j) for i in range(rc) for j in range(sc)}
+            assert all(r < R and s < S for (r, s) in taps)
+            for i in range(hc):
+                for j in range(wc):
+                    h, w = h0 + sh * i, w0 + sw * j
+                    assert 0 <= h < H and 0 <= w < W and (h, w) not in owner
+                    owner[(h, w)] = (a, b)
+                    exact = {(r, s) for r in range(R) for s in range(S)
+                             if (h + ph - r) % sh == 0 and (w + pw - s) % sw == 0}
+                    assert exact == taps
+                    reach = {(r, s) for (r, s) in exact
+                             if 0 <= (h + ph - r) // sh < ho and 0 <= (w + pw - s) // sw < wo}
+                    assert reach <= taps
+        assert len(owner) == H * W
