@@ -6,6 +6,7 @@
 // support, decided before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <exception>
@@ -409,6 +410,35 @@ int run_conv(const skg_conv_args_t* a, bool dgrad, void* ws, size_t ws_bytes, hi
     c.pix_w = a->w;
     c.div_pix_hw = make_fastdiv((uint32_t)(a->h * a->w));
     c.act_bytes = (uint32_t)((int64_t)a->n * ho * wo * a->k * 2);
+  }
+  c.pix_h = dgrad ? a->h : ho;
+  c.nimg = a->n;
+  c.nph = 0;
+  if (dgrad && t->group_block) {
+    // Stride phases of the block-diagonal dgrad: M tiles phase by phase.
+    DgradPhase ph[kMaxDgradPhases];
+    c.nph = dgrad_phases(a, ph);
+    int tiles = 0;
+    for (int i = 0; i < c.nph; ++i) {
+      const DgradPhase& q = ph[i];
+      c.ph_tile[i] = tiles;
+      tiles += (int)ceil_div(int64_t(a->n) * q.hc * q.wc, t->tm);
+      c.ph_h0[i] = q.h0;
+      c.ph_w0[i] = q.w0;
+      c.ph_hc[i] = q.hc;
+      c.ph_wc[i] = q.wc;
+      c.ph_a[i] = q.a;
+      c.ph_b[i] = q.b;
+      c.ph_rc[i] = q.rc;
+      c.ph_sc[i] = q.sc;
+      // h0 + pad_h and a agree modulo the stride: exact divisions
+      c.ph_qh[i] = (q.h0 + a->pad_h - q.a) / a->stride_h;
+      c.ph_qw[i] = (q.w0 + a->pad_w - q.b) / a->stride_w;
+      c.ph_div_hw[i] = make_fastdiv((uint32_t)std::max(1, q.hc * q.wc));
+      c.ph_div_w[i] = make_fastdiv((uint32_t)std::max(1, q.wc));
+      c.ph_div_sc[i] = make_fastdiv((uint32_t)std::max(1, q.sc));
+    }
+    c.ph_tile[c.nph] = tiles;
   }
   c.nt_per_group = (int)ceil_div(c.npg, t->tn);
   c.filt_bytes = (uint32_t)((int64_t)a->k * a->r * a->s * cpg * 2);

@@ -24,6 +24,8 @@
 
 namespace skg {
 
+constexpr int kMaxPhases = 16;  // stride phases of a block-diagonal dgrad (sh * sw)
+
 struct ConvParams {
   const char* act;    // forward: X (N,H,W,C); dgrad: dY (N,Ho,Wo,K)
   const char* filt;   // forward: W (K,R,S,Cpg); dgrad: Wt (groups,Cpg,R,S,Kpg)
@@ -37,9 +39,21 @@ struct ConvParams {
   int act_c, out_c;   // channels of the activation and of the output tensor
   int act_h, act_w;   // spatial size of the activation tensor
   int pix_w;          // row length of the GEMM-M pixel grid (Wo forward, W dgrad)
+  int pix_h;          // its height (Ho forward, H dgrad)
   int S, sh, sw, ph, pw;
   uint32_t act_bytes, filt_bytes;
   FastDiv div_pix_hw, div_pix_w, div_cin, div_s, div_sh, div_sw;
+  // Stride phases of a block-diagonal dgrad, whose GEMM-M runs phase by
+  // phase: phase p owns M tiles [ph_tile[p], ph_tile[p+1]) over the pixels
+  // h = ph_h0 + sh*i (i < ph_hc), w = ph_w0 + sw*j (j < ph_wc) of every
+  // image, and the taps r = ph_a + sh*ri (ri < ph_rc), s = ph_b + sw*si
+  // (si < ph_sc); pixel (i, j) meets dY at (i + ph_qh - ri, j + ph_qw - si).
+  int nph, nimg;
+  int ph_tile[kMaxPhases + 1];
+  int ph_h0[kMaxPhases], ph_w0[kMaxPhases], ph_hc[kMaxPhases], ph_wc[kMaxPhases];
+  int ph_a[kMaxPhases], ph_b[kMaxPhases], ph_rc[kMaxPhases], ph_sc[kMaxPhases];
+  int ph_qh[kMaxPhases], ph_qw[kMaxPhases];
+  FastDiv ph_div_hw[kMaxPhases], ph_div_w[kMaxPhases], ph_div_sc[kMaxPhases];
 };
 
 // Operand loader of the grouped pipeline.  Group j of a segment is the A
@@ -232,6 +246,16 @@ struct ConvProblem {
   SKG_DEV static int dtype_c(const Params& c) { return c.dtype_out; }
 };
 
+// Stride phase of GEMM-M tile tm of a block-diagonal dgrad: the number of
+// phase boundaries at or below it (every boundary is compared, so the
+// table is fetched in one go instead of one dependent load per step).
+SKG_DEV int phase_of(const ConvParams& c, int tm) {
+  int p = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxPhases; ++q) p += (q < c.nph) & (tm >= c.ph_tile[q]);
+  return p;
+}
+
 // Block-diagonal grouped tile for 16 input and 16 output channels per group
 // (so C == K): the tile's TN = 16 * BDG channels are BDG whole groups, one
 // wave per group, over TM pixels.  A MAC iteration covers TK / 16 filter
@@ -254,7 +278,8 @@ struct ConvBdLoader {
   static constexpr int PLANE = Cfg::TM * PA;
   static constexpr int B_OFF = NPL * PLANE;
   static constexpr int ENTRY = B_OFF + Cfg::TN * RBB;
-  static constexpr int D = Cfg::BD_LDS / ENTRY > 6 ? 6 : Cfg::BD_LDS / ENTRY;
+  static constexpr int EPI = 64 * PA;  // copy-out staging beside the ring: 64 rows of 16-bit outputs
+  static constexpr int D = (Cfg::BD_LDS - EPI) / ENTRY > 6 ? 6 : (Cfg::BD_LDS - EPI) / ENTRY;
   static_assert(D >= 2 && PA == 128 && (RBB == 64 || RBB == 128), "ring entries");
   static constexpr int STEP = Cfg::THREADS / (PA / 16);  // A rows per DMA instruction
   static constexpr int UPL = Cfg::TM / STEP;              // DMA instructions per plane
@@ -266,14 +291,19 @@ struct ConvBdLoader {
   int wave;
   uint32_t cofs;               // A: byte offset of this thread's channels within a pixel
   bool chan_ok;                // its channels lie inside the activation
-  int pn[UPL];                 // n * act_h, or -1 for a row past GEMM-M
-  int py[UPL], px[UPL];        // forward: ho*sh - ph, wo*sw - pw; dgrad: h + ph, w + pw
-  uint32_t offb[UB], limb[UB]; // B: this thread's chunk, and the bytes left in its row
-  int act_h, act_w, S, RS, sh, sw;
+  int pn[UPL];                 // n * act_h, or -1 for a row past the tile's pixels
+  int py[UPL], px[UPL];        // forward: ho*sh - ph, wo*sw - pw; dgrad: dY row, column at tap (a, b)
+  uint32_t offb[UB], limb[UB]; // B: this thread's filter row (bytes), and its length (0 past the channels)
+  uint32_t bch[UB];            // B: this thread's 16-byte chunk within the iteration's row slice
+  int act_h, act_w, S, RS, ntap;
   uint32_t act_c2;
-  FastDiv div_s, div_sh, div_sw;
+  FastDiv div_s, div_sc;
+  // dgrad: the tile's stride phase (first tap (a, b), strides, taps per row)
+  int pa, pb, sc, sh, sw;
 
-  SKG_DEV void init(const ConvParams& c, int m0, int k0, int tid) {
+  // Tile tm of GEMM-M (forward: pixels tm*TM..; dgrad: the tm-th tile of
+  // the phase-major order), channels k0.. .
+  SKG_DEV void init(const ConvParams& c, int tm, int k0, int tid) {
     ra = make_rsrc(c.act, c.act_bytes);
     rb = make_rsrc(c.filt, c.filt_bytes);
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -281,28 +311,50 @@ struct ConvBdLoader {
     act_w = c.act_w;
     S = c.S;
     RS = c.kred / 16;
-    sh = c.sh;
-    sw = c.sw;
     act_c2 = (uint32_t)c.act_c * 2;
     div_s = c.div_s;
-    div_sh = c.div_sh;
-    div_sw = c.div_sw;
     int row, chunk;
     lds_slot<PA>(tid, row, chunk);
     const int ch = k0 + chunk * 8;
     chan_ok = ch < c.act_c;
     cofs = (uint32_t)ch * 2;
-    const int pix_w = c.pix_w;
+    if constexpr (!DGRAD) {
+      const int m0 = tm * Cfg::TM, pix_w = c.pix_w;
+      ntap = RS;
 #pragma unroll
-    for (int u = 0; u < UPL; ++u) {
-      const int m = m0 + row + u * STEP;
-      const uint32_t n = fdiv((uint32_t)m, c.div_pix_hw);
-      const int rem = m - (int)n * (int)c.div_pix_hw.d;
-      const int y = (int)fdiv((uint32_t)rem, c.div_pix_w);
-      const int x = rem - y * pix_w;
-      pn[u] = m < c.gm ? (int)n * act_h : -1;
-      py[u] = DGRAD ? y + c.ph : y * c.sh - c.ph;
-      px[u] = DGRAD ? x + c.pw : x * c.sw - c.pw;
+      for (int u = 0; u < UPL; ++u) {
+        const int m = m0 + row + u * STEP;
+        const uint32_t n = fdiv((uint32_t)m, c.div_pix_hw);
+        const int rem = m - (int)n * (int)c.div_pix_hw.d;
+        const int y = (int)fdiv((uint32_t)rem, c.div_pix_w);
+        const int x = rem - y * pix_w;
+        pn[u] = m < c.gm ? (int)n * act_h : -1;
+        py[u] = y * c.sh - c.ph;
+        px[u] = x * c.sw - c.pw;
+      }
+    } else {
+      const int p = phase_of(c, tm);
+      const int p0 = (tm - c.ph_tile[p]) * Cfg::TM;
+      const int hw = c.ph_hc[p] * c.ph_wc[p];
+      const int total = c.nimg * hw;  // the phase's pixels over all images
+      pa = c.ph_a[p];
+      pb = c.ph_b[p];
+      sc = c.ph_sc[p];
+      sh = c.sh;
+      sw = c.sw;
+      div_sc = c.ph_div_sc[p];
+      ntap = c.ph_rc[p] * c.ph_sc[p];
+#pragma unroll
+      for (int u = 0; u < UPL; ++u) {
+        const int m = p0 + row + u * STEP;
+        const uint32_t n = fdiv((uint32_t)m, c.ph_div_hw[p]);
+        const int rem = m - (int)n * hw;
+        const int i = (int)fdiv((uint32_t)rem, c.ph_div_w[p]);
+        const int j = rem - i * c.ph_wc[p];
+        pn[u] = m < total ? (int)n * act_h : -1;
+        py[u] = i + c.ph_qh[p];
+        px[u] = j + c.ph_qw[p];
+      }
     }
     const uint32_t rowb = (uint32_t)c.kred * 2;
 #pragma unroll
@@ -310,46 +362,71 @@ struct ConvBdLoader {
       int br, bc;
       lds_slot<RBB>(tid + u * Cfg::THREADS, br, bc);
       const int frow = k0 + br;
-      offb[u] = (uint32_t)frow * rowb + bc * 16;
-      limb[u] = frow < c.out_c ? rowb - bc * 16 : 0u;
+      offb[u] = (uint32_t)frow * rowb;
+      limb[u] = frow < c.out_c ? rowb : 0u;
+      bch[u] = (uint32_t)bc;
     }
   }
 
-  // Activation row u of this thread at filter tap `tap`, or kOOB.
-  SKG_DEV uint32_t a_off(int u, int tap, int r, int s) const {
-    int hi, wi;
-    bool ok = chan_ok & (tap < RS) & (pn[u] >= 0);
+  // Tap jj of the tile (forward: of the filter; dgrad: of its stride
+  // phase): filter position (r, s) and, for dgrad, the dY offset (ri, si)
+  // from the phase's first tap.
+  struct Tap {
+    int r, s, ri, si;
+    bool ok;
+  };
+  SKG_DEV Tap tap_of(int jj) const {
+    Tap t;
+    t.ok = jj < ntap;
     if constexpr (!DGRAD) {
-      hi = py[u] + r;
-      wi = px[u] + s;
+      t.r = (int)fdiv((uint32_t)jj, div_s);
+      t.s = jj - t.r * S;
+      t.ri = t.si = 0;
     } else {
-      const int t = py[u] - r, v = px[u] - s;
-      hi = (int)fdiv((uint32_t)t, div_sh);
-      wi = (int)fdiv((uint32_t)v, div_sw);
-      ok = ok & (t >= 0) & (v >= 0) & (hi * sh == t) & (wi * sw == v);
+      t.ri = (int)fdiv((uint32_t)jj, div_sc);
+      t.si = jj - t.ri * sc;
+      t.r = pa + sh * t.ri;
+      t.s = pb + sw * t.si;
     }
-    ok = ok & ((uint32_t)hi < (uint32_t)act_h) & ((uint32_t)wi < (uint32_t)act_w);
+    return t;
+  }
+
+  // Activation row u of this thread at tap t, or kOOB.
+  SKG_DEV uint32_t a_off(int u, const Tap& t) const {
+    const int hi = DGRAD ? py[u] - t.ri : py[u] + t.r;
+    const int wi = DGRAD ? px[u] - t.si : px[u] + t.s;
+    const bool ok = chan_ok & t.ok & (pn[u] >= 0) & ((uint32_t)hi < (uint32_t)act_h) &
+                    ((uint32_t)wi < (uint32_t)act_w);
     const uint32_t off = (uint32_t)((pn[u] + hi) * act_w + wi) * act_c2 + cofs;
     return ok ? off : kOOB;
   }
 
   // MAC iteration `it` into the ring entry at `e`: the A planes, then the
-  // B slab.
+  // B slab (the filter rows' entries of the iteration's taps; dgrad: the
+  // phase's taps, which are not consecutive in the filter row).
   SKG_DEV void issue_iter(int it, SKG_LDS char* e) const {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int tap = it * NPL + j;
-      const int r = (int)fdiv((uint32_t)tap, div_s);
-      const int s = tap - r * S;
+      const Tap t = tap_of(it * NPL + j);
 #pragma unroll
       for (int u = 0; u < UPL; ++u)
-        dma16(ra, lds_addr(e + j * PLANE + u * Cfg::THREADS * 16 + wave * 1024), a_off(u, tap, r, s));
+        dma16(ra, lds_addr(e + j * PLANE + u * Cfg::THREADS * 16 + wave * 1024), a_off(u, t));
     }
-    const uint32_t kb = (uint32_t)it * RBB;
 #pragma unroll
-    for (int u = 0; u < UB; ++u)
-      dma16(rb, lds_addr(e + B_OFF + u * Cfg::THREADS * 16 + wave * 1024),
-            kb < limb[u] ? offb[u] + kb : kOOB);
+    for (int u = 0; u < UB; ++u) {
+      uint32_t off;
+      if constexpr (!DGRAD) {
+        const uint32_t kb = (uint32_t)it * RBB + bch[u] * 16u;
+        off = kb < limb[u] ? offb[u] + kb : kOOB;
+      } else {
+        // Chunk bch of the iteration's slice: half bch % 2 of the 16
+        // channels of tap it * NPL + bch / 2 of the phase.
+        const Tap t = tap_of(it * NPL + (int)(bch[u] >> 1));
+        const uint32_t kb = (uint32_t)(t.r * S + t.s) * 32u + (bch[u] & 1u) * 16u;
+        off = (t.ok && limb[u] != 0u) ? offb[u] + kb : kOOB;
+      }
+      dma16(rb, lds_addr(e + B_OFF + u * Cfg::THREADS * 16 + wave * 1024), off);
+    }
   }
 };
 
@@ -359,23 +436,36 @@ struct ConvBdProblem {
   static constexpr int kScaleInc = 1;  // no scales
   typedef ConvBdLoader<Cfg, DGRAD> Loader;
 
+  // dgrad: tile rows are pixels of one stride phase (out_row remaps them)
+  static constexpr bool kRowRemap = DGRAD;
+
   SKG_DEV static void setup(const Params& c, const KPlan& p, int tile, Loader& ld, OutTile& out, int tid) {
     const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-    ld.init(c, tm * Cfg::TM, tn * Cfg::TN, tid);
+    ld.init(c, tm, tn * Cfg::TN, tid);
     out = out_tile(c, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& c, const KPlan& p, int tile) {
     const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-    const int m0 = tm * Cfg::TM, k0 = tn * Cfg::TN;
+    const int k0 = tn * Cfg::TN;
     const int esz = c.dtype_out == DT_F32 ? 4 : 2;
     OutTile o;
-    // Pixel rows of out_c channels; the tile's channels start at k0.
-    o.base = c.out + ((size_t)m0 * c.out_c + k0) * esz;
     o.sa = nullptr;
     o.sb = nullptr;
     o.ld = c.out_c;
-    o.rows = c.gm - m0;
     o.cols = c.out_c - k0;
+    if constexpr (!DGRAD) {
+      // Pixel rows of out_c channels; the tile's channels start at k0.
+      const int m0 = tm * Cfg::TM;
+      o.base = c.out + ((size_t)m0 * c.out_c + k0) * esz;
+      o.rows = c.gm - m0;
+    } else {
+      const int ph = phase_of(c, tm);
+      const int p0 = (tm - c.ph_tile[ph]) * Cfg::TM;
+      o.base = c.out + (size_t)k0 * esz;
+      o.rows = c.nimg * c.ph_hc[ph] * c.ph_wc[ph] - p0;
+      o.rm = RowRemap{p0, c.ph_hc[ph] * c.ph_wc[ph], c.ph_wc[ph], c.ph_h0[ph], c.ph_w0[ph],
+                      c.sh, c.sw, c.ph_div_hw[ph], c.ph_div_w[ph], c.pix_h, c.pix_w};
+    }
     return o;
   }
   SKG_DEV static int dtype_c(const Params& c) { return c.dtype_out; }

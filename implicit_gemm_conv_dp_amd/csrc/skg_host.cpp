@@ -11,6 +11,8 @@
 #include <climits>
 #include <cstring>
 
+#include <algorithm>
+
 #include "skg_internal.hpp"
 
 namespace skg {
@@ -284,9 +286,20 @@ GemmShape conv_shape(const skg_conv_args_t* a, const TileDesc& t, bool dgrad) {
   const int64_t kpg = a->k / a->groups, cpg = a->c / a->groups;
   if (t.group_block) {
     // Block-diagonal: group_block whole groups per N tile, the reduction
-    // per group (16 channels at every tap).
-    const int64_t gm = dgrad ? int64_t(a->n) * a->h * a->w : int64_t(a->n) * ho * wo;
-    return {ceil_div(gm, t.tm), ceil_div(a->groups, t.group_block), ceil_div(a->r * a->s * 16, t.tk)};
+    // per group (16 channels at every tap).  dgrad runs GEMM-M stride phase
+    // by phase, each with its own taps: M tiles per phase, the iterations of
+    // the phase with the most taps.
+    if (!dgrad)
+      return {ceil_div(int64_t(a->n) * ho * wo, t.tm), ceil_div(a->groups, t.group_block),
+              ceil_div(a->r * a->s * 16, t.tk)};
+    DgradPhase ph[kMaxDgradPhases];
+    const int np = dgrad_phases(a, ph);
+    int64_t tiles_m = 0, taps = 0;
+    for (int i = 0; i < np; ++i) {
+      tiles_m += ceil_div(int64_t(a->n) * ph[i].hc * ph[i].wc, t.tm);
+      taps = std::max<int64_t>(taps, int64_t(ph[i].rc) * ph[i].sc);
+    }
+    return {tiles_m, ceil_div(a->groups, t.group_block), std::max<int64_t>(1, ceil_div(taps * 16, t.tk))};
   }
   // Groups fold into GEMM-N with the tile count per group.
   if (!dgrad)
@@ -395,6 +408,8 @@ int validate_conv(const skg_conv_args_t* a, bool dgrad) {
   if (cpg % 8 || kpg % 8) return unsupported("channels per group must be multiples of 8");
   if (t->group_block && (cpg != 16 || kpg != 16))
     return unsupported("the block-diagonal tile needs 16 input and 16 output channels per group");
+  if (t->group_block && dgrad && int64_t(a->stride_h) * a->stride_w > kMaxDgradPhases)
+    return unsupported("the block-diagonal dgrad tile takes strides with at most 16 phases (stride_h * stride_w)");
   const int64_t ho = (int64_t(a->h) + 2 * a->pad_h - a->r) / a->stride_h + 1;
   const int64_t wo = (int64_t(a->w) + 2 * a->pad_w - a->s) / a->stride_w + 1;
   if (int64_t(a->h) + 2 * a->pad_h < a->r || int64_t(a->w) + 2 * a->pad_w < a->s || ho <= 0 || wo <= 0)

@@ -75,4 +75,32 @@ int64_t dgrad_filter_bytes(const skg_conv_args_t* a);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Stride phases of the input gradient, row phase major: phase (a, b) holds
+// the pixels with (h + pad_h) mod stride_h == a and (w + pad_w) mod
+// stride_w == b (rows h0, h0 + stride_h, ..., hc of them; columns w0, ...,
+// wc) and meets exactly the taps r = a + stride_h * ri (ri < rc), s = b +
+// stride_w * si (si < sc).  Returns the number of phases written to out.
+struct DgradPhase {
+  int a, b, h0, w0, hc, wc, rc, sc;
+};
+inline int dgrad_phases(const skg_conv_args_t* c, DgradPhase* out) {
+  int n = 0;
+  for (int a = 0; a < c->stride_h; ++a)
+    for (int b = 0; b < c->stride_w; ++b) {
+      DgradPhase p;
+      p.a = a;
+      p.b = b;
+      p.h0 = ((a - c->pad_h) % c->stride_h + c->stride_h) % c->stride_h;
+      p.w0 = ((b - c->pad_w) % c->stride_w + c->stride_w) % c->stride_w;
+      p.hc = c->h > p.h0 ? (int)ceil_div(c->h - p.h0, c->stride_h) : 0;
+      p.wc = c->w > p.w0 ? (int)ceil_div(c->w - p.w0, c->stride_w) : 0;
+      p.rc = c->r > a ? (int)ceil_div(c->r - a, c->stride_h) : 0;
+      p.sc = c->s > b ? (int)ceil_div(c->s - b, c->stride_w) : 0;
+      out[n++] = p;
+    }
+  return n;
+}
+// Stride phases a block-diagonal dgrad can carry.
+constexpr int kMaxDgradPhases = 16;
+
 }  // namespace skg

@@ -55,13 +55,50 @@ struct Scratch {
 // rows x cols, optional per-row / per-column scales (the problem's
 // kScaleInc is 1), or one scale for every row and one for every column
 // (kScaleInc is 0: per-tensor).
+// Rows of a block-diagonal dgrad tile are pixels of one stride phase: tile
+// row r is phase pixel q = p0 + r, i.e. image q / hw, row h0 + sh * i and
+// column w0 + sw * j with (i, j) = divmod(q % hw, wc).
+struct RowRemap {
+  int p0, hw, wc, h0, w0, sh, sw;
+  FastDiv div_hw, div_wc;
+  int H, W;
+};
+
 struct OutTile {
   char* base;
   const float* sa;
   const float* sb;
   int ld;
   int rows, cols;
+  RowRemap rm;  // read only by problems with kRowRemap
 };
+
+// Element offset of tile row r from the tile base.
+SKG_DEV size_t remap_row(const RowRemap& m, int r) {
+  const uint32_t q = (uint32_t)(m.p0 + r);
+  const uint32_t n = fdiv(q, m.div_hw);
+  const uint32_t rem = q - n * (uint32_t)m.hw;
+  const uint32_t i = fdiv(rem, m.div_wc);
+  const uint32_t j = rem - i * (uint32_t)m.wc;
+  return ((size_t)n * m.H + m.h0 + m.sh * i) * m.W + m.w0 + m.sw * j;
+}
+
+// Problems whose output rows are not consecutive declare kRowRemap.
+template <class P, class = void>
+struct ProbRemap {
+  static constexpr bool value = false;
+};
+template <class P>
+struct ProbRemap<P, std::void_t<decltype(P::kRowRemap)>> {
+  static constexpr bool value = P::kRowRemap;
+};
+template <class P>
+SKG_DEV size_t out_row(const OutTile& o, int r) {
+  if constexpr (ProbRemap<P>::value)
+    return remap_row(o.rm, r) * (size_t)o.ld;
+  else
+    return (size_t)r * o.ld;
+}
 
 struct GemmParams {
   const char* A;
@@ -842,6 +879,7 @@ struct WgradBdLoader {
   // ring of D entries filling the LDS.
   static constexpr int TAPS = Cfg::TN / 16, PLANE = Cfg::TK * PA;
   static constexpr int ENTRY = PLANE * (1 + TAPS);
+  static constexpr int EPI = 0;  // copy-out straight from the accumulators
   static constexpr int D = Cfg::BD_LDS / ENTRY > 6 ? 6 : Cfg::BD_LDS / ENTRY;
   static_assert(D >= 2, "two ring entries at least");
   static constexpr int CPR = PA / 16;
@@ -996,14 +1034,15 @@ struct LoaderMx<L, std::void_t<decltype(L::kMx)>> {
   static constexpr bool value = L::kMx;
 };
 
-// Block-diagonal loaders declare their ring: D entries of ENTRY bytes.
+// Block-diagonal loaders declare their ring (D entries of ENTRY bytes) and
+// the copy-out staging (EPI bytes) that follows it.
 template <class L, class = void>
 struct LoaderRing {
-  static constexpr int bytes = 0;
+  static constexpr int ring = 0, bytes = 0;
 };
 template <class L>
 struct LoaderRing<L, std::void_t<decltype(L::ENTRY)>> {
-  static constexpr int bytes = L::D * L::ENTRY;
+  static constexpr int ring = L::D * L::ENTRY, bytes = ring + L::EPI;
 };
 
 template <class Cfg, class Prob, int FIX>
@@ -1907,7 +1946,7 @@ struct Engine {
         const float sb = o.sb && col + e < o.cols ? o.sb[(col + e) * Prob::kScaleInc] : 1.f;
         x[e] = (v[e] * sa) * sb;
       }
-      const size_t idx = (size_t)row * o.ld + col;
+      const size_t idx = out_row<Prob>(o, row) + col;
       if (full && dt == DT_F32 && ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
         *(f32x4*)(o.base + idx * 4) = f32x4{x[0], x[1], x[2], x[3]};
         continue;
@@ -2102,7 +2141,7 @@ struct Engine {
             for (int e = 0; e < 4; ++e) unsafeAtomicAdd(wsp + row * Cfg::TN + col + e, v[e]);
             continue;
           }
-          const size_t idx = (size_t)row * o.ld + col;
+          const size_t idx = out_row<Prob>(o, row) + col;
           if (fx.how == OUT_STORE && !o.sa && !o.sb && col + 4 <= o.cols) {
             if (dt == DT_F32 && ((uintptr_t)(o.base + idx * 4) & 15) == 0) {
               __builtin_nontemporal_store(v, (f32x4*)((float*)o.base + idx));
@@ -2132,8 +2171,50 @@ struct Engine {
     }
   }
 
+  // Copy-out of a block-diagonal forward / dgrad tile with 16-bit outputs
+  // through the staging area beside the ring (which keeps streaming the
+  // next tile meanwhile): two passes of 64 rows; each wave leaves its 16
+  // channels of every row there (one packed 8-byte write per fragment, 16-byte
+  // chunks XOR-swizzled by row), then 8 lanes store each 128-byte row whole.
+  // Stored straight from the registers, a row arrives as four 32-byte pieces
+  // from four waves.
+  SKG_DEV void write_bd_staged(const OutTile& o, int dt) {
+    static_assert(Cfg::WM == 1 && Cfg::FN == 1 && Cfg::TN * 2 == 128 && Cfg::TM % 64 == 0, "staging map");
+    constexpr int PR = 64, FPP = PR / Cfg::MN, NCH = PR * 8 / Cfg::THREADS;
+    SKG_LDS char* st = lds + LoaderRing<Loader>::ring;
+#pragma unroll
+    for (int pass = 0; pass < Cfg::TM / PR; ++pass) {
+#pragma unroll
+      for (int ff = 0; ff < FPP; ++ff) {
+        const f32x4 v = acc[pass * FPP + ff][0];
+        const int r = ff * Cfg::MN + (lane & 15);
+        const int byte = wn * 32 + 8 * (lane >> 4);  // 4 channels of the wave's 16
+        const i32x2 h = dt == DT_F16 ? i32x2{(int)pack_f16x2(v[0], v[1]), (int)pack_f16x2(v[2], v[3])}
+                                     : i32x2{(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+        *(SKG_LDS i32x2*)(st + r * 128 + ((((byte >> 4) ^ (r & 7))) << 4) + (byte & 15)) = h;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int id = tid + k * Cfg::THREADS, r = id >> 3, c = id & 7;
+        const int row = pass * PR + r;
+        if (row < o.rows && c * 8 < o.cols) {
+          const i32x4 d = *(const SKG_LDS i32x4*)(st + r * 128 + ((c ^ (r & 7)) << 4));
+          __builtin_nontemporal_store(d, (i32x4*)((uint16_t*)o.base + out_row<Prob>(o, row) + c * 8));
+        }
+      }
+      lds_barrier();  // the staging area is free for the next pass
+    }
+  }
+
   SKG_DEV void write_out(const OutTile& o, const Fix& fx, float* wsp) {
-    if constexpr (kBd) {
+    if constexpr (kStream) {
+      const int dt = Prob::dtype_c(prm);
+      if (fx.how == OUT_STORE && dt != DT_F32 && !o.sa && !o.sb)
+        write_bd_staged(o, dt);
+      else
+        write_direct(o, fx, wsp);
+    } else if constexpr (kBd) {
       write_direct(o, fx, wsp);
     } else {
       write_staged(o, fx, wsp);
@@ -2526,7 +2607,7 @@ __global__ __launch_bounds__(256) void stage2_kernel(typename Prob::Params prm, 
     float v = w[idx];
     if (o.sa) v *= o.sa[row * Prob::kScaleInc];
     if (o.sb) v *= o.sb[col * Prob::kScaleInc];
-    const size_t oi = (size_t)row * o.ld + col;
+    const size_t oi = out_row<Prob>(o, row) + col;
     if (dt == DT_F32)
       ((float*)o.base)[oi] = v;
     else if (dt == DT_F16)

@@ -79,6 +79,12 @@ def test_block_diagonal_conv_plans_equal_oracle(op):
                         assert v == getattr(o, f), (op, shape, mode, red, ctas, f)
     kw = kw_of((2, 8, 8, 64, 128, 3, 3, (1, 1), (1, 1), 4), "128x64x32", "dp_sk", "tree", 8)
     assert "16 input and 16 output channels" in rejected(op, **kw)
+    # dgrad runs phase by phase: at most 16 stride phases
+    kw = kw_of((1, 40, 40, 64, 64, 3, 3, (5, 4), (1, 1), 4), "128x64x32", "dp_sk", "tree", 8)
+    if op == "dgrad":
+        assert "phases" in rejected(op, **kw)
+    else:
+        (skg.plan_fwd)(**kw)
 
 
 def rejected(op, **kw):

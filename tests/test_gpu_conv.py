@@ -160,6 +160,12 @@ BD_SHAPES = {
     "bd_1x1": (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
     # 5x5 over 13 iterations, strides 2 x 1
     "bd_5x5": (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+    # dgrad stride phases: 1x1 with stride 2 (three of four phases meet no
+    # tap: zero rows), stride 3 (nine phases of one tap each), 4x4 with
+    # strides 2 x 3 (phases of 2 x 2 and 2 x 1 taps)
+    "bd_s2_1x1": (2, 9, 8, 64, 64, 1, 1, (2, 2), (0, 0), 4),
+    "bd_s3": (2, 13, 11, 48, 48, 3, 3, (3, 3), (1, 1), 3),
+    "bd_s23_4x4": (2, 10, 9, 64, 64, 4, 4, (2, 3), (1, 1), 4),
 }
 
 
