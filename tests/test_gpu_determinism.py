@@ -5,8 +5,10 @@ so a partial read before its release would show up as a NaN or a different
 value (rocm-libraries PR #13151, GPU test plan and the review finding that
 only the flags had been reset between launches).  Workloads: the fp16 GEMM
 over a 6-CTA pool whose ranges straddle tiles, the bf16 GEMM with 48
-stream-K tiles over 256 CTAs, and both conv wgrad workloads, each in the
-dp_sk and persistent modes.  That no bounded flag wait gave up during these
+stream-K tiles over 256 CTAs, both conv wgrad workloads (the grouped one
+on the block-diagonal and on the per-group tile), each in the dp_sk and
+persistent modes; the reduce-scatter launches; and forward / dgrad
+convolutions with shared stream-K tiles.  That no bounded flag wait gave up during these
 launches is checked for every GPU test by the fixture in conftest.py (the
 library counts give-ups; skg_fixup_timeouts).
 """
@@ -123,3 +125,52 @@ def test_wgrad_scatter_repeat(index, tile):
     assert plan["slices"] > 1 and plan["sk_ctas"] == plan["tiles"] * plan["slices"]
     ws = skg.workspace_for(plan, "cuda")
     repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)
+
+
+def test_wgrad_block_diagonal_scatter_repeat():
+    # The grouped layer's benchmark launch: block-diagonal tile, dp_sk over
+    # 224 CTAs = 28 whole slices per tile, reduce-scatter fix-up.
+    wl = synth.WORKLOADS[4]
+    inp = wl.inputs()
+    dx, ddy = to_dev(inp["x"], wl.dtype), to_dev(inp["dy"], wl.dtype)
+    dw = torch.empty(wl.k * wl.r * wl.s * (wl.c // wl.groups), dtype=torch.float32, device="cuda")
+    kw = dict(n=wl.n, h=wl.h, w=wl.w, c=wl.c, k=wl.k, r=wl.r, s=wl.s, stride=wl.stride,
+              pad=wl.pad, groups=wl.groups, dtype=wl.dtype, tile="64x144x32", mode="dp_sk",
+              reduction="scatter", ctas=224)
+    plan = skg.plan_wgrad(**kw)
+    assert plan["sk_ctas"] == 224 and plan["max_contrib"] == 28
+    ws = skg.workspace_for(plan, "cuda")
+    repeat(lambda: skg.wgrad(dx, ddy, dw, workspace=ws, **kw), dw, ws)
+
+
+# Convolutions with stream-K tiles shared by several CTAs: the dense layer's
+# forward / dgrad on 256x256x64 tiles (the benchmark's launch), and grouped
+# shapes on the block-diagonal tile (dgrad by stride phase).
+CONV_REPEATS = [
+    ("fwd", (32, 56, 56, 256, 256, 3, 3, (1, 1), (1, 1), 1), "f16", "256x256x64", 256),
+    ("dgrad", (32, 56, 56, 256, 256, 3, 3, (1, 1), (1, 1), 1), "f16", "256x256x64", 256),
+    ("fwd", (64, 28, 28, 512, 512, 3, 3, (2, 2), (1, 1), 32), "bf16", "128x64x32", 512),
+    ("dgrad", (4, 14, 14, 64, 64, 3, 3, (2, 2), (1, 1), 4), "bf16", "128x64x32", 5),
+]
+
+
+@pytest.mark.parametrize("reduction", ["linear", "tree"])
+@pytest.mark.parametrize("mode", ["dp_sk", "persistent"])
+@pytest.mark.parametrize("case", range(len(CONV_REPEATS)))
+def test_conv_repeat(case, mode, reduction):
+    op, shape, fmt, tile, ctas = CONV_REPEATS[case]
+    n, h, w, c, k, r, s, st, pd, g = shape
+    ho = (h + 2 * pd[0] - r) // st[0] + 1
+    wo = (w + 2 * pd[1] - s) // st[1] + 1
+    na = n * h * w * c if op == "fwd" else n * ho * wo * k
+    act = to_dev(synth.to_codes(synth.draw("uniform", na, 301), fmt), fmt)
+    filt = to_dev(synth.to_codes(synth.draw("uniform", k * r * s * (c // g), 302), fmt), fmt)
+    out = torch.empty(n * ho * wo * k if op == "fwd" else n * h * w * c, dtype=torch.bfloat16,
+                      device="cuda")
+    kw = dict(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=st, pad=pd, groups=g, dtype=fmt,
+              dtype_out="bf16", tile=tile, mode=mode, reduction=reduction, ctas=ctas)
+    plan = (skg.plan_fwd if op == "fwd" else skg.plan_dgrad)(**kw)
+    assert plan["sk_ctas"] > 0 and plan["max_contrib"] >= 2, plan
+    ws = skg.workspace_for(plan, "cuda")
+    call = skg.fwd if op == "fwd" else skg.dgrad
+    repeat(lambda: call(act, filt, out, workspace=ws, **kw), out, ws)
