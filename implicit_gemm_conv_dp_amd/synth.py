@@ -204,10 +204,9 @@ class ConvWorkload:
         }
 
 
-# The five workloads.  Tiles for 1, 2 and 4 are the ones the workloads name;
-# 3 and 5 use the tiles measured fastest for them.  Workload 4 runs its pool
-# at the resident capacity of the 32x64x64 tile (two CTAs per CU), which
-# keeps twice the loads in flight on this latency-bound shape.  Workload 3
+# The five workloads.  Tiles for 1 and 2 are the ones the workloads name;
+# 3, 4 and 5 use the tiles measured fastest for them (4: block-diagonal,
+# below).  Workload 3
 # runs 256x256 tiles (9 output tiles) over a pool of 252 = 9 x 28 CTAs: every
 # stream-K CTA then holds 56 whole iterations of one tile, which the k-major
 # CTA order turns into 28 k ranges read by all 9 tiles at about the same time.
@@ -218,7 +217,8 @@ WORKLOADS = {
                     "normal01", "256x256x64", ("persistent", "dp_sk"), ("tree",), 256),
     3: WgradWorkload(3, "wgrad_f16_n32_56x56_c256_k256_3x3", 32, 56, 56, 256, 256, 3, 3,
                      (1, 1), (1, 1), 1, "f16", "uniform", "256x256x64",
-                     ("persistent", "dp_sk"), ("tree", "linear", "atomic", "workspace"), 252),
+                     ("persistent", "dp_sk"), ("scatter", "tree", "linear", "atomic", "workspace"),
+                     252),
     # 16 channels per group: the block-diagonal tile (four whole groups per
     # 64-row tile, whole 128-byte lines) over 224 CTAs, i.e. 28 whole slices
     # of 14 iterations per tile, with the reduce-scatter fix-up; the
@@ -260,12 +260,14 @@ NEXT_WORKLOADS = {
 }
 
 # Further launches of a workload reported beside its own: the dense wgrad
-# layer with the reduce-scatter fix-up (not one of the page's four); the
+# layer with the tree fix-up (its own launch takes the reduce-scatter
+# fix-up, which is not one of the page's four; all five run at full size in
+# the parity tests); the
 # grouped layer with the linear and tree fix-ups on the block-diagonal tile
 # and with the per-group tile (partial 32-row M tiles, groups folded into
 # GEMM-M one per tile); the grouped forward and dgrad on the dense
 # per-group 128x128x64 tile (16 of its 128 columns used).
-EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "scatter", 252)],
+EXTRA_LAUNCHES = {3: [("256x256x64", "persistent", "tree", 252)],
                   4: [("64x144x32", "dp_sk", "tree", 224), ("64x144x32", "dp_sk", "linear", 128),
                       ("32x64x64", "dp_sk", "linear", 512)],
                   8: [("128x64x32", "persistent", "tree", 512), ("128x128x64", "dp_sk", "tree", 256)],
