@@ -264,7 +264,8 @@ SKG_DEV int phase_of(const ConvParams& c, int tm) {
 // 128-byte line per row for TN = 64), the B side TN filter rows (W for the
 // forward pass, the per-group transposed Wt for dgrad) of TK reduction
 // elements; the filter rows of consecutive groups are consecutive, so B is
-// one dense slab.  Wave w multiplies its group's 32-byte slice of every A
+// one dense slab.  dgrad tiles hold the pixels of one stride phase (see
+// ConvParams) and walk only that phase's taps.  Wave w multiplies its group's 32-byte slice of every A
 // row by its group's 16 filter rows.  Two CTAs share a CU (two ring entries
 // each): the loads of a CU are bound by the requests its waves keep in
 // flight, and the short per-tile reduction leaves little to pipeline.
