@@ -94,16 +94,27 @@ def copy_calibration(mib, steps):
                       "launches": steps}), flush=True)
 
 
+def _code_only(src):
+    """C/C++ source without its comments and with whitespace runs folded, so
+    that an edit to a comment does not change the hash (string literals are
+    kept as they are)."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+    out = tok.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+    return re.sub(r"\s+", " ", out).strip()
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources, so that counters taken on other code are not used."""
+    """Hash of the HIP sources' code (comments and layout left out), so that
+    counters taken on other code are not used."""
     import hashlib
     d = os.path.join(ROOT, "implicit_gemm_conv_dp_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".hpp", ".cpp", ".h")):
             h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(d, f), encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
