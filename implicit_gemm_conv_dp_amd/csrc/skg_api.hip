@@ -423,20 +423,22 @@ int run_conv(const skg_conv_args_t* a, bool dgrad, void* ws, size_t ws_bytes, hi
       const DgradPhase& q = ph[i];
       c.ph_tile[i] = tiles;
       tiles += (int)ceil_div(int64_t(a->n) * q.hc * q.wc, t->tm);
-      c.ph_h0[i] = q.h0;
-      c.ph_w0[i] = q.w0;
-      c.ph_hc[i] = q.hc;
-      c.ph_wc[i] = q.wc;
-      c.ph_a[i] = q.a;
-      c.ph_b[i] = q.b;
-      c.ph_rc[i] = q.rc;
-      c.ph_sc[i] = q.sc;
+      DgradPhaseRec& r = c.phase[i];
+      r = DgradPhaseRec{};
+      r.h0 = q.h0;
+      r.w0 = q.w0;
+      r.hc = q.hc;
+      r.wc = q.wc;
+      r.a = q.a;
+      r.b = q.b;
+      r.rc = q.rc;
+      r.sc = q.sc;
       // h0 + pad_h and a agree modulo the stride: exact divisions
-      c.ph_qh[i] = (q.h0 + a->pad_h - q.a) / a->stride_h;
-      c.ph_qw[i] = (q.w0 + a->pad_w - q.b) / a->stride_w;
-      c.ph_div_hw[i] = make_fastdiv((uint32_t)std::max(1, q.hc * q.wc));
-      c.ph_div_w[i] = make_fastdiv((uint32_t)std::max(1, q.wc));
-      c.ph_div_sc[i] = make_fastdiv((uint32_t)std::max(1, q.sc));
+      r.qh = (q.h0 + a->pad_h - q.a) / a->stride_h;
+      r.qw = (q.w0 + a->pad_w - q.b) / a->stride_w;
+      r.div_hw = make_fastdiv((uint32_t)std::max(1, q.hc * q.wc));
+      r.div_w = make_fastdiv((uint32_t)std::max(1, q.wc));
+      r.div_sc = make_fastdiv((uint32_t)std::max(1, q.sc));
     }
     c.ph_tile[c.nph] = tiles;
   }

@@ -26,6 +26,20 @@ namespace skg {
 
 constexpr int kMaxPhases = 16;  // stride phases of a block-diagonal dgrad (sh * sw)
 
+// One stride phase of a block-diagonal dgrad: the pixels h = h0 + sh*i
+// (i < hc), w = w0 + sw*j (j < wc) of every image, and the taps
+// r = a + sh*ri (ri < rc), s = b + sw*si (si < sc); pixel (i, j) meets dY
+// at (i + qh - ri, j + qw - si).  One record per phase, so that a tile's
+// set-up reads its phase in one round of scalar loads.
+struct alignas(16) DgradPhaseRec {
+  int h0, w0, hc, wc;
+  int a, b, rc, sc;
+  int qh, qw, pad0, pad1;
+  FastDiv div_hw, div_w, div_sc;  // by hc * wc, wc, sc
+  int pad2[3];
+};
+static_assert(sizeof(DgradPhaseRec) == 96, "phase record");
+
 struct ConvParams {
   const char* act;    // forward: X (N,H,W,C); dgrad: dY (N,Ho,Wo,K)
   const char* filt;   // forward: W (K,R,S,Cpg); dgrad: Wt (groups,Cpg,R,S,Kpg)
@@ -44,16 +58,11 @@ struct ConvParams {
   uint32_t act_bytes, filt_bytes;
   FastDiv div_pix_hw, div_pix_w, div_cin, div_s, div_sh, div_sw;
   // Stride phases of a block-diagonal dgrad, whose GEMM-M runs phase by
-  // phase: phase p owns M tiles [ph_tile[p], ph_tile[p+1]) over the pixels
-  // h = ph_h0 + sh*i (i < ph_hc), w = ph_w0 + sw*j (j < ph_wc) of every
-  // image, and the taps r = ph_a + sh*ri (ri < ph_rc), s = ph_b + sw*si
-  // (si < ph_sc); pixel (i, j) meets dY at (i + ph_qh - ri, j + ph_qw - si).
+  // phase: phase p owns M tiles [ph_tile[p], ph_tile[p+1]), described by
+  // phase[p].
   int nph, nimg;
   int ph_tile[kMaxPhases + 1];
-  int ph_h0[kMaxPhases], ph_w0[kMaxPhases], ph_hc[kMaxPhases], ph_wc[kMaxPhases];
-  int ph_a[kMaxPhases], ph_b[kMaxPhases], ph_rc[kMaxPhases], ph_sc[kMaxPhases];
-  int ph_qh[kMaxPhases], ph_qw[kMaxPhases];
-  FastDiv ph_div_hw[kMaxPhases], ph_div_w[kMaxPhases], ph_div_sc[kMaxPhases];
+  DgradPhaseRec phase[kMaxPhases];
 };
 
 // Operand loader of the grouped pipeline.  Group j of a segment is the A
@@ -335,26 +344,27 @@ struct ConvBdLoader {
       }
     } else {
       const int p = phase_of(c, tm);
+      const DgradPhaseRec& r = c.phase[p];
       const int p0 = (tm - c.ph_tile[p]) * Cfg::TM;
-      const int hw = c.ph_hc[p] * c.ph_wc[p];
+      const int hw = r.hc * r.wc;
       const int total = c.nimg * hw;  // the phase's pixels over all images
-      pa = c.ph_a[p];
-      pb = c.ph_b[p];
-      sc = c.ph_sc[p];
+      pa = r.a;
+      pb = r.b;
+      sc = r.sc;
       sh = c.sh;
       sw = c.sw;
-      div_sc = c.ph_div_sc[p];
-      ntap = c.ph_rc[p] * c.ph_sc[p];
+      div_sc = r.div_sc;
+      ntap = r.rc * r.sc;
 #pragma unroll
       for (int u = 0; u < UPL; ++u) {
         const int m = p0 + row + u * STEP;
-        const uint32_t n = fdiv((uint32_t)m, c.ph_div_hw[p]);
+        const uint32_t n = fdiv((uint32_t)m, r.div_hw);
         const int rem = m - (int)n * hw;
-        const int i = (int)fdiv((uint32_t)rem, c.ph_div_w[p]);
-        const int j = rem - i * c.ph_wc[p];
+        const int i = (int)fdiv((uint32_t)rem, r.div_w);
+        const int j = rem - i * r.wc;
         pn[u] = m < total ? (int)n * act_h : -1;
-        py[u] = i + c.ph_qh[p];
-        px[u] = j + c.ph_qw[p];
+        py[u] = i + r.qh;
+        px[u] = j + r.qw;
       }
     }
     const uint32_t rowb = (uint32_t)c.kred * 2;
@@ -368,6 +378,9 @@ struct ConvBdLoader {
       bch[u] = (uint32_t)bc;
     }
   }
+
+  // MAC iterations that hold at least one of the tile's taps.
+  SKG_DEV int iters() const { return (ntap * 16 + Cfg::TK - 1) / Cfg::TK; }
 
   // Tap jj of the tile (forward: of the filter; dgrad: of its stride
   // phase): filter position (r, s) and, for dgrad, the dY offset (ri, si)
@@ -461,11 +474,11 @@ struct ConvBdProblem {
       o.rows = c.gm - m0;
     } else {
       const int ph = phase_of(c, tm);
+      const DgradPhaseRec& r = c.phase[ph];
       const int p0 = (tm - c.ph_tile[ph]) * Cfg::TM;
       o.base = c.out + (size_t)k0 * esz;
-      o.rows = c.nimg * c.ph_hc[ph] * c.ph_wc[ph] - p0;
-      o.rm = RowRemap{p0, c.ph_hc[ph] * c.ph_wc[ph], c.ph_wc[ph], c.ph_h0[ph], c.ph_w0[ph],
-                      c.sh, c.sw, c.ph_div_hw[ph], c.ph_div_w[ph], c.pix_h, c.pix_w};
+      o.rows = c.nimg * r.hc * r.wc - p0;
+      o.rm = RowRemap{p0, r.hc * r.wc, r.wc, r.h0, r.w0, c.sh, c.sw, r.div_hw, r.div_w, c.pix_h, c.pix_w};
     }
     return o;
   }

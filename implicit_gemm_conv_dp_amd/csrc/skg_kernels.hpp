@@ -2518,6 +2518,12 @@ struct Engine {
   // handed on and written out (none of which touches the LDS).
   static constexpr bool kStream = kBd && !Loader::kTrans;
 
+  // A tile's iterations past the last tap it has (a dgrad stride phase with
+  // fewer taps than the largest) add nothing and are skipped.
+  SKG_DEV static int seg_iters(const Seg& sg, const Loader& ld) {
+    return max(0, min(sg.k1, ld.iters()) - sg.k0);
+  }
+
   SKG_DEV void run_stream(Walk& w) {
     constexpr int D = Loader::D;
     Seg cur, nxt;
@@ -2525,18 +2531,21 @@ struct Engine {
     Loader lc, ln;
     OutTile oc, on;
     Prob::setup(prm, p, cur.tile, lc, oc, tid);
+    int nc = seg_iters(cur, lc), nn = 0;  // iterations run of cur, nxt
     bool has_nxt = next_segment(w, nxt);
-    if (has_nxt) Prob::setup(prm, p, nxt.tile, ln, on, tid);
+    if (has_nxt) {
+      Prob::setup(prm, p, nxt.tile, ln, on, tid);
+      nn = seg_iters(nxt, ln);
+    }
     int base = 0;    // stream position of cur's first iteration
     int issued = 0;  // positions [0, issued) are issued
     // Issues position q (q == issued) if it lies in cur or nxt.
     auto issue_next = [&]() -> bool {
-      const int ic = cur.k1 - cur.k0;
       const int q = issued;
-      if (q < base + ic) {
+      if (q < base + nc) {
         lc.issue_iter(cur.k0 + (q - base), bd_entry(q));
-      } else if (has_nxt && q < base + ic + (nxt.k1 - nxt.k0)) {
-        ln.issue_iter(nxt.k0 + (q - base - ic), bd_entry(q));
+      } else if (has_nxt && q < base + nc + nn) {
+        ln.issue_iter(nxt.k0 + (q - base - nc), bd_entry(q));
       } else {
         return false;
       }
@@ -2547,8 +2556,7 @@ struct Engine {
     }
     while (true) {
       zero_acc();
-      const int ic = cur.k1 - cur.k0;
-      for (int i = 0; i < ic; ++i) {
+      for (int i = 0; i < nc; ++i) {
         const int q = base + i;
         wait_iters(issued - 1 - q);
         lds_barrier();
@@ -2566,12 +2574,16 @@ struct Engine {
       }
       finish(cur, oc);
       if (!has_nxt) break;
-      base += ic;
+      base += nc;
       cur = nxt;
       lc = ln;
       oc = on;
+      nc = nn;
       has_nxt = next_segment(w, nxt);
-      if (has_nxt) Prob::setup(prm, p, nxt.tile, ln, on, tid);
+      if (has_nxt) {
+        Prob::setup(prm, p, nxt.tile, ln, on, tid);
+        nn = seg_iters(nxt, ln);
+      }
     }
     wait_vm<0>();
   }
