@@ -236,7 +236,7 @@ WORKLOADS = {
 # the launches measured fastest (256x256x64 tiles, persistent, tree fix-up
 # for the dense layer; the block-diagonal 128x64x32 tile for the grouped
 # one, 16 channels per group, two CTAs per CU, where a tile's reduction is
-# 5 MAC iterations (dgrad: 2, its tiles run stride phase by phase) and
+# 5 MAC iterations (dgrad: 1 or 2, its tiles run stride phase by phase) and
 # stream-K does not pay), and the
 # fp8 GEMM of workload 5 with OCP MX (E8M0) block scales instead of
 # row/column scales (256x256x128 tiles: 4 ring slots once the scale bytes
