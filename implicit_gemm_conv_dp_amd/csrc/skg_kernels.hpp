@@ -1019,9 +1019,10 @@ struct WgradBdProblem {
 // ---------------------------------------------------------------------------
 // Fix-up families: each kernel instance carries the code of one, so the
 // epilogue of the other does not take part in its register allocation.
-//   FIX_HANDOFF: linear and tree (partials handed on through flags);
+//   FIX_HANDOFF: linear, tree and reduce-scatter (partials handed on
+//                through flags);
 //   FIX_ATOMIC:  atomic and workspace (fp32 atomics, nothing waits).
-// Data-parallel-only launches use FIX_HANDOFF.
+// Data-parallel-only launches use FIX_ATOMIC (FIX_HANDOFF on MX tiles).
 enum { FIX_HANDOFF = 0, FIX_ATOMIC = 1 };
 
 // Loaders that move MX block scales with the tiles declare kMx.
