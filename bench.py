@@ -392,6 +392,9 @@ def table(args, dev, headline_runner):
                "kernel_us": k, "step_us": stats_us(step),
                "bound": roof["bound"], "achieved": roof["achieved"], "unit": roof["unit"],
                "peak": roof["peak"], "frac": roof["frac"]}
+        if r.red == "scatter":
+            # the linear fix-up's sums in its order, split over the contributors
+            row["same_bits_as"] = "linear"
         for key in ("pool_cap", "frac_of_pool_cap", "traffic"):
             if key in roof:
                 row[key] = roof[key]

@@ -210,6 +210,9 @@ class ConvWorkload:
 # runs 256x256 tiles (9 output tiles) over a pool of 252 = 9 x 28 CTAs: every
 # stream-K CTA then holds 56 whole iterations of one tile, which the k-major
 # CTA order turns into 28 k ranges read by all 9 tiles at about the same time.
+# Workloads 3 and 4 hand their tiles on with the reduce-scatter fix-up: the
+# linear fix-up's additions in the linear order, split over the tile's
+# contributors (its results are the linear fix-up's bit for bit).
 WORKLOADS = {
     1: GemmWorkload(1, "gemm_f16_256x256x4096_pool6_linear", 256, 256, 4096, "f16", "f16",
                     "uniform", "128x128x32", ("dp_sk",), ("linear",), 6),
@@ -222,7 +225,8 @@ WORKLOADS = {
     # 16 channels per group: the block-diagonal tile (four whole groups per
     # 64-row tile, whole 128-byte lines) over 224 CTAs, i.e. 28 whole slices
     # of 14 iterations per tile, with the reduce-scatter fix-up; the
-    # per-group 32x64x64 tile and the linear fix-up are reported beside it.
+    # per-group 32x64x64 tile and the one-CTA linear fold are reported
+    # beside it.
     4: WgradWorkload(4, "wgrad_bf16_n64_28x28_c512_k512_g32_3x3_s2", 64, 28, 28, 512, 512, 3, 3,
                      (2, 2), (1, 1), 32, "bf16", "uniform", "64x144x32", ("dp_sk",), ("scatter",),
                      224),
@@ -261,8 +265,7 @@ NEXT_WORKLOADS = {
 
 # Further launches of a workload reported beside its own: the dense wgrad
 # layer with the tree fix-up (its own launch takes the reduce-scatter
-# fix-up, which is not one of the page's four; all five run at full size in
-# the parity tests); the
+# fix-up; all five run at full size in the parity tests); the
 # grouped layer with the linear and tree fix-ups on the block-diagonal tile
 # and with the per-group tile (partial 32-row M tiles, groups folded into
 # GEMM-M one per tile); the grouped forward and dgrad on the dense

@@ -142,7 +142,9 @@ enum skg_mode {
  *              Every contributor publishes its fp32 partial; contributor k
  *              of a tile's S then sums the k-th of S equal parts of the tile
  *              over all S partials, in contributor order, and writes that
- *              part of the output.  One round of hand-offs where linear
+ *              part of the output: the additions and the epilogue of LINEAR
+ *              in LINEAR's order, so the output is LINEAR's bit for bit for
+ *              the same partition.  One round of hand-offs where linear
  *              takes S - 1 and tree ceil(log2 S); same workspace and the
  *              same residency rule as linear/tree.  Other partitions: -2.
  *              Never chosen by AUTO. */

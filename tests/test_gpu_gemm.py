@@ -384,6 +384,36 @@ def test_scatter_fixup_integer_exact(tile, fmt):
             assert np.array_equal(Y, R), "%s %s %s S=%d scatter" % (tile, fmt, mode, S)
 
 
+@pytest.mark.parametrize("tile,fmt,fmt_c", [("256x256x64", "bf16", "bf16"),
+                                            ("128x128x64", "f16", "f32"),
+                                            ("256x256x128", "e4m3", "bf16")])
+def test_scatter_is_linear_bit_for_bit(tile, fmt, fmt_c):
+    # Random data with per-row / per-column scales: the reduce-scatter adds
+    # the partials in the linear fix-up's order and applies the same
+    # epilogue, so for the same partition both give the same bits.
+    M, N, K = shape_for(tile)
+    A = synth.to_codes(synth.draw("normal", M * K, 111), fmt)
+    B = synth.to_codes(synth.draw("normal", N * K, 112), fmt)
+    sa = np.random.default_rng(113).uniform(0.5, 2.0, M).astype(np.float32)
+    sb = np.random.default_rng(114).uniform(0.5, 2.0, N).astype(np.float32)
+    dA, dB, dsa, dsb = to_dev(A, fmt), to_dev(B, fmt), to_dev_f32(sa), to_dev_f32(sb)
+    p0 = skg.plan_gemm(M=M, N=N, K=K, dtype_ab=fmt, dtype_c=fmt_c, tile=tile, mode="dp_sk",
+                       reduction="tree", ctas=8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    for S in [d for d in (2, 3, 8) if ipt % d == 0]:
+        for mode in ("dp_sk", "persistent"):
+            out = {}
+            for red in ("scatter", "linear"):
+                dC = out_buffer(fmt_c, M * N)
+                plan = skg.gemm(dA, dB, dC, dsa, dsb, M=M, N=N, K=K, dtype_ab=fmt, dtype_c=fmt_c,
+                                tile=tile, mode=mode, reduction=red, ctas=T * S)
+                torch.cuda.synchronize()
+                assert plan["sk_ctas"] == T * S
+                out[red] = dC.cpu().numpy().copy()
+            assert np.array_equal(out["scatter"], out["linear"]), "%s %s %s S=%d" % (tile, fmt,
+                                                                                    mode, S)
+
+
 @pytest.mark.parametrize("fmt_c", ["f16", "bf16"])
 def test_scatter_fixup_16bit_output(fmt_c):
     # Random data, 16-bit output: the part a contributor writes goes through

@@ -178,6 +178,40 @@ def test_scatter_fixup_integer_exact(name, tile):
                                                                           order)
 
 
+@pytest.mark.parametrize("tile", ["32x64x64", "256x256x64", "64x144x32"])
+def test_scatter_is_linear_bit_for_bit(tile):
+    # The reduce-scatter fix-up adds the tile's partials in the linear
+    # fix-up's order -- the first contributor's, then each later one in CTA
+    # order -- only split over the contributors: on random data, for the same
+    # partition, both give the same bits.
+    shape = (8, 16, 16, 64, 64, 3, 3, (2, 2), (1, 1), 4) if tile == "64x144x32" else LONG
+    x, dy, _ = inputs(shape, "f16", False, 131)
+    _, p0 = run(x, dy, shape, "f16", tile, "dp_sk", "workspace", 8)
+    T, ipt = p0["tiles"], p0["iters_per_tile"]
+    ds = divisors(ipt)
+    for S in sorted({ds[0], ds[len(ds) // 2], ipt}):
+        for mode in ("dp_sk", "persistent"):
+            for order in ("xcd", "kmajor"):
+                Ys, ps = run(x, dy, shape, "f16", tile, mode, "scatter", T * S, sk_order=order)
+                Yl, pl = run(x, dy, shape, "f16", tile, mode, "linear", T * S, sk_order=order)
+                assert ps["sk_ctas"] == pl["sk_ctas"] == T * S and ps["sk_order"] == pl["sk_order"]
+                assert np.array_equal(Ys, Yl), "%s %s S=%d %s" % (tile, mode, S, order)
+
+
+@pytest.mark.parametrize("index", [3, 4])
+def test_scatter_is_linear_bit_for_bit_full_size(index):
+    # Both wgrad workloads in the benchmark's launch (pool, mode, CTA order):
+    # the reduce-scatter and the linear fix-up give the same bits.
+    wl = synth.WORKLOADS[index]
+    inp = wl.inputs()
+    shape = (wl.n, wl.h, wl.w, wl.c, wl.k, wl.r, wl.s, wl.stride, wl.pad, wl.groups)
+    mode = wl.modes[0]
+    Ys, ps = run(inp["x"], inp["dy"], shape, wl.dtype, wl.tile, mode, "scatter", wl.ctas)
+    Yl, pl = run(inp["x"], inp["dy"], shape, wl.dtype, wl.tile, mode, "linear", wl.ctas)
+    assert ps["sk_ctas"] == pl["sk_ctas"] == wl.ctas and ps["sk_order"] == pl["sk_order"]
+    assert np.array_equal(Ys, Yl), wl.name
+
+
 def test_scatter_fixup_full_layer():
     # The 56x56 layer, split-K over the default pool with the scatter fix-up
     # in k-major order, element by element against the oracle.
