@@ -73,14 +73,15 @@ struct OutTile {
   RowRemap rm;  // read only by problems with kRowRemap
 };
 
-// Element offset of tile row r from the tile base.
-SKG_DEV size_t remap_row(const RowRemap& m, int r) {
+// Pixel of tile row r (its offset from the tile base in rows of ld
+// elements).  32-bit: the host keeps every output under 2^31 bytes.
+SKG_DEV uint32_t remap_row(const RowRemap& m, int r) {
   const uint32_t q = (uint32_t)(m.p0 + r);
   const uint32_t n = fdiv(q, m.div_hw);
   const uint32_t rem = q - n * (uint32_t)m.hw;
   const uint32_t i = fdiv(rem, m.div_wc);
   const uint32_t j = rem - i * (uint32_t)m.wc;
-  return ((size_t)n * m.H + m.h0 + m.sh * i) * m.W + m.w0 + m.sw * j;
+  return (n * (uint32_t)m.H + m.h0 + m.sh * i) * (uint32_t)m.W + m.w0 + m.sw * j;
 }
 
 // Problems whose output rows are not consecutive declare kRowRemap.
@@ -95,7 +96,7 @@ struct ProbRemap<P, std::void_t<decltype(P::kRowRemap)>> {
 template <class P>
 SKG_DEV size_t out_row(const OutTile& o, int r) {
   if constexpr (ProbRemap<P>::value)
-    return remap_row(o.rm, r) * (size_t)o.ld;
+    return remap_row(o.rm, r) * (uint32_t)o.ld;  // < 2^31 elements
   else
     return (size_t)r * o.ld;
 }
