@@ -104,6 +104,8 @@ int injected_fault() {
   return INJECT_NONE;
 }
 
+FastDiv make_fastdiv(uint32_t d);
+
 KPlan to_kplan(const skg_plan_t& pl, int inject) {
   KPlan k;
   k.tiles_m = (int)pl.tiles_m;
@@ -123,6 +125,10 @@ KPlan to_kplan(const skg_plan_t& pl, int inject) {
   k.sk_slices = whole_slices(pl) ? (int)(pl.iters_per_tile / pl.iters_per_sk_cta) : 1;
   k.spin_limit = inject == INJECT_HANDOFF ? kFaultSpin : kSpinLimit;
   k.fault = inject == INJECT_HANDOFF ? FAULT_NO_PUBLISH : FAULT_NONE;
+  const int tn = k.tiles_n > 0 ? k.tiles_n : 1;
+  k.dp_rows = k.dp_tiles / tn;
+  k.div_tiles_n = make_fastdiv((uint32_t)tn);
+  k.div_groups = make_fastdiv((uint32_t)(kDpGroupRows * tn));
   return k;
 }
 

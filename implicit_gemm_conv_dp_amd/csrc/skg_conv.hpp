@@ -226,7 +226,7 @@ struct ConvProblem {
   typedef ConvGrpLoader<Cfg, DGRAD> Loader;
 
   SKG_DEV static void coords(const Params& c, const KPlan& p, int tile, int& group, int& m0, int& n0) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     group = tn / c.nt_per_group;
     n0 = (tn - group * c.nt_per_group) * Cfg::TN;
     m0 = tm * Cfg::TM;
@@ -454,12 +454,12 @@ struct ConvBdProblem {
   static constexpr bool kRowRemap = DGRAD;
 
   SKG_DEV static void setup(const Params& c, const KPlan& p, int tile, Loader& ld, OutTile& out, int tid) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     ld.init(c, tm, tn * Cfg::TN, tid);
     out = out_tile(c, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& c, const KPlan& p, int tile) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int k0 = tn * Cfg::TN;
     const int esz = c.dtype_out == DT_F32 ? 4 : 2;
     OutTile o;

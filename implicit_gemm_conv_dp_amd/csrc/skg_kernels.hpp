@@ -34,6 +34,9 @@ enum { SK_ORDER_BLOCK = 0, SK_ORDER_XCD = 1, SK_ORDER_KMAJOR = 2 };
 // their flags, so every wait on them runs into its (then small) spin limit.
 enum { FAULT_NONE = 0, FAULT_NO_PUBLISH = 1 };
 
+// Tile rows per group of the data-parallel tile order (dp_order).
+constexpr int kDpGroupRows = 4;
+
 struct KPlan {
   int tiles_m, tiles_n, ipt;
   int dp_tiles, sk_tiles, sk_ctas, ipc, extra;
@@ -42,6 +45,11 @@ struct KPlan {
   int sk_slices;        // SK_ORDER_KMAJOR: slices per tile (sk_ctas = sk_tiles * sk_slices)
   uint32_t spin_limit;  // polls before a flag wait gives up
   int fault;            // FAULT_*
+  int dp_rows;          // dp_tiles / tiles_n
+  FastDiv div_tiles_n;  // by tiles_n
+  FastDiv div_groups;   // by kDpGroupRows * tiles_n
+  // Row of the tile grid that tile id `tile` lies in.
+  SKG_DEV int tile_row(int tile) const { return (int)fdiv((uint32_t)tile, div_tiles_n); }
 };
 
 // The caller's workspace, carved up on the host.
@@ -579,13 +587,13 @@ struct GemmProblem {
 
   SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int m0 = tm * Cfg::TM, n0 = tn * Cfg::TN;
     ld.init(g, m0, n0, tid);
     out = out_tile(g, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& g, const KPlan& p, int tile) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int m0 = tm * Cfg::TM, n0 = tn * Cfg::TN;
     const int esz = g.dtype_c == DT_F32 ? 4 : 2;
     OutTile o;
@@ -610,7 +618,7 @@ struct GemmMxProblem {
 
   SKG_DEV static void setup(const Params& g, const KPlan& p, int tile, Loader& ld, OutTile& out,
                             int tid) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     ld.init(g, tm * Cfg::TM, tn * Cfg::TN, tid);
     out = out_tile(g, p, tile);
   }
@@ -829,14 +837,14 @@ struct WgradProblem {
 
   SKG_DEV static void setup(const Params& w, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int group = tm / w.mt_per_group;
     const int mrow0 = (tm - group * w.mt_per_group) * Cfg::TM;
     ld.init(w, group, mrow0, tn * Cfg::TN, tid);
     out = out_tile(w, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& w, const KPlan& p, int tile) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int group = tm / w.mt_per_group;
     const int mrow0 = (tm - group * w.mt_per_group) * Cfg::TM;
     const int n0 = tn * Cfg::TN;
@@ -996,12 +1004,12 @@ struct WgradBdProblem {
 
   SKG_DEV static void setup(const Params& w, const KPlan& p, int tile, Loader& ld, OutTile& out,
                                int tid) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     ld.init(w, tm * Cfg::TM, tn * Loader::TAPS, tid);
     out = out_tile(w, p, tile);
   }
   SKG_DEV static OutTile out_tile(const Params& w, const KPlan& p, int tile) {
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    const int tm = p.tile_row(tile), tn = tile - tm * p.tiles_n;
     const int k0 = tm * Cfg::TM, n0 = tn * Cfg::TN;
     OutTile o;
     // dW is K x (R*S*16) row-major; the tile's rows are output channels
@@ -2371,15 +2379,18 @@ struct Engine {
   // bijection on [0, dp_tiles); the DP tiles are whole rows of the tile
   // grid plus a partial last row, which keeps its order.
   SKG_DEV int dp_order(int s) const {
-    constexpr int XCDS = 8, GM = 4;
+    constexpr int XCDS = 8, GM = kDpGroupRows;
     const int n8 = p.dp_tiles & ~(XCDS - 1);
     const int u = s < n8 ? (s % XCDS) * (n8 / XCDS) + s / XCDS : s;
-    const int rows = p.dp_tiles / p.tiles_n;
+    const int rows = p.dp_rows;
     if (u >= rows * p.tiles_n) return u;
-    const int g = u / (GM * p.tiles_n);
+    const int g = (int)fdiv((uint32_t)u, p.div_groups);
     const int within = u - g * GM * p.tiles_n;
-    const int rg = min(GM, rows - g * GM);
-    return (g * GM + within % rg) * p.tiles_n + within / rg;
+    const int rg = min(GM, rows - g * GM);  // 1 .. 4
+    // within / rg without a division: a shift for 1, 2, 4; for 3 the
+    // multiply-high by ceil(2^33 / 3), exact for every 32-bit value
+    const int q = rg == 3 ? (int)(__umulhi((uint32_t)within, 0xAAAAAAABu) >> 1) : within >> (rg >> 1);
+    return (g * GM + (within - q * rg)) * p.tiles_n + q;
   }
 
   // One bounded work loop: the stream-K range (if any) segment by segment,
