@@ -186,6 +186,27 @@ def test_block_diagonal_integer_exact_all_modes_and_fixups(op, name):
                     break
 
 
+@pytest.mark.parametrize("tile", [BD_TILE, "128x128x64"])
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_data_parallel_plan_same_bits_for_every_reduction(op, tile):
+    # All-DP plans run no fix-up: every reduction name (and the kernel
+    # family it selects) gives the same output, in dp mode and in
+    # persistent mode with a pool that divides the tiles (on the
+    # block-diagonal tile the ring then streams across a CTA's tiles).
+    shape = BD_SHAPES["bd_s23_4x4"] if tile == BD_TILE else SHAPES["grouped"]
+    act, filt, _ = inputs(op, shape, "bf16", False, 163)
+    _, p0 = run(op, act, filt, shape, "bf16", "f32", tile, "dp", "linear", 1)
+    T = p0["tiles"]
+    ref = None
+    for mode, ctas in [("dp", 1)] + [("persistent", d) for d in sorted({T, max(1, T // 3)}) if T % d == 0]:
+        for red in REDS:
+            Y, plan = run(op, act, filt, shape, "bf16", "f32", tile, mode, red, ctas)
+            assert plan["sk_ctas"] == 0 and plan["dp_tiles"] == T, (mode, red, ctas, plan)
+            if ref is None:
+                ref = Y
+            assert np.array_equal(Y, ref), "%s %s %s %s ctas=%d" % (op, tile, mode, red, ctas)
+
+
 @pytest.mark.parametrize("name", list(BD_SHAPES))
 @pytest.mark.parametrize("op", ["fwd", "dgrad"])
 def test_block_diagonal_random_16bit_outputs(op, name):

@@ -77,6 +77,28 @@ def test_random_all_modes_and_fixups(tile, fmt):
                     break
 
 
+@pytest.mark.parametrize("tile,fmt", TILE_DT)
+def test_data_parallel_plan_same_bits_for_every_reduction(tile, fmt):
+    # A plan without stream-K CTAs runs no fix-up, so the reduction it names
+    # (and the kernel family that name selects) cannot change a bit of C:
+    # all-DP launches (dp mode, persistent with a pool that divides the
+    # tiles) give the same output under every reduction.
+    M, N, K = shape_for(tile)
+    dist = "normal" if fmt in FP8 else "uniform"
+    A = synth.to_codes(synth.draw(dist, M * K, 21), fmt)
+    B = synth.to_codes(synth.draw(dist, N * K, 22), fmt)
+    sa = synth.draw("scale", M, 23).astype(np.float32)
+    sb = synth.draw("scale", N, 24).astype(np.float32)
+    ref = None
+    for mode, ctas in (("dp", 4), ("persistent", 3), ("persistent", 6)):
+        for red in REDS:
+            Y, plan = run(A, B, M, N, K, fmt, "f32", tile, mode, red, ctas, sa, sb)
+            assert plan["sk_ctas"] == 0 and plan["dp_tiles"] == plan["tiles"], (mode, red, ctas)
+            if ref is None:
+                ref = Y
+            assert np.array_equal(Y, ref), "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas)
+
+
 def exact_in(fmt_c, R):
     if fmt_c == "f32":
         return np.array_equal(R.astype(np.float32).astype(np.float64), R)
