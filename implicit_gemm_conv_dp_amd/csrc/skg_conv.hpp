@@ -105,7 +105,7 @@ struct ConvGrpLoader {
     lds_slot<128>(tid, row, chunk);
     offb = (uint32_t)row * rowb + chunk * 16;
     stepb = STEP * rowb;
-    limb = rowb - chunk * 16;
+    limb = rowb > (uint32_t)chunk * 16 ? rowb - chunk * 16 : 0;  // a chunk past a short reduction reads nothing
     act_h = c.act_h;
     act_w = c.act_w;
     kred = c.kred;

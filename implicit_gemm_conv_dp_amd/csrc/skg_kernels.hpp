@@ -304,7 +304,9 @@ struct DmaRows {
     offb = (uint32_t)row * g.ldb_b + chunk * 16;
     stepa = STEP * g.lda_b;
     stepb = STEP * g.ldb_b;
-    lim = (uint32_t)g.K * Cfg::ESZ - chunk * 16;
+    // Clamped at zero: with K shorter than one LDS row the chunk may start
+    // past K, and a wrapped limit would let it read the row's padding.
+    lim = (uint32_t)max(g.K * Cfg::ESZ - chunk * 16, 0);
   }
 
   // RBX bytes of K starting at byte kb of every row, A rows into `la`, B

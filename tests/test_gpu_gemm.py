@@ -99,6 +99,38 @@ def test_data_parallel_plan_same_bits_for_every_reduction(tile, fmt):
             assert np.array_equal(Y, ref), "%s %s %s %s ctas=%d" % (tile, fmt, mode, red, ctas)
 
 
+@pytest.mark.parametrize("tile,fmt", TILE_DT)
+def test_leading_dimensions_and_tiny_shapes(tile, fmt):
+    # rcr operands in rows wider than the K they hold (lda, ldb > K) and C
+    # rows wider than N (ldc > N), down to a single output element and one
+    # 16-byte slice of K: the oracle's result bit for bit on integer data,
+    # in every launch mode and fix-up, and C's padding columns keep what
+    # they held.
+    eb = 1 if fmt in FP8 else 2
+    kq = 16 // eb  # the K granule: 16 bytes
+    tm, tn, tk = map(int, tile.split("x"))
+    shapes = [(1, 1, kq), (3, 5, 2 * kq), (tm + 3, 2, tk + kq), (2, tn + 9, 3 * tk - kq)]
+    for si, (M, N, K) in enumerate(shapes):
+        lda, ldb = K + 3 * kq, K + kq
+        ldc = (N + 3) // 4 * 4 + 4  # fp32 C: 16-byte rows, 4 spare columns at least
+        A = synth.integer_codes(fmt, M * lda, 171 + si, 0.15)
+        B = synth.integer_codes(fmt, N * ldb, 181 + si, 0.15)
+        sa, sb = synth.pow2_scales(M, 191 + si), synth.pow2_scales(N, 201 + si)
+        R = oracle_gemm(fmt, A, B, M, N, K, lda=lda, ldb=ldb, scale_a=sa, scale_b=sb)
+        dA, dB, dsa, dsb = to_dev(A, fmt), to_dev(B, fmt), to_dev_f32(sa), to_dev_f32(sb)
+        for mode, red, ctas in [("dp", "linear", 1), ("dp_sk", "tree", 3), ("persistent", "linear", 5),
+                                ("dp_sk", "atomic", 4), ("persistent", "workspace", 3)]:
+            dC = out_buffer("f32", M * ldc)
+            plan = skg.gemm(dA, dB, dC, dsa, dsb, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc,
+                            dtype_ab=fmt, dtype_c="f32", tile=tile, mode=mode, reduction=red,
+                            ctas=ctas)
+            torch.cuda.synchronize()
+            Y = decode_out(dC, "f32").reshape(M, ldc)
+            what = "%s %s M=%d N=%d K=%d %s %s ctas=%d" % (tile, fmt, M, N, K, mode, red, ctas)
+            assert np.array_equal(Y[:, :N], R), what
+            assert np.isnan(Y[:, N:]).all(), what + ": padding of C written"
+
+
 def exact_in(fmt_c, R):
     if fmt_c == "f32":
         return np.array_equal(R.astype(np.float32).astype(np.float64), R)
