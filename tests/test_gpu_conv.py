@@ -33,6 +33,8 @@ SHAPES = {
     "grouped": (2, 12, 12, 64, 32, 3, 3, (2, 2), (1, 1), 4),
     "wide": (1, 17, 15, 144, 40, 3, 2, (1, 2), (1, 0), 1),
     "deep": (2, 8, 8, 264, 136, 3, 3, (1, 1), (1, 1), 1),
+    # 1x1 over 16 channels: a 32-byte forward reduction, shorter than one LDS row
+    "c16_1x1": (2, 5, 7, 16, 24, 1, 1, (1, 1), (0, 0), 1),
 }
 
 

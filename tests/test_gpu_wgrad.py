@@ -28,6 +28,9 @@ SHAPES = {
     "strided": (3, 11, 10, 32, 16, 3, 3, (2, 2), (1, 1), 1),
     "grouped": (2, 12, 12, 64, 32, 3, 3, (2, 2), (1, 1), 4),
     "wide": (1, 17, 15, 144, 40, 3, 2, (1, 2), (1, 0), 1),
+    # reductions shorter than one K tile: a single pixel, and 9 pixels
+    "one_pixel": (1, 1, 1, 16, 16, 1, 1, (1, 1), (0, 0), 1),
+    "short": (1, 3, 3, 16, 24, 3, 3, (1, 1), (1, 1), 1),
 }
 TILES = ["128x128x32", "32x64x64", "128x128x64", "256x128x64", "256x256x64"]
 
@@ -257,6 +260,8 @@ BD_SHAPES = {
     "bd_1x1": (2, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0), 4),
     # 5x5: 25 taps in three N tiles (the last holds 7), strides 2 x 1
     "bd_5x5": (2, 11, 9, 80, 80, 5, 5, (2, 1), (2, 2), 5),
+    # a 6-pixel reduction: one MAC iteration, mostly past its end
+    "bd_short": (1, 2, 3, 16, 16, 3, 3, (1, 1), (1, 1), 1),
 }
 
 
