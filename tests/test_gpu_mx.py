@@ -7,6 +7,8 @@ column of B, applied by the gfx950 scaled f8f6f4 MFMA per operand lane.
   mode x fix-up, with ragged M and N tiles: a scale applied to the wrong
   block, row or column, or a wrong bias, changes the result.
 * Random data (N(0,1) quantised, scales 2^-3 .. 2^3) within 2e-2.
+* Padded operand and output rows (lda, ldb > K, ldc > N) with compact scale
+  arrays: bit-exact, padding untouched.
 * A full-size 8192^3 e4m3 launch on sampled entries.
 * Unsupported MX arguments (wrong tile, K not a multiple of 128, 16-bit
   inputs, a missing scale array) are -2.
@@ -76,6 +78,34 @@ def test_random_within_tolerance(fmt, tile):
                              ("persistent", "workspace", "f32"), ("dp_sk", "atomic", "f32")):
         Y, plan = run(A, B, SA, SB, M, N, K, fmt, fmt_c, mode, red, 11, tile)
         assert_close(Y, R, fmt, "mx %s %s %s %s" % (tile, fmt, mode, red))
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_leading_dimensions(tile):
+    # A and B rows wider than K (lda, ldb > K) and C rows wider than N, with
+    # the scale arrays still M x K/32 and N x K/32: bit-exact against the
+    # oracle on the compact operands, and C's padding columns keep their NaN.
+    tm = int(tile.split("x")[0])
+    M, N, K = tm + 8, 72, 2 * 128
+    lda, ldb, ldc = K + 48, K + 16, N + 4
+    A = synth.integer_codes("e4m3", M * lda, 81, 0.2)
+    B = synth.integer_codes("e4m3", N * ldb, 82, 0.2)
+    SA, SB = e8m0(M * K // 32, 83, -4, 4), e8m0(N * K // 32, 84, -4, 4)
+    Ac = np.ascontiguousarray(A.reshape(M, lda)[:, :K]).reshape(-1)
+    Bc = np.ascontiguousarray(B.reshape(N, ldb)[:, :K]).reshape(-1)
+    R = gemm_mx("e4m3", Ac, Bc, SA, SB, M, N, K)
+    dA, dB = to_dev(A, "e4m3"), to_dev(B, "e4m3")
+    dSA, dSB = torch.from_numpy(SA).to("cuda"), torch.from_numpy(SB).to("cuda")
+    for mode, red, ctas in [("dp", "linear", 1), ("dp_sk", "tree", 5), ("persistent", "linear", 3),
+                            ("dp_sk", "atomic", 4), ("persistent", "workspace", 7)]:
+        dC = out_buffer("f32", M * ldc)
+        skg.gemm(dA, dB, dC, dSA, dSB, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc, dtype_ab="e4m3",
+                 dtype_c="f32", tile=tile, mode=mode, reduction=red, ctas=ctas, scale_mode="mx")
+        torch.cuda.synchronize()
+        Y = decode_out(dC, "f32").reshape(M, ldc)
+        what = "%s %s %s ctas=%d" % (tile, mode, red, ctas)
+        assert np.array_equal(Y[:, :N], R), what
+        assert np.isnan(Y[:, N:]).all(), what + ": padding written"
 
 
 @pytest.mark.parametrize("tile,ctas", [("128x128x128", 512), ("256x256x128", 256)])
