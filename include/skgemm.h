@@ -240,7 +240,10 @@ typedef struct skg_tile_info {
  * ("gemm_rowcolquant dispatcher bridge" PR, final description: scales applied
  * in the epilogue, fp32 accumulator narrowed only there).
  * Alignment: A, B, C 16-byte aligned; lda, ldb multiples of 16 bytes; K a
- * multiple of 16 bytes of input type. */
+ * multiple of 16 bytes of input type; ldc a multiple of 16 bytes; lda, ldb
+ * >= K and ldc >= N (else -2).  Only the first K elements of each A row and
+ * B column are read, and only the M x N elements of C are written: padding
+ * columns of C keep what they held. */
 typedef struct skg_gemm_args {
   int64_t M, N, K;
   int32_t dtype_ab;        /* SKG_F16, SKG_BF16, SKG_F8E4M3 or SKG_F8E5M2 */
